@@ -1,0 +1,150 @@
+"""Throughput of the Stable LatentMoE forward on one MI355X.
+
+One step = one lmoe_forward over one batch of the K3-shaped prefill workload
+(T=8192 tokens, d=7168, latent 3584, 896 routed experts choose 16, 2 shared,
+expert hidden 512, bf16, every weight resident in HBM), seeded synthetic
+inputs already in device memory.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--config C2] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    return ap.parse_args()
+
+
+def routed_w12_bytes(cfg, counts):
+    """Algorithmic HBM bytes of the routed W1/W2 + SiTU-GLU kernel for one launch:
+    each touched expert's W1 and W2 once, each dispatched latent row once, each
+    gated hidden row written once."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    touched = int((counts > 0).sum())
+    rows = int(counts.sum())
+    return touched * 2 * cfg.D * cfg.L * es + rows * (cfg.L + cfg.D) * es, touched
+
+
+def cpu_baseline(cfg, n_tok):
+    """Time the oracle (as it stands) on the first n_tok tokens of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import synth
+    from oracle import ref
+    P = synth.HostParams(cfg, cache=True)
+    x = P.x_rows(np.arange(n_tok))
+    # input synthesis (not timed): generate the weights the sample touches
+    pre = ref.forward(x, P, cfg.k, cfg.n_shared, cfg.dtype, cfg.beta1, cfg.beta2, cfg.eps)
+    t0 = time.perf_counter()
+    ref.forward(x, P, cfg.k, cfg.n_shared, cfg.dtype, cfg.beta1, cfg.beta2, cfg.eps)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_tok} tokens of the {cfg.name} workload (T={cfg.T}), NumPy fp64 oracle, "
+                      f"{int((pre['counts'] > 0).sum())} experts touched; weight synthesis excluded; "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's expert bank is "
+              "resident on a single MI355X and no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import sparse_moe_layer_down_amd as lmoe
+    import synth
+
+    cfg = synth.get_config(args.config)
+    dev = torch.device("cuda:0")
+    w = synth.device_params(cfg, device=dev)
+    x = w.pop("x")
+    dims = lmoe.dims_of(x, w, cfg.k)
+    ws = lmoe.make_workspace(dims, x.dtype, dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        lmoe.forward(x, w, cfg.k, y=y, workspace=ws, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps,
+                     stage_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K plain forwards
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-stage durations: K more forwards with HIP events recorded between stages on the same stream
+    stage_ms = np.zeros(lmoe.N_STAGES)
+    for _ in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(lmoe.N_STAGES + 1)]
+        step(evs)
+        torch.cuda.synchronize()
+        stage_ms += np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(lmoe.N_STAGES)])
+    stage_ms /= args.steps
+
+    counts = lmoe.workspace_view(ws, dims, x.dtype, "counts").cpu().numpy()
+    flops = cfg.flops_per_token() * cfg.T
+    tflops = flops / (ms * 1e-3) / 1e12
+    w12_bytes, touched = routed_w12_bytes(cfg, counts)
+    w12_ms = float(stage_ms[lmoe.STAGES.index("routed_w12")])
+    achieved = w12_bytes / (w12_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": "LatentMoE fwd tokens/s + % bf16 MFMA peak (d=7168, 896c16) on 1 MI355X",
+        "value": cfg.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded SplitMix64/Irwin-Hall normal inputs and weights, generated in HBM)",
+        "config": {"workload": f"{cfg.name}: K3-shaped LatentMoE prefill forward" if cfg.name == "C2" else cfg.name,
+                   "T": cfg.T, "d": cfg.d, "latent": cfg.L, "experts": cfg.n, "top_k": cfg.k,
+                   "shared": cfg.n_shared, "expert_hidden": cfg.D},
+        "tflops": tflops,
+        "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
+        "stage_ms": {name: float(v) for name, v in zip(lmoe.STAGES, stage_ms)},
+        "roofline": {"kernel": "routed experts W1/W2 + SiTU-GLU grouped GEMM", "bound": "hbm",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": None, "algorithmic_bytes": w12_bytes, "experts_touched": touched,
+                     "avg_ms": w12_ms},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

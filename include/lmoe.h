@@ -1,0 +1,201 @@
+/*
+ * lmoe.h - C ABI of the Stable LatentMoE forward pass and the Quantile
+ * Balancing estimator on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (three web pages on the Kimi K3 architecture):
+ *   [DD] "Kimi K3 Architecture Deep Dive": §1 SiTU-GLU, §2 Stable LatentMoE,
+ *        §3 Quantile Balancing.
+ *   [IK] "Inside K3: How Stable Latent MoE and MLA Attention Are Designed":
+ *        sections SiTU-GLU, RMSNorm insertion, Quantile Balancing (QB).
+ *   [RB] LeiPhone report on Su Jianlin's K3 notes: "LatentMoE: paying for a
+ *        bigger pool", "Keeping the numbers in range".
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) unless
+ *     stated; matrices are row-major with the PyTorch [out, in] weight layout.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     memory and keeps no state between calls, so calls on different streams
+ *     with different workspaces may run concurrently.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; no entry point synchronises with the host.
+ *   - Arguments are validated before anything is enqueued; on a validation
+ *     error nothing is launched and a negative lmoe_status is returned.  A
+ *     failed launch returns LMOE_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Pointers must be 16-byte aligned (LMOE_ERR_ALIGN otherwise).
+ */
+#ifndef LMOE_H
+#define LMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMOE_OK = 0,
+  LMOE_ERR_NULL = -1,      /* a required pointer is NULL                       */
+  LMOE_ERR_SHAPE = -2,     /* dims violate the layer's or the kernels' rules   */
+  LMOE_ERR_DTYPE = -3,     /* unknown work dtype                               */
+  LMOE_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                 */
+  LMOE_ERR_WORKSPACE = -5, /* workspace smaller than lmoe_workspace_size()     */
+  LMOE_ERR_HIP = -6,       /* a HIP launch or runtime call failed              */
+  LMOE_ERR_VALUE = -7      /* a scalar argument is out of range                */
+} lmoe_status;
+
+/* Work dtype: the storage type of x, the weights, and the stored activations
+ * z, a, v, y.  Accumulation, router scores, routing weights, the aggregated
+ * latent and the norm statistics are always fp32. */
+typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
+
+/* Layer dimensions ([DD] §2: d -> d/2 -> D -> d/2 -> d, k of n routed experts;
+ * [RB] "LatentMoE: paying for a bigger pool": hidden 7168, latent 3584,
+ * 16 of 896 routed experts, two always-on shared experts).
+ *   T         tokens (>= 0; T == 0 is a successful no-op)
+ *   d         model width; multiple of 128 (so that L is a multiple of 64)
+ *   L         latent width; must equal d / 2
+ *   n         routed experts, 1..1024
+ *   k         experts chosen per token, 1..min(n, 64)
+ *   n_shared  shared experts, 0..8
+ *   D         expert hidden width; multiple of 64                              */
+typedef struct {
+  int64_t T, d, L, n, k, n_shared, D;
+} lmoe_dims;
+
+/* Weights (device pointers, work dtype unless noted).
+ *   w_down [L, d]        down-projection, no bias ([DD] §2: pure linear map)
+ *   w_router [n, L]      router; scores s = sigmoid(z w_router^T + o)
+ *   router_bias [n] fp32 loss-free selection bias b: added to s for the top-k
+ *                        choice only ([DD] §3; [RB] "Keeping the numbers in
+ *                        range")
+ *   router_logit_offset [n] fp32 or NULL: per-expert offset o added to the
+ *                        logits before the sigmoid (a hook to make routing
+ *                        skewed in synthetic workloads)
+ *   w1, w2 [n, D, L]     SiTU gate branch / softcapped linear branch
+ *   w3 [n, L, D]         expert output projection
+ *   ws1, ws2 [n_shared, D, L], ws3 [n_shared, L, D]   shared experts (NULL iff
+ *                        n_shared == 0); SiTU-GLU in the latent space, weight 1
+ *   rms_gain [L]         gain of the single RMSNorm ([DD] §2: kept before the
+ *                        up-projection only)
+ *   w_up [d, L]          up-projection
+ *   beta1, beta2         SiTU and softcap caps ([DD] §1: 4 and 25; > 0)
+ *   rms_eps              RMSNorm epsilon (>= 0; 1e-6 by default)            */
+typedef struct {
+  const void *w_down;
+  const void *w_router;
+  const float *router_bias;
+  const float *router_logit_offset;
+  const void *w1, *w2, *w3;
+  const void *ws1, *ws2, *ws3;
+  const void *rms_gain;
+  const void *w_up;
+  float beta1, beta2, rms_eps;
+} lmoe_weights;
+
+/* Bytes of device workspace lmoe_forward needs for these dims and dtype
+ * (0 for invalid dims). */
+size_t lmoe_workspace_size(const lmoe_dims *dims, int dtype);
+
+/* Workspace regions that can be inspected after a forward (for tests and
+ * debugging; contents are valid once the stream reaches the end of the call). */
+typedef enum {
+  LMOE_WS_Z = 0,         /* [T, L] work dtype: latent z = x w_down^T                    */
+  LMOE_WS_COUNTS = 1,    /* [n] int32: tokens routed to each expert                      */
+  LMOE_WS_OFFS = 2,      /* [n+1] int32: exclusive prefix sum of counts                  */
+  LMOE_WS_ROW_TOKEN = 3, /* [T*k] int32: token of each dispatched row, rows ordered by
+                                   (expert, token)                                        */
+  LMOE_WS_ROW_SLOT = 4,  /* [T*k] int32: dispatched row of (token t, slot r) at t*k+r      */
+  LMOE_WS_HIDDEN = 5,    /* [T*k, D] work dtype: gated hidden a of each dispatched row     */
+  LMOE_WS_U = 6,         /* [T, L] fp32: shared-expert part of the aggregated latent u    */
+  LMOE_WS_V = 7          /* [T, L] work dtype: v = RMSNorm(u)                             */
+} lmoe_ws_region;
+
+/* Byte offset of a region inside the workspace (-1 for an invalid request). */
+int64_t lmoe_workspace_offset(const lmoe_dims *dims, int dtype, int region);
+
+/* Forward pass of one Stable LatentMoE layer ([DD] §1-§3; [IK]; [RB]):
+ *   z = x w_down^T                      (stored in the work dtype)
+ *   s = sigmoid(z w_router^T + o)       (fp32)
+ *   K_i = top-k of s_i + b, ties -> lower expert index, ordered by decreasing
+ *         biased score
+ *   g_ie = s_ie / sum_{e' in K_i} s_ie'
+ *   per routed expert e and each row routed to it:
+ *     a = SiTU(z W1_e^T; beta1) * softcap(z W2_e^T; beta2)   (work dtype)
+ *     u_i += g_ie * (a W3_e^T)
+ *   u_i += sum_j W3s_j (SiTU(W1s_j z_i; beta1) * softcap(W2s_j z_i; beta2))
+ *   v = rms_gain * u / sqrt(mean(u^2) + rms_eps)  (work dtype)
+ *   y = v w_up^T                        (work dtype)
+ * where softcap(x; b) = b tanh(x / b) and SiTU(x; b) = softcap(x; b) sigmoid(x).
+ * Arguments:
+ *   x [T, d]      input tokens, work dtype
+ *   y [T, d]      output, work dtype (may not alias x)
+ *   topk_idx [T, k] int32 out, or NULL
+ *   topk_w [T, k] fp32 out (g), or NULL
+ *   scores [T, n] fp32 out (unbiased sigmoid scores, the input of
+ *                 lmoe_qb_update), or NULL
+ *   workspace     device buffer of at least lmoe_workspace_size() bytes,
+ *                 16-byte aligned; its contents need no initialisation.
+ * Routing is dropless: no capacity limit, every chosen (token, expert) pair is
+ * computed.  NaN in x propagates to y. */
+int lmoe_forward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
+                 int32_t *topk_idx, float *topk_w, float *scores, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/* Stages of lmoe_forward, in launch order (for lmoe_forward_timed). */
+#define LMOE_N_STAGES 10
+/*  0 down-projection GEMM            5 routed experts' W1/W2 + SiTU-GLU (grouped)
+ *  1 router GEMM + sigmoid           6 shared experts' W3 (fp32 shared part of u)
+ *  2 top-k + routing weights         7 routed experts' W3 scaled by g (grouped)
+ *  3 dispatch permutation (3 kernels) 8 combine + RMSNorm
+ *  4 shared experts' W1/W2 + SiTU-GLU 9 up-projection GEMM                      */
+
+/* lmoe_forward with per-stage timing: events is an array of n_events ==
+ * LMOE_N_STAGES + 1 hipEvent_t handles created by the caller; events[i] is
+ * recorded on `stream` before stage i and events[LMOE_N_STAGES] after the last
+ * one, so hipEventElapsedTime(events[i], events[i+1]) is stage i's duration.
+ * Computes exactly what lmoe_forward computes (same kernels, same results). */
+int lmoe_forward_timed(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
+                       int32_t *topk_idx, float *topk_w, float *scores, void *workspace,
+                       size_t workspace_bytes, void *const *events, int n_events, void *stream);
+
+/* Quantile Balancing update ([DD] §3: scores in [0,1] -> B-bin histogram ->
+ * histograms summed across devices -> quantile read; [IK] Quantile Balancing;
+ * [RB] "Keeping the numbers in range": each expert's threshold is moved to
+ * where it receives its target share).
+ *   scores [T, n] fp32    unbiased router scores (as written by lmoe_forward)
+ *   nbins                 B, 1..16384 (1000 by default on the pages)
+ *   hist [n, nbins] int32 per-expert histogram, in/out.  With accumulate == 0 it
+ *                         is overwritten by this batch's counts; with
+ *                         accumulate == 1 the batch's counts are added (the
+ *                         single-device form of the cross-device sum).
+ *                         bin(s) = min(B-1, floor(fp32(s * B))) for s*B >= 1,
+ *                         else 0 (negative scores and NaN go to bin 0).
+ *   bias [n] fp32         written only if solve != 0:
+ *                           N_e  = sum_j hist[e][j]
+ *                           q_e  = read(hist[e], N_e * k / n)
+ *                           tau  = read(sum_e hist[e], (sum_e N_e) * k / n)
+ *                           bias[e] = fp32(tau - q_e)     (computed in fp64)
+ *                         where read(h, c) = (j* + 1 - (c - G(j*+1)) / h[j*]) / B,
+ *                         G(j) = sum_{j' >= j} h[j'], j* = max{j : G(j) >= c}.
+ *                         Experts with an empty histogram keep their bias.
+ *   workspace             device buffer of lmoe_qb_workspace_size(nbins) bytes when
+ *                         solve != 0 (may be NULL otherwise)
+ * T == 0 with accumulate == 0 clears the histogram.  Counts are int32: the
+ * caller keeps every bin below 2^31 across accumulated batches. */
+int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins,
+                   int32_t *hist, int accumulate, float *bias, int solve, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace lmoe_qb_update needs when solve != 0 (the pooled
+ * histogram, int64 [nbins]); 0 for an invalid nbins. */
+size_t lmoe_qb_workspace_size(int32_t nbins);
+
+/* Static description of a status code. */
+const char *lmoe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMOE_H */

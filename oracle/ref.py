@@ -263,7 +263,8 @@ def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_id
     x = np.asarray(x, dtype=np.float64)
     w_router = P.w_router()
     n = w_router.shape[0]
-    z = round_to(x @ P.w_down().T, dtype)
+    z_pre = x @ P.w_down().T
+    z = round_to(z_pre, dtype)
     s = router_scores(z, w_router, P.logit_offset())
     if forced_idx is None:
         idx, gap = biased_topk(s, P.bias(), k)
@@ -285,10 +286,13 @@ def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_id
     for j in range(n_shared):
         a = expert_hidden(z, P.ws1(j), P.ws2(j), beta1, beta2, dtype)
         u += a @ P.ws3(j).T
-    v = round_to(rms_norm(u, P.gamma(), eps), dtype)
-    y = round_to(v @ P.w_up().T, dtype)
+    v_pre = rms_norm(u, P.gamma(), eps)
+    v = round_to(v_pre, dtype)
+    y_pre = v @ P.w_up().T
+    y = round_to(y_pre, dtype)
+    # *_pre: the same tensors before their store rounding (for tolerance checks)
     return dict(z=z, s=s, s32=s.astype(np.float32), idx=idx, gap=gap, g=g, counts=counts, offs=offs,
-                row_token=row_token, row_slot=row_slot, u=u, v=v, y=y)
+                row_token=row_token, row_slot=row_slot, u=u, v=v, y=y, z_pre=z_pre, v_pre=v_pre, y_pre=y_pre)
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,118 @@
+"""Stable LatentMoE forward + Quantile Balancing on AMD MI355X.
+
+Thin Python binding over the C ABI of ``liblmoe.so`` (include/lmoe.h): it
+only reads shapes and device pointers off torch tensors and passes them with
+the current HIP stream.  Every step of the layer runs in the library's HIP
+kernels; there is no other implementation behind these functions.
+"""
+import ctypes
+
+import torch
+
+from ._abi import (Dims, Weights, LMOE_BF16, LMOE_F32, WS_REGIONS, EXPORTS, N_STAGES, STAGES, lib,  # noqa: F401
+                   check, strerror)
+
+__all__ = ["dims_of", "workspace_size", "workspace_view", "forward", "qb_update", "qb_workspace_size",
+           "strerror", "make_workspace"]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return LMOE_BF16
+    if dt == torch.float32:
+        return LMOE_F32
+    raise TypeError(f"unsupported work dtype {dt}")
+
+
+def dims_of(x, weights, k):
+    T, d = x.shape
+    n, D, L = weights["w1"].shape
+    ws1 = weights.get("ws1")
+    return Dims(T, d, weights["w_down"].shape[0], n, int(k), 0 if ws1 is None else ws1.shape[0], D)
+
+
+def workspace_size(dims, dtype):
+    return int(lib().lmoe_workspace_size(dims, _dtype_code(dtype) if isinstance(dtype, torch.dtype) else dtype))
+
+
+def make_workspace(dims, dtype, device="cuda"):
+    return torch.empty(max(workspace_size(dims, dtype), 256), dtype=torch.uint8, device=device)
+
+
+def workspace_view(workspace, dims, dtype, region):
+    """A typed view of one inspectable workspace region (see lmoe_ws_region)."""
+    code = _dtype_code(dtype)
+    off = int(lib().lmoe_workspace_offset(dims, code, WS_REGIONS[region]))
+    if off < 0:
+        raise ValueError(region)
+    T, L, n, k, D = dims.T, dims.L, dims.n, dims.k, dims.D
+    shapes = {"z": ((T, L), dtype), "counts": ((n,), torch.int32), "offs": ((n + 1,), torch.int32),
+              "row_token": ((T * k,), torch.int32), "row_slot": ((T * k,), torch.int32),
+              "hidden": ((T * k, D), dtype), "u_shared": ((T, L), torch.float32), "v": ((T, L), dtype)}
+    shape, dt = shapes[region]
+    nbytes = torch.tensor([], dtype=dt).element_size()
+    cnt = 1
+    for s in shape:
+        cnt *= s
+    return workspace[off:off + cnt * nbytes].view(dt).view(*shape)
+
+
+def _weights_struct(w, beta1, beta2, eps):
+    return Weights(_ptr(w["w_down"]), _ptr(w["w_router"]), _ptr(w["router_bias"]),
+                   _ptr(w.get("router_logit_offset")), _ptr(w["w1"]), _ptr(w["w2"]), _ptr(w["w3"]),
+                   _ptr(w.get("ws1")), _ptr(w.get("ws2")), _ptr(w.get("ws3")), _ptr(w["rms_gain"]),
+                   _ptr(w["w_up"]), float(beta1), float(beta2), float(eps))
+
+
+def forward(x, weights, k, y=None, topk_idx=None, topk_w=None, scores=None, workspace=None, beta1=4.0,
+            beta2=25.0, eps=1e-6, stream=None, stage_events=None):
+    """y = LatentMoE(x) via lmoe_forward on the current stream; returns y.
+
+    ``weights`` holds device tensors named as in include/lmoe.h (w_down, w_router,
+    router_bias, router_logit_offset, w1, w2, w3, ws1, ws2, ws3, rms_gain, w_up).
+    """
+    dims = dims_of(x, weights, k)
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = make_workspace(dims, x.dtype, x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    W = _weights_struct(weights, beta1, beta2, eps)
+    if stage_events is None:
+        rc = lib().lmoe_forward(dims, W, _dtype_code(x.dtype), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w),
+                                _ptr(scores), _ptr(workspace), workspace.numel(), stream)
+        check(rc, "lmoe_forward")
+    else:
+        # stage_events: N_STAGES + 1 torch.cuda.Event(enable_timing=True); their hipEvent_t handles
+        for ev in stage_events:
+            ev.record()  # materialise the underlying hipEvent_t on this device
+        handles = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
+        rc = lib().lmoe_forward_timed(dims, W, _dtype_code(x.dtype), _ptr(x), _ptr(y), _ptr(topk_idx),
+                                      _ptr(topk_w), _ptr(scores), _ptr(workspace), workspace.numel(), handles,
+                                      len(stage_events), stream)
+        check(rc, "lmoe_forward_timed")
+    return y
+
+
+def qb_workspace_size(nbins):
+    return int(lib().lmoe_qb_workspace_size(int(nbins)))
+
+
+def qb_update(scores, k, hist, bias=None, accumulate=False, solve=True, workspace=None, stream=None):
+    """Quantile Balancing: update the per-expert histogram and (optionally) solve the bias in place."""
+    T, n = scores.shape
+    nbins = hist.shape[1]
+    if solve and workspace is None:
+        workspace = torch.empty(qb_workspace_size(nbins), dtype=torch.uint8, device=hist.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(hist.device).cuda_stream
+    rc = lib().lmoe_qb_update(_ptr(scores), T, n, int(k), int(nbins), _ptr(hist), int(bool(accumulate)),
+                              _ptr(bias), int(bool(solve)), _ptr(workspace),
+                              0 if workspace is None else workspace.numel(), stream)
+    check(rc, "lmoe_qb_update")
+    return hist, bias

@@ -1,0 +1,375 @@
+// C ABI of the Stable LatentMoE forward pass and Quantile Balancing (gfx950).
+//
+// The host code validates every argument, carves the caller's workspace and
+// enqueues the kernels on the caller's stream.  It never allocates, never
+// synchronises with the device and keeps no state.
+//
+// Forward launch sequence ("Kimi K3 Architecture Deep Dive" §1-§3; "Inside
+// K3"; LeiPhone report "LatentMoE: paying for a bigger pool" and "Keeping the
+// numbers in range"):
+//   1 gemm   z = x W_down^T
+//   2 gemm   s = sigmoid(z W_r^T + o)                 (fp32 scores)
+//   3 topk   biased top-k, routing weights g
+//   4 perm   chunk masks -> scan (offsets, tile table) -> scatter
+//   5 gemm   shared experts' gated hidden (dense, SiTU-GLU epilogue)
+//   6 gemm   routed experts' gated hidden (grouped, gathered rows, SiTU-GLU)
+//   7 gemm   shared W3 -> u_shared (fp32)
+//   8 gemm   routed W3, scaled by g -> one row per (token, slot)
+//   9 norm   u = u_shared + sum of the token's k rows; v = RMSNorm(u)
+//  10 gemm   y = v W_up^T
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/lmoe.h"
+#include "gemm.hpp"
+#include "norm.hpp"
+#include "qb.hpp"
+#include "route.hpp"
+
+using namespace lmoe;
+
+namespace {
+
+constexpr int G_BM = 128, G_BN = 128, G_WM = 2, G_WN = 2;
+constexpr int G_LDS = 2 * (G_BM + G_BN) * 128;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t align256(int64_t a) { return (a + 255) & ~(int64_t)255; }
+
+struct WsLayout {
+  int64_t off[32];
+  int64_t total;
+};
+
+enum {
+  R_Z = 0, R_COUNTS, R_OFFS, R_ROW_TOKEN, R_SLOT_ROW, R_HIDDEN, R_USH, R_V,
+  R_SCORES, R_IDX, R_W, R_MASKS, R_CBASE, R_TILES, R_NTILES, R_ROW_W, R_HSH, R_YSTAGE, R_COUNT_
+};
+
+int64_t max_tiles(const lmoe_dims &d) { return d.n + cdiv(d.T * d.k, G_BM); }
+
+WsLayout layout(const lmoe_dims &d, int dtype) {
+  const int64_t es = dtype == LMOE_BF16 ? 2 : 4;
+  const int64_t nch = cdiv(d.T, PERM_CHUNK);
+  int64_t sz[R_COUNT_];
+  sz[R_Z] = d.T * d.L * es;
+  sz[R_COUNTS] = d.n * 4;
+  sz[R_OFFS] = (d.n + 1) * 4;
+  sz[R_ROW_TOKEN] = d.T * d.k * 4;
+  sz[R_SLOT_ROW] = d.T * d.k * 4;
+  sz[R_HIDDEN] = d.T * d.k * d.D * es;
+  sz[R_USH] = d.T * d.L * 4;
+  sz[R_V] = d.T * d.L * es;
+  sz[R_SCORES] = d.T * d.n * 4;
+  sz[R_IDX] = d.T * d.k * 4;
+  sz[R_W] = d.T * d.k * 4;
+  sz[R_MASKS] = nch * d.n * 4 * 8;
+  sz[R_CBASE] = nch * d.n * 4;
+  sz[R_TILES] = max_tiles(d) * 16;
+  sz[R_NTILES] = 4;
+  sz[R_ROW_W] = d.T * d.k * 4;
+  sz[R_HSH] = d.T * d.n_shared * d.D * es;
+  sz[R_YSTAGE] = d.T * d.k * d.L * es;
+  WsLayout w;
+  int64_t o = 0;
+  for (int i = 0; i < R_COUNT_; ++i) {
+    w.off[i] = o;
+    o += align256(sz[i]);
+  }
+  w.total = o;
+  return w;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dims(const lmoe_dims *d) {
+  if (!d) return LMOE_ERR_NULL;
+  if (d->T < 0 || d->d <= 0 || d->L <= 0 || d->n <= 0 || d->k <= 0 || d->D <= 0 || d->n_shared < 0)
+    return LMOE_ERR_SHAPE;
+  if (d->L * 2 != d->d) return LMOE_ERR_SHAPE;  // latent is half the model width
+  if (d->d % 128 || d->D % 64) return LMOE_ERR_SHAPE;
+  if (d->n > 1024 || d->k > d->n || d->k > 64 || d->n_shared > 8) return LMOE_ERR_SHAPE;
+  if (d->L > 8192 || d->d > 65536 || d->D > 65536) return LMOE_ERR_SHAPE;
+  if (d->T * d->k >= (int64_t)1 << 31 || d->T >= (int64_t)1 << 31) return LMOE_ERR_SHAPE;
+  return LMOE_OK;
+}
+
+template <typename T, typename TO, int EPI, bool GATHER, bool GROUPED>
+hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
+  a.tiles_n = (int)cdiv(a.N, G_BN);
+  if (!GROUPED) a.tiles_m = (int)cdiv(a.M, G_BM);
+  a.n_logical = a.tiles_m * a.tiles_n;
+  if (a.n_logical == 0) return hipSuccess;
+  a.xcd_chunk = a.n_logical >= 1024 ? 8 : 1;
+  const int64_t grid = cdiv(a.n_logical, 8 * a.xcd_chunk) * 8 * a.xcd_chunk;
+  if (a.kb_len == 0) a.kb_len = a.K;
+  hipLaunchKernelGGL((gemm_kernel<T, TO, G_BM, G_BN, G_WM, G_WN, EPI, GATHER, GROUPED>), dim3((unsigned)grid),
+                     dim3(64 * G_WM * G_WN), G_LDS, st, a);
+  return hipGetLastError();
+}
+
+GemmArgs gargs() {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.beta1 = 4.0f;
+  a.beta2 = 25.0f;
+  return a;
+}
+
+template <typename T>
+hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T *y, int32_t *topk_idx,
+                       float *topk_w, float *scores, unsigned char *ws, hipStream_t st,
+                       void *const *ev = nullptr) {
+  const WsLayout Lw = layout(d, sizeof(T) == 2 ? LMOE_BF16 : LMOE_F32);
+  T *z = (T *)(ws + Lw.off[R_Z]);
+  int32_t *counts = (int32_t *)(ws + Lw.off[R_COUNTS]);
+  int32_t *offs = (int32_t *)(ws + Lw.off[R_OFFS]);
+  int32_t *row_token = (int32_t *)(ws + Lw.off[R_ROW_TOKEN]);
+  int32_t *slot_row = (int32_t *)(ws + Lw.off[R_SLOT_ROW]);
+  T *hid = (T *)(ws + Lw.off[R_HIDDEN]);
+  float *ush = (float *)(ws + Lw.off[R_USH]);
+  T *v = (T *)(ws + Lw.off[R_V]);
+  float *s = scores ? scores : (float *)(ws + Lw.off[R_SCORES]);
+  int32_t *idx = topk_idx ? topk_idx : (int32_t *)(ws + Lw.off[R_IDX]);
+  float *gw = topk_w ? topk_w : (float *)(ws + Lw.off[R_W]);
+  uint64_t *masks = (uint64_t *)(ws + Lw.off[R_MASKS]);
+  int32_t *cbase = (int32_t *)(ws + Lw.off[R_CBASE]);
+  int4 *tiles = (int4 *)(ws + Lw.off[R_TILES]);
+  int32_t *ntiles = (int32_t *)(ws + Lw.off[R_NTILES]);
+  float *row_w = (float *)(ws + Lw.off[R_ROW_W]);
+  T *hsh = (T *)(ws + Lw.off[R_HSH]);
+  T *ystage = (T *)(ws + Lw.off[R_YSTAGE]);
+  const int T_ = (int)d.T, n = (int)d.n, k = (int)d.k, L = (int)d.L, D = (int)d.D, ns = (int)d.n_shared;
+  hipError_t e;
+#define LMOE_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
+#define LMOE_MARK(i) do { if (ev) LMOE_TRY(hipEventRecord((hipEvent_t)ev[i], st)); } while (0)
+
+  // 1 z = x W_down^T
+  LMOE_MARK(0);
+  {
+    GemmArgs a = gargs();
+    a.A = x; a.lda = d.d; a.B = w.w_down; a.ldb = d.d; a.C = z; a.ldc = L;
+    a.M = T_; a.N = L; a.K = (int)d.d;
+    LMOE_TRY((launch_gemm<T, T, EPI_STORE, false, false>(a, st)));
+  }
+  // 2 s = sigmoid(z W_r^T + o)
+  LMOE_MARK(1);
+  {
+    GemmArgs a = gargs();
+    a.A = z; a.lda = L; a.B = w.w_router; a.ldb = L; a.C = s; a.ldc = n;
+    a.M = T_; a.N = n; a.K = L; a.col_bias = w.router_logit_offset;
+    LMOE_TRY((launch_gemm<T, float, EPI_SIGMOID, false, false>(a, st)));
+  }
+  // 3 top-k + routing weights
+  LMOE_MARK(2);
+  {
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(d.T, 4), 65536);
+    if (n <= 64) hipLaunchKernelGGL(topk_kernel<1>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
+    else if (n <= 128) hipLaunchKernelGGL(topk_kernel<2>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
+    else if (n <= 256) hipLaunchKernelGGL(topk_kernel<4>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
+    else if (n <= 512) hipLaunchKernelGGL(topk_kernel<8>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
+    else hipLaunchKernelGGL(topk_kernel<16>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
+    LMOE_TRY(hipGetLastError());
+  }
+  // 4 permutation
+  LMOE_MARK(3);
+  {
+    const int nch = (int)cdiv(d.T, PERM_CHUNK);
+    hipLaunchKernelGGL(perm_mask_kernel, dim3(nch), dim3(PERM_CHUNK), (size_t)n * 32, st, idx, T_, n, k, masks, cbase);
+    LMOE_TRY(hipGetLastError());
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cbase, nch, n, G_BM, counts, offs, tiles, ntiles);
+    LMOE_TRY(hipGetLastError());
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch), dim3(PERM_CHUNK), 0, st, idx, gw, T_, n, k, masks, cbase,
+                       row_token, row_w, slot_row);
+    LMOE_TRY(hipGetLastError());
+  }
+  // 5 shared experts' gated hidden: [T, ns*D]
+  LMOE_MARK(4);
+  if (ns > 0) {
+    GemmArgs a = gargs();
+    a.A = z; a.lda = L; a.B = w.ws1; a.B2 = w.ws2; a.ldb = L; a.C = hsh; a.ldc = (int64_t)ns * D;
+    a.M = T_; a.N = 2 * ns * D; a.K = L; a.beta1 = w.beta1; a.beta2 = w.beta2;
+    LMOE_TRY((launch_gemm<T, T, EPI_GLU, false, false>(a, st)));
+  }
+  // 6 routed experts' gated hidden: [T*k, D] in dispatched order
+  LMOE_MARK(5);
+  {
+    GemmArgs a = gargs();
+    a.A = z; a.lda = L; a.a_rows = row_token; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
+    a.b_group_stride = (int64_t)D * L; a.C = hid; a.ldc = D;
+    a.N = 2 * D; a.K = L; a.tiles = tiles; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d);
+    a.beta1 = w.beta1; a.beta2 = w.beta2;
+    LMOE_TRY((launch_gemm<T, T, EPI_GLU, true, true>(a, st)));
+  }
+  // 7 shared W3 (the shared experts summed through one K = ns*D contraction)
+  LMOE_MARK(6);
+  if (ns > 0) {
+    GemmArgs a = gargs();
+    a.A = hsh; a.lda = (int64_t)ns * D; a.B = w.ws3; a.ldb = D; a.kb_len = D; a.kb_stride = (int64_t)L * D;
+    a.C = ush; a.ldc = L; a.M = T_; a.N = L; a.K = ns * D;
+    LMOE_TRY((launch_gemm<T, float, EPI_STORE, false, false>(a, st)));
+  }
+  // 8 routed W3, scaled by g, one row per dispatched (token, slot)
+  LMOE_MARK(7);
+  {
+    GemmArgs a = gargs();
+    a.A = hid; a.lda = D; a.B = w.w3; a.ldb = D; a.b_group_stride = (int64_t)L * D;
+    a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles; a.ntiles = ntiles;
+    a.tiles_m = (int)max_tiles(d); a.row_scale = row_w;
+    LMOE_TRY((launch_gemm<T, T, EPI_ROWSCALE, false, true>(a, st)));
+  }
+  // 9 combine + RMSNorm
+  LMOE_MARK(8);
+  {
+    const int nch8 = L / 8;
+    const float *us = ns > 0 ? ush : nullptr;
+    const T *gain = (const T *)w.rms_gain;
+    if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, 1>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
+    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, 2>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
+    else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, 4>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
+    LMOE_TRY(hipGetLastError());
+  }
+  // 10 y = v W_up^T
+  LMOE_MARK(9);
+  {
+    GemmArgs a = gargs();
+    a.A = v; a.lda = L; a.B = w.w_up; a.ldb = L; a.C = y; a.ldc = d.d;
+    a.M = T_; a.N = (int)d.d; a.K = L;
+    LMOE_TRY((launch_gemm<T, T, EPI_STORE, false, false>(a, st)));
+  }
+  LMOE_MARK(10);
+#undef LMOE_MARK
+#undef LMOE_TRY
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lmoe_workspace_size(const lmoe_dims *dims, int dtype) {
+  if (check_dims(dims) != LMOE_OK || (dtype != LMOE_F32 && dtype != LMOE_BF16)) return 0;
+  return (size_t)layout(*dims, dtype).total;
+}
+
+int64_t lmoe_workspace_offset(const lmoe_dims *dims, int dtype, int region) {
+  if (check_dims(dims) != LMOE_OK || (dtype != LMOE_F32 && dtype != LMOE_BF16)) return -1;
+  if (region < LMOE_WS_Z || region > LMOE_WS_V) return -1;
+  return layout(*dims, dtype).off[region];
+}
+
+static int forward_impl(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
+                        int32_t *topk_idx, float *topk_w, float *scores, void *workspace, size_t workspace_bytes,
+                        void *stream, void *const *events) {
+  int rc = check_dims(dims);
+  if (rc != LMOE_OK) return rc;
+  if (!w) return LMOE_ERR_NULL;
+  if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
+  if (!(w->beta1 > 0.0f) || !(w->beta2 > 0.0f) || !(w->rms_eps >= 0.0f) || w->rms_eps == INFINITY)
+    return LMOE_ERR_VALUE;
+  if (dims->T == 0) return LMOE_OK;
+  if (!x || !y || !workspace || !w->w_down || !w->w_router || !w->router_bias || !w->w1 || !w->w2 || !w->w3 ||
+      !w->rms_gain || !w->w_up)
+    return LMOE_ERR_NULL;
+  if (dims->n_shared > 0 && (!w->ws1 || !w->ws2 || !w->ws3)) return LMOE_ERR_NULL;
+  if (dims->n_shared == 0 && (w->ws1 || w->ws2 || w->ws3)) return LMOE_ERR_SHAPE;
+  const void *ptrs[] = {x, y, workspace, w->w_down, w->w_router, w->router_bias, w->router_logit_offset,
+                        w->w1, w->w2, w->w3, w->ws1, w->ws2, w->ws3, w->rms_gain, w->w_up,
+                        topk_idx, topk_w, scores};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return LMOE_ERR_ALIGN;
+  if (workspace_bytes < (size_t)layout(*dims, dtype).total) return LMOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (dtype == LMOE_BF16)
+    e = run_forward<bf16>(*dims, *w, (const bf16 *)x, (bf16 *)y, topk_idx, topk_w, scores,
+                          (unsigned char *)workspace, st, events);
+  else
+    e = run_forward<float>(*dims, *w, (const float *)x, (float *)y, topk_idx, topk_w, scores,
+                           (unsigned char *)workspace, st, events);
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
+}
+
+int lmoe_forward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
+                 int32_t *topk_idx, float *topk_w, float *scores, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+  return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, workspace, workspace_bytes, stream,
+                      nullptr);
+}
+
+int lmoe_forward_timed(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
+                       int32_t *topk_idx, float *topk_w, float *scores, void *workspace, size_t workspace_bytes,
+                       void *const *events, int n_events, void *stream) {
+  if (!events) return LMOE_ERR_NULL;
+  if (n_events != LMOE_N_STAGES + 1) return LMOE_ERR_VALUE;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return LMOE_ERR_NULL;
+  return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, workspace, workspace_bytes, stream, events);
+}
+
+size_t lmoe_qb_workspace_size(int32_t nbins) {
+  if (nbins < 1 || nbins > 16384) return 0;
+  return (size_t)align256((int64_t)nbins * 8);
+}
+
+int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
+                   int accumulate, float *bias, int solve, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+  if (T < 0 || n < 1 || n > ((int64_t)1 << 30) || k < 1 || k > n) return LMOE_ERR_SHAPE;
+  if (nbins < 1 || nbins > 16384) return LMOE_ERR_VALUE;
+  if (!hist || (T > 0 && !scores) || (solve && (!bias || !workspace))) return LMOE_ERR_NULL;
+  if (!aligned16(hist) || (scores && !aligned16(scores)) || (bias && !aligned16(bias)) ||
+      (workspace && !aligned16(workspace)))
+    return LMOE_ERR_ALIGN;
+  if (solve && workspace_bytes < lmoe_qb_workspace_size(nbins)) return LMOE_ERR_WORKSPACE;
+  if (n * nbins >= ((int64_t)1 << 40)) return LMOE_ERR_SHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  const int ni = (int)n, kb = nbins;
+  if (!accumulate) {
+    const int64_t cnt = n * nbins;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(cnt, 256), 4096)), dim3(256), 0, st,
+                       hist, cnt, 0);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+  }
+  if (T > 0) {
+    // experts per work-group: as many B-bin LDS histograms as fit in 64 KB (max 16)
+    int eg = (int)std::min<int64_t>(16, std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4)));
+    const int64_t groups = cdiv(n, eg);
+    // token runs: aim for ~4 work-groups per CU in total
+    int64_t runs = std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, groups), cdiv(T, 256)));
+    const int64_t tpb = cdiv(T, runs);
+    runs = cdiv(T, tpb);
+    if (groups > 65535 || runs > 65535) return LMOE_ERR_SHAPE;
+    hipLaunchKernelGGL(qb_hist_kernel, dim3((unsigned)groups, (unsigned)runs), dim3(256),
+                       (size_t)eg * nbins * 4, st, scores, T, ni, kb, eg, tpb, hist);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+  }
+  if (solve) {
+    long long *pooled = (long long *)workspace;
+    hipLaunchKernelGGL(qb_pool_kernel, dim3((unsigned)cdiv(nbins, 64)), dim3(256), 0, st, hist, ni, kb, pooled);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+    hipLaunchKernelGGL(qb_solve_kernel, dim3((unsigned)cdiv(n, 4)), dim3(256), 0, st, hist, pooled, ni, kb, (int)k,
+                       bias);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+  }
+  return LMOE_OK;
+}
+
+const char *lmoe_strerror(int status) {
+  switch (status) {
+    case LMOE_OK: return "ok";
+    case LMOE_ERR_NULL: return "a required pointer is NULL";
+    case LMOE_ERR_SHAPE: return "dimensions violate the layer's or the kernels' rules";
+    case LMOE_ERR_DTYPE: return "unknown work dtype";
+    case LMOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case LMOE_ERR_WORKSPACE: return "workspace smaller than required";
+    case LMOE_ERR_HIP: return "a HIP launch or runtime call failed";
+    case LMOE_ERR_VALUE: return "a scalar argument is out of range";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// Router top-k and token permutation kernels.
+//
+// Top-k ("Kimi K3 Architecture Deep Dive" §3: 896-choose-16 with a loss-free
+// selection bias; LeiPhone report "Keeping the numbers in range": the bias
+// steers selection): one wavefront per token.  Lane l holds experts
+// l, l+64, ... as 64-bit keys (order-preserving bits of s+b, then the
+// complemented expert index), so a single max-reduction picks the largest
+// biased score and, among equal scores, the lowest index.  k rounds of
+// "local max -> wave max -> winner drops it" give the k largest without
+// sorting the n scores.  Routing weights renormalise the unbiased scores of
+// the chosen experts.
+//
+// Permutation (dispatch of tokens to experts, rows ordered by expert then
+// token): tokens are cut into chunks of 256.  For each chunk and expert a
+// 256-bit mask of the tokens that chose the expert is built in LDS; a single
+// scan work-group turns mask popcounts into per-(chunk, expert) bases and the
+// global expert offsets, and writes the grouped-GEMM tile table; the scatter
+// kernel then places (token, slot) at base + popcount(mask bits below the
+// token).  Every step is integer and deterministic.
+#pragma once
+#include "common.hpp"
+
+namespace lmoe {
+
+constexpr int PERM_CHUNK = 256;  // tokens per permutation chunk (4 mask words)
+
+LMOE_DEV uint32_t ord_f32(float f) {
+  f = f + 0.0f;  // -0 -> +0
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0u;  // NaN ranks lowest
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+LMOE_DEV uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+template <int MAXJ>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ s, const float *__restrict__ bias,
+                                                   int T, int n, int k, int32_t *__restrict__ idx_out,
+                                                   float *__restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  for (int t = wave; t < T; t += nwaves) {
+    const float *row = s + (int64_t)t * n;
+    uint64_t key[MAXJ];
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int e = lane + 64 * j;
+      key[j] = 0;  // padding ranks below every real expert (NaN included)
+      if (e < n) key[j] = ((uint64_t)ord_f32(row[e] + bias[e]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+    }
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) best = key[j] > best ? key[j] : best;
+    int my_e = 0;
+    for (int r = 0; r < k; ++r) {
+      const uint64_t g = wave_max_u64(best);
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)g);
+      if (lane == r) my_e = e;
+      if (best == g) {  // the owning lane drops the winner and refreshes its max
+        best = 0;
+#pragma unroll
+        for (int j = 0; j < MAXJ; ++j) {
+          if (key[j] == g) key[j] = 0;
+          best = key[j] > best ? key[j] : best;
+        }
+      }
+    }
+    const float sv = lane < k ? row[my_e] : 0.0f;
+    const float tot = wave_sum(sv);
+    if (lane < k) {
+      idx_out[(int64_t)t * k + lane] = my_e;
+      w_out[(int64_t)t * k + lane] = sv / tot;
+    }
+  }
+}
+
+// masks[chunk][e][4] (uint64), ccount[chunk][e] (int32)
+__global__ __launch_bounds__(256) void perm_mask_kernel(const int32_t *__restrict__ idx, int T, int n, int k,
+                                                        uint64_t *__restrict__ masks,
+                                                        int32_t *__restrict__ ccount) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  unsigned long long *m = (unsigned long long *)smem_raw;  // [n][4]
+  const int c = blockIdx.x;
+  for (int i = threadIdx.x; i < n * 4; i += blockDim.x) m[i] = 0ull;
+  __syncthreads();
+  const int tl = threadIdx.x;
+  const int t = c * PERM_CHUNK + tl;
+  if (t < T) {
+    for (int r = 0; r < k; ++r) {
+      const int e = idx[(int64_t)t * k + r];
+      atomicOr(&m[e * 4 + (tl >> 6)], 1ull << (tl & 63));
+    }
+  }
+  __syncthreads();
+  uint64_t *gm = masks + (int64_t)c * n * 4;
+  for (int i = threadIdx.x; i < n * 4; i += blockDim.x) gm[i] = m[i];
+  for (int e = threadIdx.x; e < n; e += blockDim.x)
+    ccount[(int64_t)c * n + e] = __popcll(m[e * 4]) + __popcll(m[e * 4 + 1]) + __popcll(m[e * 4 + 2]) +
+                                 __popcll(m[e * 4 + 3]);
+}
+
+// Single work-group: per-(chunk, expert) bases, expert counts/offsets, tile table.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ cbase /* in: counts, out: bases */,
+                                                         int nchunks, int n, int bm, int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offs, int4 *__restrict__ tiles,
+                                                         int32_t *__restrict__ ntiles) {
+  __shared__ int32_t s_tot[1024];
+  __shared__ int32_t s_til[1024];
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < n) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int64_t i = (int64_t)c * n + e;
+      const int v = cbase[i];
+      cbase[i] = tot;
+      tot += v;
+    }
+  }
+  const int til = (tot + bm - 1) / bm;
+  s_tot[e] = e < n ? tot : 0;
+  s_til[e] = e < n ? til : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scans over 1024 entries
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int a = e >= o ? s_tot[e - o] : 0;
+    const int b = e >= o ? s_til[e - o] : 0;
+    __syncthreads();
+    s_tot[e] += a;
+    s_til[e] += b;
+    __syncthreads();
+  }
+  if (e < n) {
+    const int off = s_tot[e] - tot;
+    const int tstart = s_til[e] - til;
+    counts[e] = tot;
+    offs[e] = off;
+    if (e == n - 1) {
+      offs[n] = s_tot[e];
+      *ntiles = s_til[e];
+    }
+    for (int c = 0; c < nchunks; ++c) cbase[(int64_t)c * n + e] += off;
+    for (int j = 0; j < til; ++j) {
+      const int r0 = off + j * bm;
+      tiles[tstart + j] = make_int4(e, r0, min(r0 + bm, off + tot), 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__restrict__ idx,
+                                                           const float *__restrict__ w, int T, int n, int k,
+                                                           const uint64_t *__restrict__ masks,
+                                                           const int32_t *__restrict__ cbase,
+                                                           int32_t *__restrict__ row_token,
+                                                           float *__restrict__ row_w,
+                                                           int32_t *__restrict__ slot_row) {
+  const int c = blockIdx.x;
+  const int tl = threadIdx.x;
+  const int t = c * PERM_CHUNK + tl;
+  if (t >= T) return;
+  const int wsel = tl >> 6;
+  const uint64_t below = (1ull << (tl & 63)) - 1ull;
+  for (int r = 0; r < k; ++r) {
+    const int64_t f = (int64_t)t * k + r;
+    const int e = idx[f];
+    const uint64_t *m = masks + ((int64_t)c * n + e) * 4;
+    int rank = __popcll(m[wsel] & below);
+    for (int q = 0; q < wsel; ++q) rank += __popcll(m[q]);
+    const int pos = cbase[(int64_t)c * n + e] + rank;
+    row_token[pos] = t;
+    row_w[pos] = w[f];
+    slot_row[f] = pos;
+  }
+}
+
+}  // namespace lmoe

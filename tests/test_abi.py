@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every declared entry point, sizes its
+workspace and rejects invalid arguments before launching anything (no GPU
+needed: every call here fails validation or is a no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_down_amd as lmoe
+from sparse_moe_layer_down_amd._abi import Dims, Weights, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_header_declarations_are_exported():
+    hdr = open(os.path.join(ROOT, "include", "lmoe.h")).read()
+    declared = set(re.findall(r"^\S[^\n(]*?\b(lmoe_\w+)\(", hdr, flags=re.M))
+    assert declared == set(lmoe.EXPORTS)
+    L = lib()
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def c2dims(**kw):
+    d = dict(T=8192, d=7168, L=3584, n=896, k=16, n_shared=2, D=512)
+    d.update(kw)
+    return Dims(*[d[f] for f in ("T", "d", "L", "n", "k", "n_shared", "D")])
+
+
+def test_workspace_size():
+    ws = lmoe.workspace_size(c2dims(), lmoe.LMOE_BF16)
+    assert 1.0e9 < ws < 2.0e9
+    assert lmoe.workspace_size(c2dims(L=1000), lmoe.LMOE_BF16) == 0
+    assert lmoe.workspace_size(c2dims(), 7) == 0
+    # regions are 256-byte aligned and inside the workspace
+    for r in range(8):
+        off = lib().lmoe_workspace_offset(c2dims(), 1, r)
+        assert off >= 0 and off % 256 == 0 and off < ws
+    assert lib().lmoe_workspace_offset(c2dims(), 1, 99) == -1
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def fake_weights(n_shared=2, **over):
+    vals = dict(w_down=FAKE, w_router=FAKE, router_bias=FAKE, router_logit_offset=None, w1=FAKE, w2=FAKE,
+                w3=FAKE, ws1=FAKE if n_shared else None, ws2=FAKE if n_shared else None,
+                ws3=FAKE if n_shared else None, rms_gain=FAKE, w_up=FAKE, beta1=4.0, beta2=25.0, rms_eps=1e-6)
+    vals.update(over)
+    return Weights(*[vals[f] for f, _ in Weights._fields_])
+
+
+def call(dims, w, dtype=1, x=FAKE, y=FAKE, ws=FAKE, wsb=1 << 40):
+    return lib().lmoe_forward(ctypes.byref(dims), ctypes.byref(w), dtype, x, y, None, None, None, ws, wsb, None)
+
+
+@pytest.mark.parametrize("dims,code", [
+    (c2dims(L=3000), -2), (c2dims(k=0), -2), (c2dims(k=897), -2), (c2dims(n=2000), -2),
+    (c2dims(d=7000, L=3500), -2), (c2dims(D=500), -2), (c2dims(T=-1), -2), (c2dims(k=65, n=896), -2),
+])
+def test_shape_errors(dims, code):
+    assert call(dims, fake_weights()) == code
+
+
+def test_other_errors():
+    d = c2dims()
+    assert call(d, fake_weights(), dtype=5) == -3
+    assert call(d, fake_weights(w1=None)) == -1
+    assert call(d, fake_weights(), x=None) == -1
+    assert call(d, fake_weights(ws3=None)) == -1
+    assert call(c2dims(n_shared=0), fake_weights(n_shared=2)) == -2
+    assert call(d, fake_weights(w3=FAKE + 8)) == -4
+    assert call(d, fake_weights(), wsb=1000) == -5
+    assert call(d, fake_weights(beta1=0.0)) == -7
+    assert call(d, fake_weights(rms_eps=-1.0)) == -7
+    assert lib().lmoe_forward(None, ctypes.byref(fake_weights()), 1, FAKE, FAKE, None, None, None, FAKE, 1, None) == -1
+
+
+def test_empty_batch_is_a_noop():
+    assert call(c2dims(T=0), fake_weights(), x=None, y=None, ws=None, wsb=0) == 0
+
+
+def test_qb_validation():
+    q = lib().lmoe_qb_update
+    assert q(FAKE, 10, 896, 0, 1000, FAKE, 0, FAKE, 1, FAKE, 1 << 20, None) == -2   # k = 0
+    assert q(FAKE, 10, 896, 16, 0, FAKE, 0, FAKE, 1, FAKE, 1 << 20, None) == -7     # no bins
+    assert q(FAKE, 10, 896, 16, 1000, None, 0, FAKE, 1, FAKE, 1 << 20, None) == -1  # no histogram
+    assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, None, 1, FAKE, 1 << 20, None) == -1  # solve without bias
+    assert q(FAKE, 10, 896, 16, 1000, FAKE + 4, 0, FAKE, 1, FAKE, 1 << 20, None) == -4
+    assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, FAKE, 1, FAKE, 16, None) == -5
+    assert lmoe.qb_workspace_size(1000) == 8192
+    assert lmoe.qb_workspace_size(0) == 0
+
+
+def test_strerror():
+    assert lmoe.strerror(-5).startswith("workspace")
+    assert lmoe.strerror(123) == "unknown status"
