@@ -14,7 +14,7 @@
 //   5 gemm   shared experts' gated hidden (dense, SiTU-GLU epilogue)
 //   6 gemm   routed experts' gated hidden (grouped, gathered rows, SiTU-GLU)
 //   7 gemm   shared W3 -> u_shared (fp32)
-//   8 gemm   routed W3, scaled by g -> one row per (token, slot)
+//   8 gemm   routed W3, scaled by g -> one fp32 row per (token, slot)
 //   9 norm   u = u_shared + sum of the token's k rows; v = RMSNorm(u)
 //  10 gemm   y = v W_up^T
 #include <hip/hip_runtime.h>
@@ -72,7 +72,7 @@ WsLayout layout(const lmoe_dims &d, int dtype) {
   sz[R_NTILES] = 4;
   sz[R_ROW_W] = d.T * d.k * 4;
   sz[R_HSH] = d.T * d.n_shared * d.D * es;
-  sz[R_YSTAGE] = d.T * d.k * d.L * es;
+  sz[R_YSTAGE] = d.T * d.k * d.L * 4;  // fp32: per-slot rows are summed before any rounding
   WsLayout w;
   int64_t o = 0;
   for (int i = 0; i < R_COUNT_; ++i) {
@@ -141,7 +141,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   int32_t *ntiles = (int32_t *)(ws + Lw.off[R_NTILES]);
   float *row_w = (float *)(ws + Lw.off[R_ROW_W]);
   T *hsh = (T *)(ws + Lw.off[R_HSH]);
-  T *ystage = (T *)(ws + Lw.off[R_YSTAGE]);
+  float *ystage = (float *)(ws + Lw.off[R_YSTAGE]);
   const int T_ = (int)d.T, n = (int)d.n, k = (int)d.k, L = (int)d.L, D = (int)d.D, ns = (int)d.n_shared;
   hipError_t e;
 #define LMOE_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
@@ -219,7 +219,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     a.A = hid; a.lda = D; a.B = w.w3; a.ldb = D; a.b_group_stride = (int64_t)L * D;
     a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles; a.ntiles = ntiles;
     a.tiles_m = (int)max_tiles(d); a.row_scale = row_w;
-    LMOE_TRY((launch_gemm<T, T, EPI_ROWSCALE, false, true>(a, st)));
+    LMOE_TRY((launch_gemm<T, float, EPI_ROWSCALE, false, true>(a, st)));
   }
   // 9 combine + RMSNorm
   LMOE_MARK(8);

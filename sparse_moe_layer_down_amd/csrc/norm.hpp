@@ -1,6 +1,6 @@
 // Combine + RMSNorm: the aggregated latent of token t is the shared-expert part
-// (fp32, written by the shared W3 GEMM) plus the k routed rows of t, each
-// already scaled by its routing weight in the W3 epilogue.  The single
+// (fp32, written by the shared W3 GEMM) plus the k routed rows of t (fp32, each
+// already scaled by its routing weight in the W3 epilogue).  The single
 // retained RMSNorm then gives v = gain * u / sqrt(mean(u^2) + eps)
 // ("Kimi K3 Architecture Deep Dive" §2: one RMS norm before the
 // up-projection; LeiPhone report "Keeping the numbers in range": after
@@ -13,7 +13,7 @@ namespace lmoe {
 
 template <typename T, int CPT>
 __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float *__restrict__ ushared,
-                                                              const T *__restrict__ ystage,
+                                                              const float *__restrict__ ystage,
                                                               const int32_t *__restrict__ slot_row,
                                                               const T *__restrict__ gain, T *__restrict__ v,
                                                               int L, int k, float eps) {

@@ -98,17 +98,24 @@ def check_dispatch(cfg, gpu):
 
 
 def check_hidden(cfg, gpu, P, x_host):
-    """Gated hidden of every dispatched row vs the oracle's expert_hidden on the GPU's z rows."""
+    """Gated hidden of every dispatched row vs the oracle's unrounded SiTU-GLU on the GPU's z rows.
+
+    Elementwise bound from the arithmetic: the store rounding (half an ulp:
+    2^-9 |a| in bf16, 2^-24 |a| in fp32) plus fp32 dot-product and tanh/exp
+    error, far below 1e-3 of the expert's RMS in bf16 and 1e-5 in fp32.  (A
+    max-norm bound relative to the RMS does not fit this heavy-tailed tensor:
+    half an ulp of an element above 10 RMS is already more than 2e-2 RMS.)
+    """
     z = gpu["z"]
-    errs = []
+    rel, floor = (2.0 ** -8, 1e-3) if cfg.dtype == "bf16" else (1e-6, 1e-5)
     for e in range(cfg.n):
         lo, hi = gpu["offs"][e], gpu["offs"][e + 1]
         if lo == hi:
             continue
         toks = gpu["row_token"][lo:hi]
         a = ref.expert_hidden(z[toks], P.w1(e), P.w2(e), cfg.beta1, cfg.beta2, "f64")
-        errs.append(np.abs(gpu["hidden"][lo:hi] - a).max() / max(np.sqrt(np.mean(a ** 2)), 1e-30))
-    assert max(errs) <= tol(cfg.dtype)
+        rms = np.sqrt(np.mean(a ** 2))
+        assert np.all(np.abs(gpu["hidden"][lo:hi] - a) <= rel * np.abs(a) + floor * rms), f"expert {e}"
     assert np.all(np.abs(gpu["hidden"]) <= cfg.beta1 * cfg.beta2)
 
 
