@@ -28,7 +28,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=64)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel of known "
+                         "size whose memory counters calibrate the byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -109,6 +112,14 @@ def main():
         torch.cuda.synchronize()
         stage_ms += np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(lmoe.N_STAGES)])
     stage_ms /= args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     counts = lmoe.workspace_view(ws, dims, x.dtype, "counts").cpu().numpy()
     flops = cfg.flops_per_token() * cfg.T

@@ -16,8 +16,9 @@
 //   EPI_ROWSCALE  C[row] = row_scale[row] * acc            (routing weight g)
 //
 // Tiling: BM x BN output tile per work-group of WM x WN waves; BK = 128 bytes
-// of K per step (64 bf16 or 32 fp32).  Operands go global -> registers -> LDS,
-// double buffered; LDS rows are 128 B with the 16-B chunks XOR-swizzled by
+// of K per step (64 bf16 or 32 fp32).  Operands go global -> registers -> LDS;
+// the global loads run PF steps ahead through a ring of register sets and LDS
+// is double buffered; LDS rows are 128 B with the 16-B chunks XOR-swizzled by
 // (row & 7) so the MFMA fragment reads of 32 rows at one K offset spread
 // over all banks.  bf16 uses v_mfma_f32_32x32x16_bf16 (each lane holds 8
 // consecutive K of one row); fp32 uses v_mfma_f32_32x32x2_f32, eight per
@@ -78,28 +79,46 @@ template <> struct Mma<float> {
   }
 };
 
-LMOE_DEV int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// LDS address of 16-B chunk c of tile row r (rows of 128 B).  The chunk is
+// XOR-swizzled so that an MFMA fragment read (one chunk column, 32 consecutive
+// rows, 16 B per lane) has no bank conflict whether the LDS serves 8 or 16
+// lanes per pass: any 8 consecutive rows get 8 distinct chunk slots, and within
+// any 16 consecutive rows the even and the odd rows each get 8 distinct slots.
+LMOE_DEV int swz(int r, int c) { return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4); }
 
-template <typename T, typename TO, int BM, int BN, int WM, int WN, int EPI, bool GATHER, bool GROUPED>
+template <int V> struct IC { static constexpr int value = V; };
+
+// Tile configuration: BM x BN outputs per work-group of WM x WN waves; PF =
+// how many K steps ahead the B (weight) loads run (a ring of PF register
+// sets); A loads run one step ahead.  M subtiles of 32 rows are interleaved over the
+// wave rows (wave wm owns subtiles wm, wm + WM, ...) so that a partially
+// filled M tile still spreads its valid rows over the waves.
+template <typename T, typename TO, int BM, int BN, int WM, int WN, int PF, int EPI, bool GATHER, bool GROUPED>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WM * WN;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int WTN = BN / WN;
+  constexpr int TM = BM / WM / 32, TN = WTN / 32;
   constexpr int BKE = 128 / (int)sizeof(T);
   constexpr int CPL = Mma<T>::CPL;
   constexpr int NG = BKE / 16;
   constexpr int RPP = NT / 8;  // rows covered per load pass (8 threads x 16 B per row)
   constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
   constexpr int EPT = 16 / (int)sizeof(T);  // elements per 16-B chunk
+  constexpr int NSET = PF;  // B register sets: B(j) lives in set j % PF
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of the load pass");
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(BM % (32 * WM) == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(EPI != EPI_GLU || TN % 2 == 0, "GLU needs W1/W2 subtile pairs");
+  static_assert(PF >= 1 && PF <= 3, "prefetch distance");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char *const sA0 = smem;
   unsigned char *const sB0 = smem + 2 * BM * 128;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform by construction; readfirstlane lets the compiler keep it (and
+  // everything derived from it) in scalar registers, so per-subtile tests branch
+  // on SCC instead of masking lanes
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- which tile
@@ -127,60 +146,63 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     rows_valid = min(BM, p.M - (int)m0);
   }
 
-  // ---- per-thread source rows
+  // ---- per-thread source rows (32-bit row indices; addresses are formed per K step).
+  // Rows past the valid range are clamped onto a valid row: they only feed
+  // output rows / columns that are never stored, and unconditional loads keep
+  // the K loop free of branches (whose joins force full vmcnt waits).
   const int lrow = tid >> 3, lchunk = tid & 7;
-  const T *a_src[A_LD];
-  bool a_ok[A_LD];
+  int a_row[A_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int r = lrow + i * RPP;
-    a_ok[i] = r < rows_valid;
-    int64_t src = m0 + r;
-    if (GATHER) src = a_ok[i] ? (int64_t)p.a_rows[m0 + r] : 0;
-    else if (!a_ok[i]) src = 0;
-    a_src[i] = (const T *)p.A + src * p.lda + lchunk * EPT;
+    const int r = min(lrow + i * RPP, rows_valid - 1);
+    a_row[i] = GATHER ? p.a_rows[m0 + r] : (int)(m0 + r);
   }
-  const T *b_src[B_LD];
-  bool b_ok[B_LD];
+  int b_row[B_LD];  // row of B (GLU: hidden unit)
+  bool b_w2[B_LD];  // GLU: row comes from W2
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int br = lrow + i * RPP;
-    int64_t row;
-    const T *base;
     if (EPI == EPI_GLU) {
       const int wcol = br / WTN, within = br % WTN, j = within / 32;
-      row = (int64_t)nt * (BN / 2) + wcol * (WTN / 2) + (j / 2) * 32 + (br & 31);
-      b_ok[i] = row < p.N / 2;
-      base = (const T *)((j & 1) ? p.B2 : p.B);
+      const int row = nt * (BN / 2) + wcol * (WTN / 2) + (j / 2) * 32 + (br & 31);
+      b_row[i] = min(row, p.N / 2 - 1);
+      b_w2[i] = (j & 1) != 0;
     } else {
-      row = (int64_t)nt * BN + br;
-      b_ok[i] = row < p.N;
-      base = (const T *)p.B;
+      b_row[i] = min(nt * BN + br, p.N - 1);
+      b_w2[i] = false;
     }
-    if (!b_ok[i]) row = 0;
-    b_src[i] = base + b_off + row * p.ldb + lchunk * EPT;
   }
+  const T *const Abase = (const T *)p.A + lchunk * EPT;
+  const T *const B1base = (const T *)p.B + b_off + lchunk * EPT;
+  const T *const B2base = (EPI == EPI_GLU) ? (const T *)p.B2 + b_off + lchunk * EPT : B1base;
 
   const int nk = p.K / BKE;
-  u32x4 ra[A_LD], rb[B_LD];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // B (weights) runs PF steps ahead through a ring of NSET register sets; A
+  // runs one step ahead in a single set (its source is usually L2-resident).
+  u32x4 ra[A_LD], rb[NSET][B_LD];
 
-  auto gload = [&](int kt) {
+  auto gloadB = [&](auto SETC, int kt) {
+    constexpr int S = decltype(SETC)::value;
     const int64_t k0 = (int64_t)kt * BKE;
     const int64_t s = k0 / p.kb_len;
     const int64_t boff = s * p.kb_stride + (k0 - s * p.kb_len);
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = a_ok[i] ? *(const u32x4 *)(a_src[i] + k0) : zero;
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = b_ok[i] ? *(const u32x4 *)(b_src[i] + boff) : zero;
+    for (int i = 0; i < B_LD; ++i)
+      rb[S][i] = *(const u32x4 *)((b_w2[i] ? B2base : B1base) + (int64_t)b_row[i] * p.ldb + boff);
   };
-  auto lstore = [&](int buf) {
+  auto gloadA = [&](int kt) {
+    const int64_t k0 = (int64_t)kt * BKE;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) ra[i] = *(const u32x4 *)(Abase + (int64_t)a_row[i] * p.lda + k0);
+  };
+  auto lstore = [&](auto SETC, int buf) {
+    constexpr int S = decltype(SETC)::value;
     unsigned char *sA = sA0 + buf * BM * 128;
     unsigned char *sB = sB0 + buf * BN * 128;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) *(u32x4 *)(sA + swz(lrow + i * RPP, lchunk)) = ra[i];
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) *(u32x4 *)(sB + swz(lrow + i * RPP, lchunk)) = rb[i];
+    for (int i = 0; i < B_LD; ++i) *(u32x4 *)(sB + swz(lrow + i * RPP, lchunk)) = rb[S][i];
   };
 
   f32x16 acc[TM][TN];
@@ -191,55 +213,91 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-  // wave-uniform: which M subtiles hold valid rows
-  bool tm_on[TM];
-#pragma unroll
-  for (int a = 0; a < TM; ++a) tm_on[a] = (wm * WTM + a * 32) < rows_valid;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // number of this wave's M subtiles (wm, wm + WM, ...) that hold valid rows
+  const int nsub = (rows_valid + 31) >> 5;
+  const int na = min(TM, max(0, (nsub - wm + WM - 1) / WM));
 
   const int half = lane >> 5, l32 = lane & 31;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  auto compute = [&](auto NAC, int buf) {
+    constexpr int NA = decltype(NAC)::value;
     const unsigned char *sA = sA0 + buf * BM * 128;
     const unsigned char *sB = sB0 + buf * BN * 128;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      u32x4 af[TM][CPL], bfg[TN][CPL];
-#pragma unroll
-      for (int a = 0; a < TM; ++a) {
-        const int r = wm * WTM + a * 32 + l32;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) af[a][c] = *(const u32x4 *)(sA + swz(r, g * 2 * CPL + half * CPL + c));
-      }
+      u32x4 bfg[TN][CPL];
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
         const int r = wn * WTN + b * 32 + l32;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) bfg[b][c] = *(const u32x4 *)(sB + swz(r, g * 2 * CPL + half * CPL + c));
       }
+      u32x4 af[TM][CPL];
 #pragma unroll
-      for (int a = 0; a < TM; ++a) {
-        if (GROUPED && !tm_on[a]) continue;
+      for (int a = 0; a < NA; ++a) {
+        const int r = (a * WM + wm) * 32 + l32;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) af[a][c] = *(const u32x4 *)(sA + swz(r, g * 2 * CPL + half * CPL + c));
+      }
+#pragma unroll
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
         for (int b = 0; b < TN; ++b) Mma<T>::run(af[a], bfg[b], acc[a][b]);
-      }
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
+  };
+
+  // Pipeline.  B(j), the weight slice of K step j, lives in register set
+  // j % PF; A(j) in the single A set.  Loads for the future are issued right
+  // after each barrier into the registers that were just stored to LDS:
+  // A(kt+2) first, then B(kt+1+PF).  vmcnt retires in issue order, so the LDS
+  // store of step kt+1 (A(kt+1), B(kt+1)) waits for nothing younger than
+  // B(kt+PF): the weights stay PF steps in flight, A one step.
+  gloadA(0);
+  gloadB(IC<0>{}, 0);
+  if (PF >= 2 && 1 < nk) gloadB(IC<1 % NSET>{}, 1);
+  if (PF >= 3 && 2 < nk) gloadB(IC<2 % NSET>{}, 2);
+  lstore(IC<0>{}, 0);
+  __syncthreads();
+  if (1 < nk) gloadA(1);
+  if (PF < nk) gloadB(IC<0>{}, PF);
+
+  // The loop is unrolled NSET times so every set index is static; the
+  // steady-state part carries no bounds tests.
+  auto kloop = [&](auto NAC) {
+    auto step = [&](auto SETC, auto CHECKC, int kt) {
+      constexpr int S1 = decltype(SETC)::value;  // == (kt + 1) % NSET
+      constexpr bool CHECK = decltype(CHECKC)::value != 0;
+      compute(NAC, kt & 1);
+      if (!CHECK || kt + 1 < nk) lstore(IC<S1>{}, (kt + 1) & 1);
+      __syncthreads();
+      if (!CHECK || kt + 2 < nk) gloadA(kt + 2);
+      if (!CHECK || kt + 1 + PF < nk) gloadB(IC<S1>{}, kt + 1 + PF);
+    };
+    int kt = 0;
+    for (; kt + NSET + PF + 1 <= nk; kt += NSET) {
+      step(IC<1 % NSET>{}, IC<0>{}, kt);
+      if (NSET > 1) step(IC<2 % NSET>{}, IC<0>{}, kt + 1);
+      if (NSET > 2) step(IC<3 % NSET>{}, IC<0>{}, kt + 2);
+    }
+    for (; kt < nk; kt += NSET) {
+      step(IC<1 % NSET>{}, IC<1>{}, kt);
+      if (NSET > 1 && kt + 1 < nk) step(IC<2 % NSET>{}, IC<1>{}, kt + 1);
+      if (NSET > 2 && kt + 2 < nk) step(IC<3 % NSET>{}, IC<1>{}, kt + 2);
+    }
+  };
+  // Every subtile is computed, valid rows or not (rows past the valid range
+  // hold copies of a valid row and are never stored): the K loop stays free
+  // of branches, and the MFMA time of a full tile is still below the time to
+  // stream its weights.
+  kloop(IC<TM>{});
 
   // ---- epilogue
   TO *C = (TO *)p.C;
 #pragma unroll
   for (int a = 0; a < TM; ++a) {
-    if (!tm_on[a]) continue;
+    if (a >= na) continue;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int rl = wm * WTM + a * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+      const int rl = (a * WM + wm) * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
       if (rl >= rows_valid) continue;
       const int64_t grow = m0 + rl;
       if (EPI == EPI_GLU) {

@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "../../include/lmoe.h"
 #include "gemm.hpp"
@@ -33,8 +34,16 @@ using namespace lmoe;
 
 namespace {
 
-constexpr int G_BM = 128, G_BN = 128, G_WM = 2, G_WN = 2;
-constexpr int G_LDS = 2 * (G_BM + G_BN) * 128;
+// Tile configurations (BM, BN, waves WM x WN, B prefetch distance PF).  Dense
+// GEMMs are MFMA-bound; the grouped expert GEMMs stream the expert bank from
+// HBM, with an M tile tall enough to cover a typical expert's rows so each
+// expert's weights are read once.
+template <int BM_, int BN_, int WM_, int WN_, int PF_> struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, PF = PF_;
+};
+using CfgDense = Cfg<256, 256, 2, 4, 1>;
+using CfgW12 = Cfg<192, 256, 2, 4, 2>;
+using CfgW3 = Cfg<192, 256, 2, 4, 2>;
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t align256(int64_t a) { return (a + 255) & ~(int64_t)255; }
@@ -46,10 +55,11 @@ struct WsLayout {
 
 enum {
   R_Z = 0, R_COUNTS, R_OFFS, R_ROW_TOKEN, R_SLOT_ROW, R_HIDDEN, R_USH, R_V,
-  R_SCORES, R_IDX, R_W, R_MASKS, R_CBASE, R_TILES, R_NTILES, R_ROW_W, R_HSH, R_YSTAGE, R_COUNT_
+  R_SCORES, R_IDX, R_W, R_MASKS, R_CBASE, R_TILES1, R_TILES2, R_NTILES, R_ROW_W, R_HSH, R_YSTAGE, R_COUNT_
 };
 
-int64_t max_tiles(const lmoe_dims &d) { return d.n + cdiv(d.T * d.k, G_BM); }
+// upper bound of sum_e ceil(count_e / bm) over any routing
+int64_t max_tiles(const lmoe_dims &d, int bm) { return d.n + cdiv(d.T * d.k, bm); }
 
 WsLayout layout(const lmoe_dims &d, int dtype) {
   const int64_t es = dtype == LMOE_BF16 ? 2 : 4;
@@ -68,8 +78,9 @@ WsLayout layout(const lmoe_dims &d, int dtype) {
   sz[R_W] = d.T * d.k * 4;
   sz[R_MASKS] = nch * d.n * 4 * 8;
   sz[R_CBASE] = nch * d.n * 4;
-  sz[R_TILES] = max_tiles(d) * 16;
-  sz[R_NTILES] = 4;
+  sz[R_TILES1] = max_tiles(d, CfgW12::BM) * 16;
+  sz[R_TILES2] = max_tiles(d, CfgW3::BM) * 16;
+  sz[R_NTILES] = 8;
   sz[R_ROW_W] = d.T * d.k * 4;
   sz[R_HSH] = d.T * d.n_shared * d.D * es;
   sz[R_YSTAGE] = d.T * d.k * d.L * 4;  // fp32: per-slot rows are summed before any rounding
@@ -97,17 +108,21 @@ int check_dims(const lmoe_dims *d) {
   return LMOE_OK;
 }
 
-template <typename T, typename TO, int EPI, bool GATHER, bool GROUPED>
+template <typename C, typename T, typename TO, int EPI, bool GATHER, bool GROUPED>
 hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
-  a.tiles_n = (int)cdiv(a.N, G_BN);
-  if (!GROUPED) a.tiles_m = (int)cdiv(a.M, G_BM);
+  constexpr int lds = 2 * (C::BM + C::BN) * 128;
+  auto kern = gemm_kernel<T, TO, C::BM, C::BN, C::WM, C::WN, C::PF, EPI, GATHER, GROUPED>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  a.tiles_n = (int)cdiv(a.N, C::BN);
+  if (!GROUPED) a.tiles_m = (int)cdiv(a.M, C::BM);
   a.n_logical = a.tiles_m * a.tiles_n;
   if (a.n_logical == 0) return hipSuccess;
   a.xcd_chunk = a.n_logical >= 1024 ? 8 : 1;
   const int64_t grid = cdiv(a.n_logical, 8 * a.xcd_chunk) * 8 * a.xcd_chunk;
   if (a.kb_len == 0) a.kb_len = a.K;
-  hipLaunchKernelGGL((gemm_kernel<T, TO, G_BM, G_BN, G_WM, G_WN, EPI, GATHER, GROUPED>), dim3((unsigned)grid),
-                     dim3(64 * G_WM * G_WN), G_LDS, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * C::WM * C::WN), lds, st, a);
   return hipGetLastError();
 }
 
@@ -137,7 +152,8 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   float *gw = topk_w ? topk_w : (float *)(ws + Lw.off[R_W]);
   uint64_t *masks = (uint64_t *)(ws + Lw.off[R_MASKS]);
   int32_t *cbase = (int32_t *)(ws + Lw.off[R_CBASE]);
-  int4 *tiles = (int4 *)(ws + Lw.off[R_TILES]);
+  int4 *tiles1 = (int4 *)(ws + Lw.off[R_TILES1]);
+  int4 *tiles2 = (int4 *)(ws + Lw.off[R_TILES2]);
   int32_t *ntiles = (int32_t *)(ws + Lw.off[R_NTILES]);
   float *row_w = (float *)(ws + Lw.off[R_ROW_W]);
   T *hsh = (T *)(ws + Lw.off[R_HSH]);
@@ -153,7 +169,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = x; a.lda = d.d; a.B = w.w_down; a.ldb = d.d; a.C = z; a.ldc = L;
     a.M = T_; a.N = L; a.K = (int)d.d;
-    LMOE_TRY((launch_gemm<T, T, EPI_STORE, false, false>(a, st)));
+    LMOE_TRY((launch_gemm<CfgDense, T, T, EPI_STORE, false, false>(a, st)));
   }
   // 2 s = sigmoid(z W_r^T + o)
   LMOE_MARK(1);
@@ -161,7 +177,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = z; a.lda = L; a.B = w.w_router; a.ldb = L; a.C = s; a.ldc = n;
     a.M = T_; a.N = n; a.K = L; a.col_bias = w.router_logit_offset;
-    LMOE_TRY((launch_gemm<T, float, EPI_SIGMOID, false, false>(a, st)));
+    LMOE_TRY((launch_gemm<CfgDense, T, float, EPI_SIGMOID, false, false>(a, st)));
   }
   // 3 top-k + routing weights
   LMOE_MARK(2);
@@ -180,7 +196,8 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     const int nch = (int)cdiv(d.T, PERM_CHUNK);
     hipLaunchKernelGGL(perm_mask_kernel, dim3(nch), dim3(PERM_CHUNK), (size_t)n * 32, st, idx, T_, n, k, masks, cbase);
     LMOE_TRY(hipGetLastError());
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cbase, nch, n, G_BM, counts, offs, tiles, ntiles);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cbase, nch, n, counts, offs, CfgW12::BM, tiles1,
+                       CfgW3::BM, tiles2, ntiles);
     LMOE_TRY(hipGetLastError());
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch), dim3(PERM_CHUNK), 0, st, idx, gw, T_, n, k, masks, cbase,
                        row_token, row_w, slot_row);
@@ -192,7 +209,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = z; a.lda = L; a.B = w.ws1; a.B2 = w.ws2; a.ldb = L; a.C = hsh; a.ldc = (int64_t)ns * D;
     a.M = T_; a.N = 2 * ns * D; a.K = L; a.beta1 = w.beta1; a.beta2 = w.beta2;
-    LMOE_TRY((launch_gemm<T, T, EPI_GLU, false, false>(a, st)));
+    LMOE_TRY((launch_gemm<CfgDense, T, T, EPI_GLU, false, false>(a, st)));
   }
   // 6 routed experts' gated hidden: [T*k, D] in dispatched order
   LMOE_MARK(5);
@@ -200,9 +217,9 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = z; a.lda = L; a.a_rows = row_token; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
     a.b_group_stride = (int64_t)D * L; a.C = hid; a.ldc = D;
-    a.N = 2 * D; a.K = L; a.tiles = tiles; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d);
+    a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, CfgW12::BM);
     a.beta1 = w.beta1; a.beta2 = w.beta2;
-    LMOE_TRY((launch_gemm<T, T, EPI_GLU, true, true>(a, st)));
+    LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU, true, true>(a, st)));
   }
   // 7 shared W3 (the shared experts summed through one K = ns*D contraction)
   LMOE_MARK(6);
@@ -210,16 +227,16 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = hsh; a.lda = (int64_t)ns * D; a.B = w.ws3; a.ldb = D; a.kb_len = D; a.kb_stride = (int64_t)L * D;
     a.C = ush; a.ldc = L; a.M = T_; a.N = L; a.K = ns * D;
-    LMOE_TRY((launch_gemm<T, float, EPI_STORE, false, false>(a, st)));
+    LMOE_TRY((launch_gemm<CfgDense, T, float, EPI_STORE, false, false>(a, st)));
   }
   // 8 routed W3, scaled by g, one row per dispatched (token, slot)
   LMOE_MARK(7);
   {
     GemmArgs a = gargs();
     a.A = hid; a.lda = D; a.B = w.w3; a.ldb = D; a.b_group_stride = (int64_t)L * D;
-    a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles; a.ntiles = ntiles;
-    a.tiles_m = (int)max_tiles(d); a.row_scale = row_w;
-    LMOE_TRY((launch_gemm<T, float, EPI_ROWSCALE, false, true>(a, st)));
+    a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles2; a.ntiles = ntiles + 1;
+    a.tiles_m = (int)max_tiles(d, CfgW3::BM); a.row_scale = row_w;
+    LMOE_TRY((launch_gemm<CfgW3, T, float, EPI_ROWSCALE, false, true>(a, st)));
   }
   // 9 combine + RMSNorm
   LMOE_MARK(8);
@@ -238,7 +255,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = v; a.lda = L; a.B = w.w_up; a.ldb = L; a.C = y; a.ldc = d.d;
     a.M = T_; a.N = (int)d.d; a.K = L;
-    LMOE_TRY((launch_gemm<T, T, EPI_STORE, false, false>(a, st)));
+    LMOE_TRY((launch_gemm<CfgDense, T, T, EPI_STORE, false, false>(a, st)));
   }
   LMOE_MARK(10);
 #undef LMOE_MARK

@@ -109,13 +109,17 @@ __global__ __launch_bounds__(256) void perm_mask_kernel(const int32_t *__restric
                                  __popcll(m[e * 4 + 3]);
 }
 
-// Single work-group: per-(chunk, expert) bases, expert counts/offsets, tile table.
+// Single work-group: per-(chunk, expert) bases, expert counts/offsets, and two
+// grouped-GEMM tile tables (M-tile heights bm1 and bm2): entry j of a table is
+// {expert, first row, end row} of one M tile; ntiles[0], ntiles[1] = lengths.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ cbase /* in: counts, out: bases */,
-                                                         int nchunks, int n, int bm, int32_t *__restrict__ counts,
-                                                         int32_t *__restrict__ offs, int4 *__restrict__ tiles,
+                                                         int nchunks, int n, int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offs, int bm1, int4 *__restrict__ tiles1,
+                                                         int bm2, int4 *__restrict__ tiles2,
                                                          int32_t *__restrict__ ntiles) {
   __shared__ int32_t s_tot[1024];
-  __shared__ int32_t s_til[1024];
+  __shared__ int32_t s_t1[1024];
+  __shared__ int32_t s_t2[1024];
   const int e = threadIdx.x;
   int tot = 0;
   if (e < n) {
@@ -126,32 +130,40 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ c
       tot += v;
     }
   }
-  const int til = (tot + bm - 1) / bm;
+  const int t1 = (tot + bm1 - 1) / bm1, t2 = (tot + bm2 - 1) / bm2;
   s_tot[e] = e < n ? tot : 0;
-  s_til[e] = e < n ? til : 0;
+  s_t1[e] = e < n ? t1 : 0;
+  s_t2[e] = e < n ? t2 : 0;
   __syncthreads();
   // inclusive Hillis-Steele scans over 1024 entries
   for (int o = 1; o < 1024; o <<= 1) {
     const int a = e >= o ? s_tot[e - o] : 0;
-    const int b = e >= o ? s_til[e - o] : 0;
+    const int b = e >= o ? s_t1[e - o] : 0;
+    const int c = e >= o ? s_t2[e - o] : 0;
     __syncthreads();
     s_tot[e] += a;
-    s_til[e] += b;
+    s_t1[e] += b;
+    s_t2[e] += c;
     __syncthreads();
   }
   if (e < n) {
     const int off = s_tot[e] - tot;
-    const int tstart = s_til[e] - til;
     counts[e] = tot;
     offs[e] = off;
     if (e == n - 1) {
       offs[n] = s_tot[e];
-      *ntiles = s_til[e];
+      ntiles[0] = s_t1[e];
+      ntiles[1] = s_t2[e];
     }
     for (int c = 0; c < nchunks; ++c) cbase[(int64_t)c * n + e] += off;
-    for (int j = 0; j < til; ++j) {
-      const int r0 = off + j * bm;
-      tiles[tstart + j] = make_int4(e, r0, min(r0 + bm, off + tot), 0);
+    const int s1 = s_t1[e] - t1, s2 = s_t2[e] - t2;
+    for (int j = 0; j < t1; ++j) {
+      const int r0 = off + j * bm1;
+      tiles1[s1 + j] = make_int4(e, r0, min(r0 + bm1, off + tot), 0);
+    }
+    for (int j = 0; j < t2; ++j) {
+      const int r0 = off + j * bm2;
+      tiles2[s2 + j] = make_int4(e, r0, min(r0 + bm2, off + tot), 0);
     }
   }
 }

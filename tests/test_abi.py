@@ -30,7 +30,8 @@ def c2dims(**kw):
 
 def test_workspace_size():
     ws = lmoe.workspace_size(c2dims(), lmoe.LMOE_BF16)
-    assert 1.0e9 < ws < 2.0e9
+    # dominated by the fp32 per-slot rows T*k*L*4 = 1.88 GB
+    assert 8192 * 16 * 3584 * 4 < ws < 2.5e9
     assert lmoe.workspace_size(c2dims(L=1000), lmoe.LMOE_BF16) == 0
     assert lmoe.workspace_size(c2dims(), 7) == 0
     # regions are 256-byte aligned and inside the workspace
