@@ -89,8 +89,7 @@ LMOE_DEV int swz(int r, int c) { return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)
 template <int V> struct IC { static constexpr int value = V; };
 
 // Tile configuration: BM x BN outputs per work-group of WM x WN waves; PF =
-// how many K steps ahead the B (weight) loads run (a ring of PF register
-// sets); A loads run one step ahead.  M subtiles of 32 rows are interleaved over the
+// how many K steps ahead the global loads run (PF register sets).  M subtiles of 32 rows are interleaved over the
 // wave rows (wave wm owns subtiles wm, wm + WM, ...) so that a partially
 // filled M tile still spreads its valid rows over the waves.
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int PF, int EPI, bool GATHER, bool GROUPED>
@@ -108,7 +107,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of the load pass");
   static_assert(BM % (32 * WM) == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(EPI != EPI_GLU || TN % 2 == 0, "GLU needs W1/W2 subtile pairs");
-  static_assert(PF >= 1 && PF <= 3, "prefetch distance");
+  static_assert(PF == 1 || PF == 2, "prefetch distance");
+  static_assert(NG == 2 || NG == 4, "16-K groups per 128-byte K step");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char *const sA0 = smem;
@@ -177,9 +177,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   const T *const B2base = (EPI == EPI_GLU) ? (const T *)p.B2 + b_off + lchunk * EPT : B1base;
 
   const int nk = p.K / BKE;
-  // B (weights) runs PF steps ahead through a ring of NSET register sets; A
-  // runs one step ahead in a single set (its source is usually L2-resident).
-  u32x4 ra[A_LD], rb[NSET][B_LD];
+  // register sets of staged global loads (see the pipeline below)
+  u32x4 ra[NSET][A_LD], rb[NSET][B_LD];
 
   auto gloadB = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
@@ -190,17 +189,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     for (int i = 0; i < B_LD; ++i)
       rb[S][i] = *(const u32x4 *)((b_w2[i] ? B2base : B1base) + (int64_t)b_row[i] * p.ldb + boff);
   };
-  auto gloadA = [&](int kt) {
+  auto gloadA = [&](auto SETC, int kt) {
+    constexpr int S = decltype(SETC)::value;
     const int64_t k0 = (int64_t)kt * BKE;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *(const u32x4 *)(Abase + (int64_t)a_row[i] * p.lda + k0);
+    for (int i = 0; i < A_LD; ++i) ra[S][i] = *(const u32x4 *)(Abase + (int64_t)a_row[i] * p.lda + k0);
   };
   auto lstore = [&](auto SETC, int buf) {
     constexpr int S = decltype(SETC)::value;
     unsigned char *sA = sA0 + buf * BM * 128;
     unsigned char *sB = sB0 + buf * BN * 128;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) *(u32x4 *)(sA + swz(lrow + i * RPP, lchunk)) = ra[i];
+    for (int i = 0; i < A_LD; ++i) *(u32x4 *)(sA + swz(lrow + i * RPP, lchunk)) = ra[S][i];
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) *(u32x4 *)(sB + swz(lrow + i * RPP, lchunk)) = rb[S][i];
   };
@@ -216,72 +216,110 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   // number of this wave's M subtiles (wm, wm + WM, ...) that hold valid rows
   const int nsub = (rows_valid + 31) >> 5;
   const int na = min(TM, max(0, (nsub - wm + WM - 1) / WM));
-
   const int half = lane >> 5, l32 = lane & 31;
-  auto compute = [&](auto NAC, int buf) {
+
+  // One K step from LDS buffer `buf`: the fragments of 16-K group g+1 are read
+  // while the MFMAs of group g run (two fragment register sets).
+  auto compute = [&](auto NAC, int buf, auto &&mid) {
     constexpr int NA = decltype(NAC)::value;
     const unsigned char *sA = sA0 + buf * BM * 128;
     const unsigned char *sB = sB0 + buf * BN * 128;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      u32x4 bfg[TN][CPL];
+    u32x4 af[2][TM][CPL], bfg[2][TN][CPL];
+    auto frags = [&](auto GC, auto SC) {
+      constexpr int g = decltype(GC)::value, f = decltype(SC)::value;
 #pragma unroll
       for (int b = 0; b < TN; ++b) {
         const int r = wn * WTN + b * 32 + l32;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) bfg[b][c] = *(const u32x4 *)(sB + swz(r, g * 2 * CPL + half * CPL + c));
+        for (int c = 0; c < CPL; ++c) bfg[f][b][c] = *(const u32x4 *)(sB + swz(r, g * 2 * CPL + half * CPL + c));
       }
-      u32x4 af[TM][CPL];
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         const int r = (a * WM + wm) * 32 + l32;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) af[a][c] = *(const u32x4 *)(sA + swz(r, g * 2 * CPL + half * CPL + c));
+        for (int c = 0; c < CPL; ++c) af[f][a][c] = *(const u32x4 *)(sA + swz(r, g * 2 * CPL + half * CPL + c));
       }
+    };
+    auto mma = [&](auto SC) {
+      constexpr int f = decltype(SC)::value;
 #pragma unroll
       for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) Mma<T>::run(af[a], bfg[b], acc[a][b]);
+        for (int b = 0; b < TN; ++b) Mma<T>::run(af[f][a], bfg[f][b], acc[a][b]);
+    };
+    // interleave: one MFMA, then one LDS read of the next group's fragments
+    auto interleave = [&]() {
+      constexpr int NR = (TN + NA) * CPL, NM = NA * TN * (CPL == 1 ? 1 : 8);
+#pragma unroll
+      for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+    };
+    frags(IC<0>{}, IC<0>{});
+    if (NG > 1) frags(IC<1 % NG>{}, IC<1>{});
+    mma(IC<0>{});
+    mid();  // e.g. the LDS store of the next step, overlapped with these MFMAs
+    if (NG > 2) {
+      frags(IC<2 % NG>{}, IC<0>{});
+      interleave();
     }
+    if (NG > 1) mma(IC<1>{});
+    if (NG > 3) {
+      frags(IC<3 % NG>{}, IC<1>{});
+      interleave();
+    }
+    if (NG > 2) mma(IC<0>{});
+    if (NG > 3) mma(IC<1>{});
   };
 
-  // Pipeline.  B(j), the weight slice of K step j, lives in register set
-  // j % PF; A(j) in the single A set.  Loads for the future are issued right
-  // after each barrier into the registers that were just stored to LDS:
-  // A(kt+2) first, then B(kt+1+PF).  vmcnt retires in issue order, so the LDS
-  // store of step kt+1 (A(kt+1), B(kt+1)) waits for nothing younger than
-  // B(kt+PF): the weights stay PF steps in flight, A one step.
-  gloadA(0);
+  // Pipeline (one barrier per K step).
+  //  PF == 1: A(kt+1), B(kt+1) are loaded at the start of step kt and stored to
+  //           the other LDS buffer after the step's MFMAs.
+  //  PF == 2: A(j), B(j) live in register set j % 2 and are loaded two steps
+  //           ahead; during step kt the loads of step kt+2 are issued first,
+  //           then the LDS store of step kt+1 (whose loads were issued a step
+  //           earlier, so vmcnt only waits for them) runs in the middle of the
+  //           step's MFMAs instead of after them.
+  gloadA(IC<0>{}, 0);
   gloadB(IC<0>{}, 0);
-  if (PF >= 2 && 1 < nk) gloadB(IC<1 % NSET>{}, 1);
-  if (PF >= 3 && 2 < nk) gloadB(IC<2 % NSET>{}, 2);
+  if (PF == 2 && 1 < nk) {
+    gloadA(IC<1 % NSET>{}, 1);
+    gloadB(IC<1 % NSET>{}, 1);
+  }
   lstore(IC<0>{}, 0);
   __syncthreads();
-  if (1 < nk) gloadA(1);
-  if (PF < nk) gloadB(IC<0>{}, PF);
 
-  // The loop is unrolled NSET times so every set index is static; the
-  // steady-state part carries no bounds tests.
   auto kloop = [&](auto NAC) {
     auto step = [&](auto SETC, auto CHECKC, int kt) {
-      constexpr int S1 = decltype(SETC)::value;  // == (kt + 1) % NSET
+      constexpr int S = decltype(SETC)::value;  // == kt % NSET
       constexpr bool CHECK = decltype(CHECKC)::value != 0;
-      compute(NAC, kt & 1);
-      if (!CHECK || kt + 1 < nk) lstore(IC<S1>{}, (kt + 1) & 1);
+      if (PF == 1) {
+        if (!CHECK || kt + 1 < nk) {
+          gloadA(IC<0>{}, kt + 1);
+          gloadB(IC<0>{}, kt + 1);
+        }
+        compute(NAC, kt & 1, [] {});
+        if (!CHECK || kt + 1 < nk) lstore(IC<0>{}, (kt + 1) & 1);
+      } else {
+        if (!CHECK || kt + 2 < nk) {
+          gloadA(IC<S>{}, kt + 2);
+          gloadB(IC<S>{}, kt + 2);
+        }
+        compute(NAC, kt & 1, [&] {
+          if (!CHECK || kt + 1 < nk) lstore(IC<(S + 1) % NSET>{}, (kt + 1) & 1);
+        });
+      }
       __syncthreads();
-      if (!CHECK || kt + 2 < nk) gloadA(kt + 2);
-      if (!CHECK || kt + 1 + PF < nk) gloadB(IC<S1>{}, kt + 1 + PF);
     };
     int kt = 0;
-    for (; kt + NSET + PF + 1 <= nk; kt += NSET) {
-      step(IC<1 % NSET>{}, IC<0>{}, kt);
-      if (NSET > 1) step(IC<2 % NSET>{}, IC<0>{}, kt + 1);
-      if (NSET > 2) step(IC<3 % NSET>{}, IC<0>{}, kt + 2);
+    for (; kt + NSET + 2 <= nk; kt += NSET) {
+      step(IC<0>{}, IC<0>{}, kt);
+      if (NSET > 1) step(IC<1 % NSET>{}, IC<0>{}, kt + 1);
     }
     for (; kt < nk; kt += NSET) {
-      step(IC<1 % NSET>{}, IC<1>{}, kt);
-      if (NSET > 1 && kt + 1 < nk) step(IC<2 % NSET>{}, IC<1>{}, kt + 1);
-      if (NSET > 2 && kt + 2 < nk) step(IC<3 % NSET>{}, IC<1>{}, kt + 2);
+      step(IC<0>{}, IC<1>{}, kt);
+      if (NSET > 1 && kt + 1 < nk) step(IC<1 % NSET>{}, IC<1>{}, kt + 1);
     }
   };
   // Every subtile is computed, valid rows or not (rows past the valid range

@@ -42,6 +42,7 @@ template <int BM_, int BN_, int WM_, int WN_, int PF_> struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, PF = PF_;
 };
 using CfgDense = Cfg<256, 256, 2, 4, 1>;
+using CfgRouter = Cfg<128, 128, 2, 2, 1>;  // N = n is narrow: smaller tiles keep every CU busy
 using CfgW12 = Cfg<192, 256, 2, 4, 2>;
 using CfgW3 = Cfg<192, 256, 2, 4, 2>;
 
@@ -177,7 +178,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = z; a.lda = L; a.B = w.w_router; a.ldb = L; a.C = s; a.ldc = n;
     a.M = T_; a.N = n; a.K = L; a.col_bias = w.router_logit_offset;
-    LMOE_TRY((launch_gemm<CfgDense, T, float, EPI_SIGMOID, false, false>(a, st)));
+    LMOE_TRY((launch_gemm<CfgRouter, T, float, EPI_SIGMOID, false, false>(a, st)));
   }
   // 3 top-k + routing weights
   LMOE_MARK(2);
