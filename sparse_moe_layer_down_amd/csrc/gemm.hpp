@@ -14,6 +14,10 @@
 //                 units so both products of one hidden unit land in the same
 //                 lane and register
 //   EPI_ROWSCALE  C[row] = row_scale[row] * acc            (routing weight g)
+//   EPI_PARTIAL   split-K: fp32 partial sums of one K range, C[split][row][col];
+//                 a finalize kernel sums the splits and applies the real
+//                 epilogue (used when M is too small to fill the GPU).  B rows
+//                 from b_split_row on are taken from B2 (W1 and W2 stacked).
 //
 // Tiling: BM x BN output tile per work-group of WM x WN waves; BK = 128 bytes
 // of K per step (64 bf16 or 32 fp32).  Operands go global -> registers -> LDS;
@@ -29,7 +33,7 @@
 
 namespace lmoe {
 
-enum { EPI_STORE = 0, EPI_SIGMOID = 1, EPI_GLU = 2, EPI_ROWSCALE = 3 };
+enum { EPI_STORE = 0, EPI_SIGMOID = 1, EPI_GLU = 2, EPI_ROWSCALE = 3, EPI_PARTIAL = 4 };
 
 struct GemmArgs {
   const void *A;            // [rows, lda]
@@ -52,6 +56,9 @@ struct GemmArgs {
   const float *row_scale;   // EPI_ROWSCALE
   const float *col_bias;    // EPI_SIGMOID (may be null)
   float beta1, beta2;
+  int splits;               // dense split-K: number of K ranges (1 = none)
+  int ksteps;               // K steps per range
+  int b_split_row;          // EPI_PARTIAL: B rows >= this come from B2
 };
 
 template <typename T> struct Mma;
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   const int lt = xcd_logical_tile(blockIdx.x, p.xcd_chunk);
   if (lt >= p.n_logical) return;
   int64_t m0;
-  int rows_valid, nt;
+  int rows_valid, nt, ks = 0;
   int64_t b_off = 0;
   if (GROUPED) {
     const int j = lt / p.tiles_n;
@@ -137,11 +144,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     b_off = (int64_t)tl.x * p.b_group_stride;
   } else {
     constexpr int GM = 8;
+    const int per_split = p.tiles_m * p.tiles_n;
+    ks = lt / per_split;
+    const int lm = lt % per_split;
     const int span = GM * p.tiles_n;
-    const int g = lt / span, first = g * GM;
+    const int g = lm / span, first = g * GM;
     const int gsz = min(p.tiles_m - first, GM);
-    const int mt = first + (lt % span) % gsz;
-    nt = (lt % span) / gsz;
+    const int mt = first + (lm % span) % gsz;
+    nt = (lm % span) / gsz;
     m0 = (int64_t)mt * BM;
     rows_valid = min(BM, p.M - (int)m0);
   }
@@ -167,6 +177,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       const int row = nt * (BN / 2) + wcol * (WTN / 2) + (j / 2) * 32 + (br & 31);
       b_row[i] = min(row, p.N / 2 - 1);
       b_w2[i] = (j & 1) != 0;
+    } else if (EPI == EPI_PARTIAL) {
+      const int row = min(nt * BN + br, p.N - 1);
+      b_w2[i] = row >= p.b_split_row;
+      b_row[i] = b_w2[i] ? row - p.b_split_row : row;
     } else {
       b_row[i] = min(nt * BN + br, p.N - 1);
       b_w2[i] = false;
@@ -174,15 +188,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   }
   const T *const Abase = (const T *)p.A + lchunk * EPT;
   const T *const B1base = (const T *)p.B + b_off + lchunk * EPT;
-  const T *const B2base = (EPI == EPI_GLU) ? (const T *)p.B2 + b_off + lchunk * EPT : B1base;
+  const T *const B2base = (EPI == EPI_GLU || EPI == EPI_PARTIAL) && p.B2 ? (const T *)p.B2 + b_off + lchunk * EPT
+                                                                         : B1base;
 
-  const int nk = p.K / BKE;
+  // K steps of this work-group: all of K, or one split's range
+  const int nk_all = p.K / BKE;
+  const int kbeg = ks * p.ksteps;
+  const int nk = (p.splits > 1) ? min(p.ksteps, nk_all - kbeg) : nk_all;
   // register sets of staged global loads (see the pipeline below)
   u32x4 ra[NSET][A_LD], rb[NSET][B_LD];
 
   auto gloadB = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
-    const int64_t k0 = (int64_t)kt * BKE;
+    const int64_t k0 = (int64_t)(kbeg + kt) * BKE;
     const int64_t s = k0 / p.kb_len;
     const int64_t boff = s * p.kb_stride + (k0 - s * p.kb_len);
 #pragma unroll
@@ -191,7 +209,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   };
   auto gloadA = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
-    const int64_t k0 = (int64_t)kt * BKE;
+    const int64_t k0 = (int64_t)(kbeg + kt) * BKE;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) ra[S][i] = *(const u32x4 *)(Abase + (int64_t)a_row[i] * p.lda + k0);
   };
@@ -360,10 +378,40 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
           } else if (EPI == EPI_ROWSCALE) {
             v *= rs;
           }
-          C[grow * p.ldc + col] = from_f32<TO>(v);
+          if (EPI == EPI_PARTIAL)
+            ((float *)p.C)[((int64_t)ks * p.M + grow) * p.ldc + col] = v;
+          else
+            C[grow * p.ldc + col] = from_f32<TO>(v);
         }
       }
     }
+  }
+}
+
+// Split-K finalize: out = epilogue(sum over splits of the fp32 partials).
+// EPI_GLU reads the stacked layout: W1 products in columns [0, H), W2 in [H, 2H).
+template <typename TO, int EPI>
+__global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__restrict__ part, int splits, int M,
+                                                              int Np, TO *__restrict__ out, int64_t ldo,
+                                                              const float *__restrict__ col_bias, float beta1,
+                                                              float beta2) {
+  const int Nout = (EPI == EPI_GLU) ? Np / 2 : Np;
+  const int64_t total = (int64_t)M * Nout;
+  const int64_t plane = (int64_t)M * Np;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / Nout), c = (int)(i % Nout);
+    const float *pp = part + (int64_t)m * Np + c;
+    float v = 0.0f;
+    for (int sp = 0; sp < splits; ++sp) v += pp[sp * plane];
+    if (EPI == EPI_GLU) {
+      float v2 = 0.0f;
+      for (int sp = 0; sp < splits; ++sp) v2 += pp[sp * plane + Nout];
+      v = situf_(v, beta1) * softcapf_(v2, beta2);
+    } else if (EPI == EPI_SIGMOID) {
+      if (col_bias) v += col_bias[c];
+      v = sigmoidf_(v);
+    }
+    out[(int64_t)m * ldo + c] = from_f32<TO>(v);
   }
 }
 

@@ -43,8 +43,14 @@ template <int BM_, int BN_, int WM_, int WN_, int PF_> struct Cfg {
 };
 using CfgDense = Cfg<256, 256, 2, 4, 1>;
 using CfgRouter = Cfg<128, 128, 2, 2, 1>;  // N = n is narrow: smaller tiles keep every CU busy
+using CfgMid = Cfg<128, 128, 2, 2, 1>;     // dense GEMMs whose 256 x 256 tiles would not fill the GPU
+using CfgSkinny = Cfg<64, 256, 1, 4, 2>;   // dense GEMMs with M <= 64 (decode), always split-K
 using CfgW12 = Cfg<192, 256, 2, 4, 2>;
 using CfgW3 = Cfg<192, 256, 2, 4, 2>;
+// experts with few rows each (decode): 32-row tiles
+using CfgW12Small = Cfg<32, 256, 1, 4, 2>;
+using CfgW3Small = Cfg<32, 256, 1, 4, 2>;
+constexpr int SMALL_ROWS_PER_EXPERT = 24;  // average rows per expert below which the small tiles are used
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t align256(int64_t a) { return (a + 255) & ~(int64_t)255; }
@@ -56,43 +62,52 @@ struct WsLayout {
 
 enum {
   R_Z = 0, R_COUNTS, R_OFFS, R_ROW_TOKEN, R_SLOT_ROW, R_HIDDEN, R_USH, R_V,
-  R_SCORES, R_IDX, R_W, R_MASKS, R_CBASE, R_TILES1, R_TILES2, R_NTILES, R_ROW_W, R_HSH, R_YSTAGE, R_COUNT_
+  R_SCORES, R_IDX, R_W, R_MASKS, R_CBASE, R_TILES1, R_TILES2, R_NTILES, R_ROW_W, R_HSH, R_YSTAGE, R_PART, R_COUNT_
 };
 
 // upper bound of sum_e ceil(count_e / bm) over any routing
 int64_t max_tiles(const lmoe_dims &d, int bm) { return d.n + cdiv(d.T * d.k, bm); }
 
-WsLayout layout(const lmoe_dims &d, int dtype) {
-  const int64_t es = dtype == LMOE_BF16 ? 2 : 4;
-  const int64_t nch = cdiv(d.T, PERM_CHUNK);
-  int64_t sz[R_COUNT_];
-  sz[R_Z] = d.T * d.L * es;
-  sz[R_COUNTS] = d.n * 4;
-  sz[R_OFFS] = (d.n + 1) * 4;
-  sz[R_ROW_TOKEN] = d.T * d.k * 4;
-  sz[R_SLOT_ROW] = d.T * d.k * 4;
-  sz[R_HIDDEN] = d.T * d.k * d.D * es;
-  sz[R_USH] = d.T * d.L * 4;
-  sz[R_V] = d.T * d.L * es;
-  sz[R_SCORES] = d.T * d.n * 4;
-  sz[R_IDX] = d.T * d.k * 4;
-  sz[R_W] = d.T * d.k * 4;
-  sz[R_MASKS] = nch * d.n * 4 * 8;
-  sz[R_CBASE] = nch * d.n * 4;
-  sz[R_TILES1] = max_tiles(d, CfgW12::BM) * 16;
-  sz[R_TILES2] = max_tiles(d, CfgW3::BM) * 16;
-  sz[R_NTILES] = 8;
-  sz[R_ROW_W] = d.T * d.k * 4;
-  sz[R_HSH] = d.T * d.n_shared * d.D * es;
-  sz[R_YSTAGE] = d.T * d.k * d.L * 4;  // fp32: per-slot rows are summed before any rounding
-  WsLayout w;
-  int64_t o = 0;
-  for (int i = 0; i < R_COUNT_; ++i) {
-    w.off[i] = o;
-    o += align256(sz[i]);
-  }
-  w.total = o;
-  return w;
+bool small_experts(const lmoe_dims &d) { return d.T * d.k <= SMALL_ROWS_PER_EXPERT * d.n; }
+int w12_bm(const lmoe_dims &d) { return small_experts(d) ? CfgW12Small::BM : CfgW12::BM; }
+int w3_bm(const lmoe_dims &d) { return small_experts(d) ? CfgW3Small::BM : CfgW3::BM; }
+
+// Split-K plan of a dense GEMM: used when its tiles cannot fill the GPU.
+struct SplitPlan {
+  int splits, ksteps;
+};
+template <typename C>
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int bke, bool force) {
+  const int64_t tiles = cdiv(M, C::BM) * cdiv(N, C::BN);
+  const int nk = (int)(K / bke);
+  if (tiles <= 0 || nk < 4 || (!force && tiles >= 256)) return {1, std::max(nk, 1)};
+  int splits = (int)std::min<int64_t>(cdiv(512, tiles), nk / 2);
+  splits = std::max(splits, 1);
+  const int ksteps = (int)cdiv(nk, splits);
+  return {(int)cdiv(nk, ksteps), ksteps};
+}
+// How a dense GEMM is run: M <= 64 -> skinny tile with split-K; otherwise the
+// large tile if it yields enough work-groups, else the 128 x 128 tile, split
+// along K only if even that leaves the GPU mostly idle.
+enum DenseMode { DM_LARGE = 0, DM_MID = 1, DM_MID_SPLIT = 2, DM_SKINNY = 3 };
+struct DensePlan {
+  DenseMode mode;
+  SplitPlan sp;
+};
+template <typename C>
+DensePlan dense_plan(int64_t M, int64_t N, int64_t K, int bke) {
+  if (M <= CfgSkinny::BM) return {DM_SKINNY, split_plan<CfgSkinny>(M, N, K, bke, true)};
+  if (cdiv(M, C::BM) * cdiv(N, C::BN) >= 256) return {DM_LARGE, {1, (int)(K / bke)}};
+  if (cdiv(M, CfgMid::BM) * cdiv(N, CfgMid::BN) >= 128) return {DM_MID, {1, (int)(K / bke)}};
+  const SplitPlan sp = split_plan<CfgMid>(M, N, K, bke, true);
+  return {sp.splits > 1 ? DM_MID_SPLIT : DM_MID, sp};
+}
+// fp32 partial-sum bytes a dense GEMM needs (0 when it runs without split-K)
+template <typename C>
+int64_t part_bytes(int64_t M, int64_t N, int64_t K, int bke) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  const DensePlan pl = dense_plan<C>(M, N, K, bke);
+  return (pl.mode == DM_SKINNY || pl.mode == DM_MID_SPLIT) ? (int64_t)pl.sp.splits * M * N * 4 : 0;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -118,7 +133,7 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   if (attr != hipSuccess) return attr;
   a.tiles_n = (int)cdiv(a.N, C::BN);
   if (!GROUPED) a.tiles_m = (int)cdiv(a.M, C::BM);
-  a.n_logical = a.tiles_m * a.tiles_n;
+  a.n_logical = a.tiles_m * a.tiles_n * (GROUPED ? 1 : std::max(a.splits, 1));
   if (a.n_logical == 0) return hipSuccess;
   a.xcd_chunk = a.n_logical >= 1024 ? 8 : 1;
   const int64_t grid = cdiv(a.n_logical, 8 * a.xcd_chunk) * 8 * a.xcd_chunk;
@@ -127,11 +142,38 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Dense GEMM with the tiling chosen by dense_plan.  Split-K writes fp32
+// partials to `part`, then the finalize kernel sums them and applies the
+// epilogue.
+template <typename C, typename T, typename TO, int EPI>
+hipError_t launch_dense(GemmArgs a, float *part, hipStream_t st) {
+  constexpr int bke = 128 / (int)sizeof(T);
+  const DensePlan pl = dense_plan<C>(a.M, a.N, a.K, bke);
+  if (pl.mode == DM_LARGE) return launch_gemm<C, T, TO, EPI, false, false>(a, st);
+  if (pl.mode == DM_MID) return launch_gemm<CfgMid, T, TO, EPI, false, false>(a, st);
+  GemmArgs b = a;
+  b.C = part;
+  b.ldc = a.N;
+  b.splits = pl.sp.splits;
+  b.ksteps = pl.sp.ksteps;
+  b.b_split_row = (EPI == EPI_GLU) ? a.N / 2 : a.N;
+  if (EPI != EPI_GLU) b.B2 = nullptr;
+  hipError_t e = (pl.mode == DM_SKINNY) ? launch_gemm<CfgSkinny, T, float, EPI_PARTIAL, false, false>(b, st)
+                                        : launch_gemm<CfgMid, T, float, EPI_PARTIAL, false, false>(b, st);
+  if (e != hipSuccess) return e;
+  const int64_t outs = (int64_t)a.M * (EPI == EPI_GLU ? a.N / 2 : a.N);
+  const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(outs, 256), 8192);
+  hipLaunchKernelGGL((splitk_finalize_kernel<TO, EPI>), dim3(blocks), dim3(256), 0, st, part, pl.sp.splits, a.M,
+                     a.N, (TO *)a.C, a.ldc, a.col_bias, a.beta1, a.beta2);
+  return hipGetLastError();
+}
+
 GemmArgs gargs() {
   GemmArgs a;
   memset(&a, 0, sizeof(a));
   a.beta1 = 4.0f;
   a.beta2 = 25.0f;
+  a.splits = 1;
   return a;
 }
 
@@ -159,6 +201,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   float *row_w = (float *)(ws + Lw.off[R_ROW_W]);
   T *hsh = (T *)(ws + Lw.off[R_HSH]);
   float *ystage = (float *)(ws + Lw.off[R_YSTAGE]);
+  float *part = (float *)(ws + Lw.off[R_PART]);
   const int T_ = (int)d.T, n = (int)d.n, k = (int)d.k, L = (int)d.L, D = (int)d.D, ns = (int)d.n_shared;
   hipError_t e;
 #define LMOE_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
@@ -170,7 +213,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = x; a.lda = d.d; a.B = w.w_down; a.ldb = d.d; a.C = z; a.ldc = L;
     a.M = T_; a.N = L; a.K = (int)d.d;
-    LMOE_TRY((launch_gemm<CfgDense, T, T, EPI_STORE, false, false>(a, st)));
+    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
   }
   // 2 s = sigmoid(z W_r^T + o)
   LMOE_MARK(1);
@@ -178,7 +221,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = z; a.lda = L; a.B = w.w_router; a.ldb = L; a.C = s; a.ldc = n;
     a.M = T_; a.N = n; a.K = L; a.col_bias = w.router_logit_offset;
-    LMOE_TRY((launch_gemm<CfgRouter, T, float, EPI_SIGMOID, false, false>(a, st)));
+    LMOE_TRY((launch_dense<CfgRouter, T, float, EPI_SIGMOID>(a, part, st)));
   }
   // 3 top-k + routing weights
   LMOE_MARK(2);
@@ -197,8 +240,8 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     const int nch = (int)cdiv(d.T, PERM_CHUNK);
     hipLaunchKernelGGL(perm_mask_kernel, dim3(nch), dim3(PERM_CHUNK), (size_t)n * 32, st, idx, T_, n, k, masks, cbase);
     LMOE_TRY(hipGetLastError());
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cbase, nch, n, counts, offs, CfgW12::BM, tiles1,
-                       CfgW3::BM, tiles2, ntiles);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cbase, nch, n, counts, offs, w12_bm(d), tiles1,
+                       w3_bm(d), tiles2, ntiles);
     LMOE_TRY(hipGetLastError());
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch), dim3(PERM_CHUNK), 0, st, idx, gw, T_, n, k, masks, cbase,
                        row_token, row_w, slot_row);
@@ -210,7 +253,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = z; a.lda = L; a.B = w.ws1; a.B2 = w.ws2; a.ldb = L; a.C = hsh; a.ldc = (int64_t)ns * D;
     a.M = T_; a.N = 2 * ns * D; a.K = L; a.beta1 = w.beta1; a.beta2 = w.beta2;
-    LMOE_TRY((launch_gemm<CfgDense, T, T, EPI_GLU, false, false>(a, st)));
+    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_GLU>(a, part, st)));
   }
   // 6 routed experts' gated hidden: [T*k, D] in dispatched order
   LMOE_MARK(5);
@@ -218,9 +261,10 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = z; a.lda = L; a.a_rows = row_token; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
     a.b_group_stride = (int64_t)D * L; a.C = hid; a.ldc = D;
-    a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, CfgW12::BM);
+    a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, w12_bm(d));
     a.beta1 = w.beta1; a.beta2 = w.beta2;
-    LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU, true, true>(a, st)));
+    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_GLU, true, true>(a, st)));
+    else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU, true, true>(a, st)));
   }
   // 7 shared W3 (the shared experts summed through one K = ns*D contraction)
   LMOE_MARK(6);
@@ -228,7 +272,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = hsh; a.lda = (int64_t)ns * D; a.B = w.ws3; a.ldb = D; a.kb_len = D; a.kb_stride = (int64_t)L * D;
     a.C = ush; a.ldc = L; a.M = T_; a.N = L; a.K = ns * D;
-    LMOE_TRY((launch_gemm<CfgDense, T, float, EPI_STORE, false, false>(a, st)));
+    LMOE_TRY((launch_dense<CfgDense, T, float, EPI_STORE>(a, part, st)));
   }
   // 8 routed W3, scaled by g, one row per dispatched (token, slot)
   LMOE_MARK(7);
@@ -236,8 +280,9 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = hid; a.lda = D; a.B = w.w3; a.ldb = D; a.b_group_stride = (int64_t)L * D;
     a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles2; a.ntiles = ntiles + 1;
-    a.tiles_m = (int)max_tiles(d, CfgW3::BM); a.row_scale = row_w;
-    LMOE_TRY((launch_gemm<CfgW3, T, float, EPI_ROWSCALE, false, true>(a, st)));
+    a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w;
+    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, float, EPI_ROWSCALE, false, true>(a, st)));
+    else LMOE_TRY((launch_gemm<CfgW3, T, float, EPI_ROWSCALE, false, true>(a, st)));
   }
   // 9 combine + RMSNorm
   LMOE_MARK(8);
@@ -256,7 +301,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = v; a.lda = L; a.B = w.w_up; a.ldb = L; a.C = y; a.ldc = d.d;
     a.M = T_; a.N = (int)d.d; a.K = L;
-    LMOE_TRY((launch_gemm<CfgDense, T, T, EPI_STORE, false, false>(a, st)));
+    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
   }
   LMOE_MARK(10);
 #undef LMOE_MARK

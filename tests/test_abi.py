@@ -41,6 +41,17 @@ def test_workspace_size():
     assert lib().lmoe_workspace_offset(c2dims(), 1, 99) == -1
 
 
+@pytest.mark.parametrize("kw", [dict(n_shared=0), dict(T=1), dict(T=0), dict(T=1, n_shared=0, n=1, k=1),
+                                dict(T=64, d=256, L=128, n=16, k=4, n_shared=1, D=64), dict(T=100000)])
+def test_workspace_size_edge_dims(kw):
+    # host-side sizing (split-K planning included) must handle every valid shape
+    for dt in (0, 1):
+        ws = lmoe.workspace_size(c2dims(**kw), dt)
+        assert ws > 0
+        for r in range(8):
+            assert 0 <= lib().lmoe_workspace_offset(c2dims(**kw), dt, r) < ws
+
+
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
 
 
