@@ -122,6 +122,11 @@ def main():
         del src, dst
 
     counts = lmoe.workspace_view(ws, dims, x.dtype, "counts").cpu().numpy()
+    # HBM traffic of the routed W1/W2 launch from the committed rocprofv3 counter summary, if it was
+    # taken on these exact kernel sources and this workload
+    from sparse_moe_layer_down_amd import profsum
+    tb, sha = profsum.read_counters(os.path.join(ROOT, "profiles", f"routed_w12_{cfg.name.lower()}_hbm_counters.md"))
+    traffic = tb if (tb is not None and sha == profsum.source_sha256()) else None
     flops = cfg.flops_per_token() * cfg.T
     tflops = flops / (ms * 1e-3) / 1e12
     w12_bytes, touched = routed_w12_bytes(cfg, counts)
@@ -149,7 +154,7 @@ def main():
         "stage_ms": {name: float(v) for name, v in zip(lmoe.STAGES, stage_ms)},
         "roofline": {"kernel": "routed experts W1/W2 + SiTU-GLU grouped GEMM", "bound": "hbm",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": None, "algorithmic_bytes": w12_bytes, "experts_touched": touched,
+                     "traffic": traffic, "algorithmic_bytes": w12_bytes, "experts_touched": touched,
                      "avg_ms": w12_ms},
     }
     if not args.no_cpu_baseline:

@@ -1,0 +1,152 @@
+"""Turn rocprofv3 CSV output of `bench.py` into the short text summaries kept
+under profiles/.
+
+  python -m sparse_moe_layer_down_amd.profsum trace  <kernel_stats.csv> <out.md> "<command>"
+  python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <out.md> "<commands>"
+
+The counters summary records, for every kernel of the forward, the mean
+FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as the counters read), the same
+counters for the 1 GiB device copy that `bench.py --copy-calibration` runs, the
+calibration factors they give, and a SHA-256 of the library's kernel sources.
+`bench.py` reports the routed W1/W2 kernel's traffic from this file only while
+that hash matches the sources it runs.
+"""
+import csv
+import glob
+import hashlib
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+COPY_BYTES = 1 << 30
+EPI = {0: "store", 1: "sigmoid", 2: "SiTU-GLU", 3: "rowscale", 4: "split-K partial"}
+
+
+def source_sha256():
+    """SHA-256 over the kernel sources and the C header, in a fixed order."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + [os.path.join(ROOT, "include", "lmoe.h")]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def label(name):
+    """Readable name for a kernel symbol (mangled or demangled)."""
+    m = re.search(r"gemm_kernelI(DF16b|f)(DF16b|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELi(\d)ELi(\d)ELb(\d)ELb(\d)E", name)
+    if m:
+        out = "fp32" if m.group(2) == "f" else "bf16"
+        return (f"gemm {m.group(3)}x{m.group(4)} waves {m.group(5)}x{m.group(6)} pf{m.group(7)} "
+                f"epi={EPI[int(m.group(8))]} out={out} gather={m.group(9)} grouped={m.group(10)}")
+    m = re.search(r"gemm_kernel<[^,]*, (\d+), (\d+), (\d), (\d), (\d), (\d), (\w+), (\w+)>", name)
+    if m:  # rocprofv3 demangles only the instances with a float output type
+        return (f"gemm {m.group(1)}x{m.group(2)} waves {m.group(3)}x{m.group(4)} pf{m.group(5)} "
+                f"epi={EPI[int(m.group(6))]} out=fp32 gather={int(m.group(7) == 'true')} "
+                f"grouped={int(m.group(8) == 'true')}")
+    m = re.search(r"(\w+_kernel)", name)
+    return m.group(1) if m else name[:60]
+
+
+def stage(lab, name):
+    rules = [("SiTU-GLU out=bf16 gather=1 grouped=1", "routed W1/W2 + SiTU-GLU"),
+             ("rowscale", "routed W3 x routing weight"),
+             ("epi=sigmoid", "router scores"),
+             ("SiTU-GLU out=bf16 gather=0", "shared W1/W2 + SiTU-GLU"),
+             ("store out=fp32 gather=0 grouped=0", "shared W3"),
+             ("store out=bf16 gather=0 grouped=0", "W_down / W_up"),
+             ("split-K", "split-K partial sums"),
+             ("splitk_finalize", "split-K finalize"),
+             ("combine", "combine + RMSNorm"),
+             ("topk", "top-k + routing weights"),
+             ("perm_", "permutation"),
+             ("synth", "input synthesis (outside the timed region)")]
+    for key, st in rules:
+        if key in lab or key in name:
+            return st
+    return ""
+
+
+def trace(stats_csv, out, cmd):
+    rows = list(csv.DictReader(open(stats_csv)))
+    with open(out, "w") as f:
+        f.write("# Kernel trace: K3-shaped prefill forward (T=8192, d=7168, 896 experts choose 16), bf16\n\n")
+        f.write(f"Kernel-source SHA-256: `{source_sha256()}`\n\n")
+        f.write(f"Command (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
+        f.write("| kernel | stage | calls | avg (us) | min (us) | max (us) | share |\n|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            lab = label(r["Name"])
+            f.write(f"| `{lab}` | {stage(lab, r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |\n")
+
+
+def _means(d, counter):
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+def counters(fetch_dir, write_dir, out, cmd):
+    fetch, nf = _means(fetch_dir, "FETCH_SIZE")
+    write, _ = _means(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no calibration copy in the fetch pass (run bench.py with --copy-calibration)")
+    # the 1 GiB copy may run as several dispatches: sum them
+    cf = fetch[copy[0]] * nf[copy[0]]
+    cw = write[copy[0]] * nf[copy[0]]
+    ff = COPY_BYTES / (cf * 1024.0)
+    wf = COPY_BYTES / (cw * 1024.0)
+    with open(out, "w") as f:
+        f.write("# HBM counters per dispatch: K3-shaped prefill forward (T=8192, d=7168, 896 experts choose 16), bf16\n\n")
+        f.write(f"source_sha256: {source_sha256()}\n")
+        f.write(f"fetch_factor: {ff:.4f}\nwrite_factor: {wf:.4f}\n\n")
+        f.write("FETCH_SIZE and WRITE_SIZE are in KiB per dispatch as rocprofv3 reports them. The factors scale them to "
+                f"bytes moved: a 1 GiB device-to-device copy read {cf:.0f} KiB (FETCH_SIZE) and wrote {cw:.0f} KiB "
+                "(WRITE_SIZE), summed over its dispatches.\n\n")
+        f.write(f"Commands (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
+        f.write("| kernel | stage | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled traffic (GB) |\n"
+                "|---|---|---|---|---|---|\n")
+        for k in sorted(fetch, key=lambda k: -fetch[k]):
+            lab = label(k)
+            st = "1 GiB calibration copy" if k in copy else stage(lab, k)
+            if st.startswith("input synthesis"):
+                continue
+            w = write.get(k, 0.0)
+            gb = (fetch[k] * ff + w * wf) * 1024 / 1e9
+            key = "routed_w12: " if st == "routed W1/W2 + SiTU-GLU" else ""
+            f.write(f"| `{lab}` | {key}{st} | {nf[k]} | {fetch[k]:.0f} | {w:.0f} | {gb:.3f} |\n")
+        rw = [k for k in fetch if stage(label(k), k) == "routed W1/W2 + SiTU-GLU"]
+        if rw:
+            k = rw[0]
+            tb = (fetch[k] * ff + write.get(k, 0.0) * wf) * 1024
+            f.write(f"\nrouted_w12_traffic_bytes: {tb:.0f}\n")
+
+
+def read_counters(path):
+    """(traffic bytes of the routed W1/W2 launch, recorded source hash) or (None, None)."""
+    if not os.path.exists(path):
+        return None, None
+    sha, tb = None, None
+    for line in open(path):
+        if line.startswith("source_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        elif line.startswith("routed_w12_traffic_bytes:"):
+            tb = float(line.split(":", 1)[1])
+    return tb, sha
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 5 and sys.argv[1] == "trace":
+        trace(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif len(sys.argv) >= 6 and sys.argv[1] == "counters":
+        counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    else:
+        print(__doc__)
+        sys.exit(2)
