@@ -46,7 +46,12 @@ typedef enum {
 
 /* Work dtype: the storage type of x, the weights, and the stored activations
  * z, a, v, y.  Accumulation, router scores, routing weights, the aggregated
- * latent and the norm statistics are always fp32. */
+ * latent and the norm statistics are always fp32.  The k routed contributions
+ * g_ie * (a W3_e^T) of a token are staged in the workspace before their fp32
+ * sum: in fp16 when the work dtype is bf16 (an element beyond +-65504 becomes
+ * +-inf and so shows in y; the gated hidden a is bounded by beta1 * beta2, so
+ * this needs a W3 row whose absolute values sum past 65504 / (beta1 * beta2)),
+ * in fp32 when it is fp32. */
 typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
 
 /* Layer dimensions ([DD] §2: d -> d/2 -> D -> d/2 -> d, k of n routed experts;

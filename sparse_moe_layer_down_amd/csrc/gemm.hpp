@@ -51,8 +51,8 @@ struct GemmArgs {
   const int4 *tiles;        // GROUPED: {expert, row_begin, row_end, 0}
   const int32_t *ntiles;    // GROUPED: number of valid tiles (device)
   int tiles_m, tiles_n;     // dense M tiles (grouped: max tiles) and N tiles
-  int n_logical;            // tiles_m * tiles_n
-  int xcd_chunk;
+  int n_logical;            // tiles_m * tiles_n (dense: x splits)
+  int xpf;                  // every tile has an even number of K steps: prefetch across tiles
   const float *row_scale;   // EPI_ROWSCALE
   const float *col_bias;    // EPI_SIGMOID (may be null)
   float beta1, beta2;
@@ -127,89 +127,121 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   // on SCC instead of masking lanes
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  // Lane-derived indices are re-derived from an opaque copy of the thread id
+  // at the start of every tile, so the compiler cannot hoist the many LDS and
+  // store addresses built from them out of the tile loop (they would then stay
+  // live through the epilogue and spill).
+  int half = lane >> 5, l32 = lane & 31;
+  int lrow = tid >> 3, lchunk = tid & 7;
 
-  // ---- which tile
-  const int lt = xcd_logical_tile(blockIdx.x, p.xcd_chunk);
-  if (lt >= p.n_logical) return;
-  int64_t m0;
-  int rows_valid, nt, ks = 0;
-  int64_t b_off = 0;
-  if (GROUPED) {
-    const int j = lt / p.tiles_n;
-    nt = lt % p.tiles_n;
-    if (j >= *p.ntiles) return;
-    const int4 tl = p.tiles[j];
-    m0 = tl.y;
-    rows_valid = tl.z - tl.y;
-    b_off = (int64_t)tl.x * p.b_group_stride;
-  } else {
-    constexpr int GM = 8;
-    const int per_split = p.tiles_m * p.tiles_n;
-    ks = lt / per_split;
-    const int lm = lt % per_split;
-    const int span = GM * p.tiles_n;
-    const int g = lm / span, first = g * GM;
-    const int gsz = min(p.tiles_m - first, GM);
-    const int mt = first + (lm % span) % gsz;
-    nt = (lm % span) / gsz;
-    m0 = (int64_t)mt * BM;
-    rows_valid = min(BM, p.M - (int)m0);
-  }
+  // ---- persistent walk over the logical tiles.  Each XCD (work-groups are
+  // dispatched round-robin over the 8 XCDs) takes one contiguous range of
+  // logical tiles, so the tiles that share A rows (one expert's N tiles, or a
+  // group of dense M tiles) meet in that XCD's L2.
+  const int nvalid = GROUPED ? min(*p.ntiles, p.tiles_m) * p.tiles_n : p.n_logical;
+  const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
+  const int per = gridDim.x / nx;
+  const int chunk = (nvalid + nx - 1) / nx;
+  const int xcd = blockIdx.x % nx;
+  const int lt_end = min(nvalid, (xcd + 1) * chunk);
+  int lt = xcd * chunk + blockIdx.x / nx;
+  if (lt >= lt_end) return;
 
-  // ---- per-thread source rows (32-bit row indices; addresses are formed per K step).
-  // Rows past the valid range are clamped onto a valid row: they only feed
-  // output rows / columns that are never stored, and unconditional loads keep
-  // the K loop free of branches (whose joins force full vmcnt waits).
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  int a_row[A_LD];
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int r = min(lrow + i * RPP, rows_valid - 1);
-    a_row[i] = GATHER ? p.a_rows[m0 + r] : (int)(m0 + r);
-  }
-  int b_row[B_LD];  // row of B (GLU: hidden unit)
-  bool b_w2[B_LD];  // GLU: row comes from W2
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int br = lrow + i * RPP;
-    if (EPI == EPI_GLU) {
-      const int wcol = br / WTN, within = br % WTN, j = within / 32;
-      const int row = nt * (BN / 2) + wcol * (WTN / 2) + (j / 2) * 32 + (br & 31);
-      b_row[i] = min(row, p.N / 2 - 1);
-      b_w2[i] = (j & 1) != 0;
-    } else if (EPI == EPI_PARTIAL) {
-      const int row = min(nt * BN + br, p.N - 1);
-      b_w2[i] = row >= p.b_split_row;
-      b_row[i] = b_w2[i] ? row - p.b_split_row : row;
-    } else {
-      b_row[i] = min(nt * BN + br, p.N - 1);
-      b_w2[i] = false;
-    }
-  }
-  const T *const Abase = (const T *)p.A + lchunk * EPT;
-  const T *const B1base = (const T *)p.B + b_off + lchunk * EPT;
-  const T *const B2base = (EPI == EPI_GLU || EPI == EPI_PARTIAL) && p.B2 ? (const T *)p.B2 + b_off + lchunk * EPT
-                                                                         : B1base;
-
-  // K steps of this work-group: all of K, or one split's range
+  struct TileI {
+    int64_t m0, b_off;
+    int rows, nt, ks, kbeg, nk;
+  };
   const int nk_all = p.K / BKE;
-  const int kbeg = ks * p.ksteps;
-  const int nk = (p.splits > 1) ? min(p.ksteps, nk_all - kbeg) : nk_all;
+  auto decode = [&](int l) {
+    TileI t;
+    t.ks = 0;
+    t.b_off = 0;
+    if (GROUPED) {
+      const int j = l / p.tiles_n;
+      t.nt = l % p.tiles_n;
+      const int4 e = p.tiles[j];
+      t.m0 = e.y;
+      t.rows = e.z - e.y;
+      t.b_off = (int64_t)e.x * p.b_group_stride;
+    } else {
+      constexpr int GM = 8;  // M tiles per group: consecutive tiles walk down a group, then across
+      const int per_split = p.tiles_m * p.tiles_n;
+      t.ks = l / per_split;
+      const int lm = l % per_split;
+      const int span = GM * p.tiles_n;
+      const int g = lm / span, first = g * GM;
+      const int gsz = min(p.tiles_m - first, GM);
+      const int mt = first + (lm % span) % gsz;
+      t.nt = (lm % span) / gsz;
+      t.m0 = (int64_t)mt * BM;
+      t.rows = min(BM, p.M - (int)t.m0);
+    }
+    t.kbeg = t.ks * p.ksteps;
+    t.nk = (p.splits > 1) ? min(p.ksteps, nk_all - t.kbeg) : nk_all;
+    return t;
+  };
+
+  // ---- per-thread source rows of the tile being loaded (32-bit row indices;
+  // addresses are formed per K step).  Rows past the valid range are clamped
+  // onto a valid row: they only feed output rows / columns that are never
+  // stored, and unconditional loads keep the K loop free of branches (whose
+  // joins force full vmcnt waits).
+  int a_row[A_LD];
+  int b_row[B_LD];  // row of B (GLU: hidden unit)
+  bool b_w2[B_LD];  // GLU / split-K: row comes from B2
+  int64_t lb_off;   // expert offset of B
+  int lkbeg;        // first K step
+  auto rows_of = [&](const TileI &t, int (&out)[A_LD]) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int r = min(lrow + i * RPP, t.rows - 1);
+      out[i] = GATHER ? p.a_rows[t.m0 + r] : (int)(t.m0 + r);
+    }
+  };
+  auto set_b = [&](const TileI &t) {
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int br = lrow + i * RPP;
+      if (EPI == EPI_GLU) {
+        const int wcol = br / WTN, within = br % WTN, j = within / 32;
+        const int row = t.nt * (BN / 2) + wcol * (WTN / 2) + (j / 2) * 32 + (br & 31);
+        b_row[i] = min(row, p.N / 2 - 1);
+        b_w2[i] = (j & 1) != 0;
+      } else if (EPI == EPI_PARTIAL) {
+        const int row = min(t.nt * BN + br, p.N - 1);
+        b_w2[i] = row >= p.b_split_row;
+        b_row[i] = b_w2[i] ? row - p.b_split_row : row;
+      } else {
+        b_row[i] = min(t.nt * BN + br, p.N - 1);
+        b_w2[i] = false;
+      }
+    }
+    lb_off = t.b_off;
+    lkbeg = t.kbeg;
+  };
+  const T *const Abase = (const T *)p.A + lchunk * EPT;
+  const T *const B1base = (const T *)p.B + lchunk * EPT;
+  const T *const B2base = (EPI == EPI_GLU || EPI == EPI_PARTIAL) && p.B2 ? (const T *)p.B2 + lchunk * EPT : B1base;
+
   // register sets of staged global loads (see the pipeline below)
   u32x4 ra[NSET][A_LD], rb[NSET][B_LD];
+  const bool kbatch = p.kb_len != p.K;
 
   auto gloadB = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
-    const int64_t k0 = (int64_t)(kbeg + kt) * BKE;
-    const int64_t s = k0 / p.kb_len;
-    const int64_t boff = s * p.kb_stride + (k0 - s * p.kb_len);
+    const int k0 = (lkbeg + kt) * BKE;
+    int64_t boff = lb_off + k0;
+    if (kbatch) {  // uniform; only the shared-expert W3 splits B along K
+      const int s = k0 / (int)p.kb_len;
+      boff = lb_off + (int64_t)s * p.kb_stride + (k0 - s * (int)p.kb_len);
+    }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i)
       rb[S][i] = *(const u32x4 *)((b_w2[i] ? B2base : B1base) + (int64_t)b_row[i] * p.ldb + boff);
   };
   auto gloadA = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
-    const int64_t k0 = (int64_t)(kbeg + kt) * BKE;
+    const int64_t k0 = (int64_t)(lkbeg + kt) * BKE;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) ra[S][i] = *(const u32x4 *)(Abase + (int64_t)a_row[i] * p.lda + k0);
   };
@@ -224,22 +256,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   };
 
   f32x16 acc[TM][TN];
-#pragma unroll
-  for (int a = 0; a < TM; ++a)
-#pragma unroll
-    for (int b = 0; b < TN; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-
-  // number of this wave's M subtiles (wm, wm + WM, ...) that hold valid rows
-  const int nsub = (rows_valid + 31) >> 5;
-  const int na = min(TM, max(0, (nsub - wm + WM - 1) / WM));
-  const int half = lane >> 5, l32 = lane & 31;
 
   // One K step from LDS buffer `buf`: the fragments of 16-K group g+1 are read
   // while the MFMAs of group g run (two fragment register sets).
-  auto compute = [&](auto NAC, int buf, auto &&mid) {
-    constexpr int NA = decltype(NAC)::value;
+  auto compute = [&](int buf, auto &&mid) {
     const unsigned char *sA = sA0 + buf * BM * 128;
     const unsigned char *sB = sB0 + buf * BN * 128;
     u32x4 af[2][TM][CPL], bfg[2][TN][CPL];
@@ -252,7 +272,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
         for (int c = 0; c < CPL; ++c) bfg[f][b][c] = *(const u32x4 *)(sB + swz(r, g * 2 * CPL + half * CPL + c));
       }
 #pragma unroll
-      for (int a = 0; a < NA; ++a) {
+      for (int a = 0; a < TM; ++a) {
         const int r = (a * WM + wm) * 32 + l32;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) af[f][a][c] = *(const u32x4 *)(sA + swz(r, g * 2 * CPL + half * CPL + c));
@@ -261,13 +281,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     auto mma = [&](auto SC) {
       constexpr int f = decltype(SC)::value;
 #pragma unroll
-      for (int a = 0; a < NA; ++a)
+      for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) Mma<T>::run(af[f][a], bfg[f][b], acc[a][b]);
+        for (int b = 0; b < TN; ++b) Mma<T>::run(bfg[f][b], af[f][a], acc[a][b]);
     };
     // interleave: one MFMA, then one LDS read of the next group's fragments
     auto interleave = [&]() {
-      constexpr int NR = (TN + NA) * CPL, NM = NA * TN * (CPL == 1 ? 1 : 8);
+      constexpr int NR = (TN + TM) * CPL, NM = TM * TN * (CPL == 1 ? 1 : 8);
 #pragma unroll
       for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -299,91 +319,183 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   //           then the LDS store of step kt+1 (whose loads were issued a step
   //           earlier, so vmcnt only waits for them) runs in the middle of the
   //           step's MFMAs instead of after them.
-  gloadA(IC<0>{}, 0);
-  gloadB(IC<0>{}, 0);
-  if (PF == 2 && 1 < nk) {
-    gloadA(IC<1 % NSET>{}, 1);
-    gloadB(IC<1 % NSET>{}, 1);
-  }
-  lstore(IC<0>{}, 0);
-  __syncthreads();
+  // Across tiles: when every tile has an even number of K steps (p.xpf), the
+  // last steps of a tile already load the first steps of the work-group's next
+  // tile, so those loads are in flight while the tile's epilogue stores run;
+  // otherwise each tile starts with its own prologue.
+  auto prologue = [&](int nk) {
+    gloadA(IC<0>{}, 0);
+    gloadB(IC<0>{}, 0);
+    if (PF == 2 && 1 < nk) {
+      gloadA(IC<1 % NSET>{}, 1);
+      gloadB(IC<1 % NSET>{}, 1);
+    }
+    lstore(IC<0>{}, 0);
+    __syncthreads();
+  };
 
-  auto kloop = [&](auto NAC) {
+  TileI cur = decode(lt);
+  rows_of(cur, a_row);
+  set_b(cur);
+  prologue(cur.nk);
+  const bool xpf = p.xpf != 0;
+
+  while (true) {
+    {
+      int t_o = threadIdx.x;
+      asm volatile("" : "+v"(t_o));
+      half = (t_o >> 5) & 1;
+      l32 = t_o & 31;
+      lrow = t_o >> 3;
+      lchunk = t_o & 7;
+    }
+    const int lt_next = lt + per;
+    const bool has_next = lt_next < lt_end;
+    const bool xnext = xpf && has_next;
+    TileI nxt = cur;
+    int n_row[A_LD];
+    if (has_next) nxt = decode(lt_next);
+    if (xnext) rows_of(nxt, n_row);
+    const int nk = cur.nk;
+
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+    // loads for step j of this tile, or (j >= nk) step j - nk of the next one
+    auto loads = [&](auto SETC, auto CHECKC, int j) {
+      constexpr bool CHECK = decltype(CHECKC)::value != 0;
+      if (!CHECK || j < nk) {
+        gloadA(SETC, j);
+        gloadB(SETC, j);
+      } else if (xnext) {
+        if (j == nk) {  // first load of the next tile: switch the source rows
+#pragma unroll
+          for (int i = 0; i < A_LD; ++i) a_row[i] = n_row[i];
+          set_b(nxt);
+        }
+        gloadA(SETC, j - nk);
+        gloadB(SETC, j - nk);
+      }
+    };
     auto step = [&](auto SETC, auto CHECKC, int kt) {
       constexpr int S = decltype(SETC)::value;  // == kt % NSET
       constexpr bool CHECK = decltype(CHECKC)::value != 0;
+      const bool st_next = !CHECK || kt + 1 < nk || xnext;
       if (PF == 1) {
-        if (!CHECK || kt + 1 < nk) {
-          gloadA(IC<0>{}, kt + 1);
-          gloadB(IC<0>{}, kt + 1);
-        }
-        compute(NAC, kt & 1, [] {});
-        if (!CHECK || kt + 1 < nk) lstore(IC<0>{}, (kt + 1) & 1);
+        loads(IC<0>{}, CHECKC, kt + 1);
+        compute(kt & 1, [] {});
+        if (st_next) lstore(IC<0>{}, (kt + 1) & 1);
       } else {
-        if (!CHECK || kt + 2 < nk) {
-          gloadA(IC<S>{}, kt + 2);
-          gloadB(IC<S>{}, kt + 2);
-        }
-        compute(NAC, kt & 1, [&] {
-          if (!CHECK || kt + 1 < nk) lstore(IC<(S + 1) % NSET>{}, (kt + 1) & 1);
+        loads(IC<S>{}, CHECKC, kt + 2);
+        compute(kt & 1, [&] {
+          if (st_next) lstore(IC<(S + 1) % NSET>{}, (kt + 1) & 1);
         });
       }
       __syncthreads();
     };
-    int kt = 0;
-    for (; kt + NSET + 2 <= nk; kt += NSET) {
-      step(IC<0>{}, IC<0>{}, kt);
-      if (NSET > 1) step(IC<1 % NSET>{}, IC<0>{}, kt + 1);
+    // Every subtile is computed, valid rows or not (rows past the valid range
+    // hold copies of a valid row and are never stored): the K loop stays free
+    // of branches, and the MFMA time of a full tile is still below the time to
+    // stream its weights.
+    {
+      int kt = 0;
+      for (; kt + NSET + 2 <= nk; kt += NSET) {
+        step(IC<0>{}, IC<0>{}, kt);
+        if (NSET > 1) step(IC<1 % NSET>{}, IC<0>{}, kt + 1);
+      }
+      for (; kt < nk; kt += NSET) {
+        step(IC<0>{}, IC<1>{}, kt);
+        if (NSET > 1 && kt + 1 < nk) step(IC<1 % NSET>{}, IC<1>{}, kt + 1);
+      }
     }
-    for (; kt < nk; kt += NSET) {
-      step(IC<0>{}, IC<1>{}, kt);
-      if (NSET > 1 && kt + 1 < nk) step(IC<1 % NSET>{}, IC<1>{}, kt + 1);
-    }
-  };
-  // Every subtile is computed, valid rows or not (rows past the valid range
-  // hold copies of a valid row and are never stored): the K loop stays free
-  // of branches, and the MFMA time of a full tile is still below the time to
-  // stream its weights.
-  kloop(IC<TM>{});
 
-  // ---- epilogue
-  TO *C = (TO *)p.C;
+    // ---- epilogue.  The MFMA takes the B fragment as its first operand, so
+    // acc[a][b] is the (B subtile b) x (A subtile a) block: lane l owns A row l32
+    // of subtile a and, in registers 4g .. 4g+3, the four consecutive B columns
+    // 8g + 4 * half .. +3 of subtile b, which leave in one vector store.
+    {
+      const int rows_valid = cur.rows;
+      const int64_t m0 = cur.m0;
+      const int nt = cur.nt;
+      TO *C = (TO *)p.C;
+      const bool vec = (p.ldc % 4) == 0;
 #pragma unroll
-  for (int a = 0; a < TM; ++a) {
-    if (a >= na) continue;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rl = (a * WM + wm) * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-      if (rl >= rows_valid) continue;
-      const int64_t grow = m0 + rl;
-      if (EPI == EPI_GLU) {
-#pragma unroll
-        for (int b = 0; b < TN; b += 2) {
-          const int64_t h = (int64_t)nt * (BN / 2) + wn * (WTN / 2) + (b / 2) * 32 + l32;
-          if (h < p.N / 2) {
-            const float v = situf_(acc[a][b][i], p.beta1) * softcapf_(acc[a][b + 1][i], p.beta2);
-            C[grow * p.ldc + h] = from_f32<TO>(v);
-          }
-        }
-      } else {
+      for (int a = 0; a < TM; ++a) {
+        const int rl = (a * WM + wm) * 32 + l32;
+        if (rl >= rows_valid) continue;
+        const int64_t grow = m0 + rl;
         const float rs = (EPI == EPI_ROWSCALE) ? p.row_scale[grow] : 1.0f;
 #pragma unroll
-        for (int b = 0; b < TN; ++b) {
-          const int64_t col = (int64_t)nt * BN + wn * WTN + b * 32 + l32;
-          if (col >= p.N) continue;
-          float v = acc[a][b][i];
-          if (EPI == EPI_SIGMOID) {
-            if (p.col_bias) v += p.col_bias[col];
-            v = sigmoidf_(v);
-          } else if (EPI == EPI_ROWSCALE) {
-            v *= rs;
+        for (int g = 0; g < 4; ++g) {
+          if (EPI == EPI_GLU) {
+#pragma unroll
+            for (int b = 0; b < TN; b += 2) {
+              const int64_t h0 = (int64_t)nt * (BN / 2) + wn * (WTN / 2) + (b / 2) * 32 + g * 8 + half * 4;
+              float o[4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                o[c] = situf_(acc[a][b][4 * g + c], p.beta1) * softcapf_(acc[a][b + 1][4 * g + c], p.beta2);
+              TO *dst = C + grow * p.ldc + h0;
+              if (vec && h0 + 3 < p.N / 2) {
+                store4(dst, o);
+              } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  if (h0 + c < p.N / 2) dst[c] = from_f32<TO>(o[c]);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int b = 0; b < TN; ++b) {
+              const int64_t c0 = (int64_t)nt * BN + wn * WTN + b * 32 + g * 8 + half * 4;
+              float o[4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                float v = acc[a][b][4 * g + c];
+                if (EPI == EPI_SIGMOID) {
+                  if (p.col_bias) v += p.col_bias[min(c0 + c, (int64_t)p.N - 1)];
+                  v = sigmoidf_(v);
+                } else if (EPI == EPI_ROWSCALE) {
+                  v *= rs;
+                }
+                o[c] = v;
+              }
+              if (EPI == EPI_PARTIAL) {
+                float *dst = (float *)p.C + ((int64_t)cur.ks * p.M + grow) * p.ldc + c0;
+                if (vec && c0 + 3 < p.N) {
+                  store4(dst, o);
+                } else {
+#pragma unroll
+                  for (int c = 0; c < 4; ++c)
+                    if (c0 + c < p.N) dst[c] = o[c];
+                }
+              } else {
+                TO *dst = C + grow * p.ldc + c0;
+                if (vec && c0 + 3 < p.N) {
+                  store4(dst, o);
+                } else {
+#pragma unroll
+                  for (int c = 0; c < 4; ++c)
+                    if (c0 + c < p.N) dst[c] = from_f32<TO>(o[c]);
+                }
+              }
+            }
           }
-          if (EPI == EPI_PARTIAL)
-            ((float *)p.C)[((int64_t)ks * p.M + grow) * p.ldc + col] = v;
-          else
-            C[grow * p.ldc + col] = from_f32<TO>(v);
         }
       }
+    }
+
+    if (!has_next) break;
+    lt = lt_next;
+    cur = nxt;
+    if (!xpf) {
+      rows_of(cur, a_row);
+      set_b(cur);
+      prologue(cur.nk);
     }
   }
 }

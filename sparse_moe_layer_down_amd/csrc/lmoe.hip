@@ -83,7 +83,8 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int bke, bool force) {
   if (tiles <= 0 || nk < 4 || (!force && tiles >= 256)) return {1, std::max(nk, 1)};
   int splits = (int)std::min<int64_t>(cdiv(512, tiles), nk / 2);
   splits = std::max(splits, 1);
-  const int ksteps = (int)cdiv(nk, splits);
+  int ksteps = (int)cdiv(nk, splits);
+  if (ksteps % 2 && nk % 2 == 0) ++ksteps;  // even ranges keep the cross-tile prefetch
   return {(int)cdiv(nk, ksteps), ksteps};
 }
 // How a dense GEMM is run: M <= 64 -> skinny tile with split-K; otherwise the
@@ -110,6 +111,46 @@ int64_t part_bytes(int64_t M, int64_t N, int64_t K, int bke) {
   return (pl.mode == DM_SKINNY || pl.mode == DM_MID_SPLIT) ? (int64_t)pl.sp.splits * M * N * 4 : 0;
 }
 
+WsLayout layout(const lmoe_dims &d, int dtype) {
+  const int64_t es = dtype == LMOE_BF16 ? 2 : 4;
+  const int bke = (int)(128 / es);
+  const int64_t nch = cdiv(d.T, PERM_CHUNK);
+  int64_t sz[R_COUNT_];
+  sz[R_Z] = d.T * d.L * es;
+  sz[R_COUNTS] = d.n * 4;
+  sz[R_OFFS] = (d.n + 1) * 4;
+  sz[R_ROW_TOKEN] = d.T * d.k * 4;
+  sz[R_SLOT_ROW] = d.T * d.k * 4;
+  sz[R_HIDDEN] = d.T * d.k * d.D * es;
+  sz[R_USH] = d.T * d.L * 4;
+  sz[R_V] = d.T * d.L * es;
+  sz[R_SCORES] = d.T * d.n * 4;
+  sz[R_IDX] = d.T * d.k * 4;
+  sz[R_W] = d.T * d.k * 4;
+  sz[R_MASKS] = nch * d.n * 4 * 8;
+  sz[R_CBASE] = nch * d.n * 4;
+  sz[R_TILES1] = max_tiles(d, w12_bm(d)) * 16;
+  sz[R_TILES2] = max_tiles(d, w3_bm(d)) * 16;
+  sz[R_NTILES] = 8;
+  sz[R_ROW_W] = d.T * d.k * 4;
+  sz[R_HSH] = d.T * d.n_shared * d.D * es;
+  sz[R_YSTAGE] = d.T * d.k * d.L * (es == 2 ? 2 : 4);  // per-slot routed rows: fp16 (bf16 inputs) or fp32
+  // split-K partial sums: the dense GEMMs run one after another and share one buffer
+  int64_t part = std::max(part_bytes<CfgDense>(d.T, d.L, d.d, bke), part_bytes<CfgRouter>(d.T, d.n, d.L, bke));
+  part = std::max(part, part_bytes<CfgDense>(d.T, 2 * d.n_shared * d.D, d.L, bke));
+  part = std::max(part, part_bytes<CfgDense>(d.T, d.L, d.n_shared * d.D, bke));
+  part = std::max(part, part_bytes<CfgDense>(d.T, d.d, d.L, bke));
+  sz[R_PART] = part;
+  WsLayout w;
+  int64_t o = 0;
+  for (int i = 0; i < R_COUNT_; ++i) {
+    w.off[i] = o;
+    o += align256(sz[i]);
+  }
+  w.total = o;
+  return w;
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_dims(const lmoe_dims *d) {
@@ -124,21 +165,46 @@ int check_dims(const lmoe_dims *d) {
   return LMOE_OK;
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// Persistent launch: one work-group per resident slot (CUs x work-groups per
+// CU), each walking its share of the logical tiles.
 template <typename C, typename T, typename TO, int EPI, bool GATHER, bool GROUPED>
 hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   constexpr int lds = 2 * (C::BM + C::BN) * 128;
+  constexpr int threads = 64 * C::WM * C::WN;
   auto kern = gemm_kernel<T, TO, C::BM, C::BN, C::WM, C::WN, C::PF, EPI, GATHER, GROUPED>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
+  static int occ = 0;
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, lds) != hipSuccess || o <= 0) o = 1;
+    occ = o;
+  }
+  constexpr int bke = 128 / (int)sizeof(T);
   a.tiles_n = (int)cdiv(a.N, C::BN);
   if (!GROUPED) a.tiles_m = (int)cdiv(a.M, C::BM);
   a.n_logical = a.tiles_m * a.tiles_n * (GROUPED ? 1 : std::max(a.splits, 1));
   if (a.n_logical == 0) return hipSuccess;
-  a.xcd_chunk = a.n_logical >= 1024 ? 8 : 1;
-  const int64_t grid = cdiv(a.n_logical, 8 * a.xcd_chunk) * 8 * a.xcd_chunk;
+  const int nk_all = a.K / bke;
+  a.xpf = (nk_all % 2 == 0) && (a.splits <= 1 || a.ksteps % 2 == 0);
+  int64_t grid = std::min<int64_t>(a.n_logical, (int64_t)device_cus() * occ);
+  if (grid >= 8) grid = grid / 8 * 8;
   if (a.kb_len == 0) a.kb_len = a.K;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * C::WM * C::WN), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -200,7 +266,10 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   int32_t *ntiles = (int32_t *)(ws + Lw.off[R_NTILES]);
   float *row_w = (float *)(ws + Lw.off[R_ROW_W]);
   T *hsh = (T *)(ws + Lw.off[R_HSH]);
-  float *ystage = (float *)(ws + Lw.off[R_YSTAGE]);
+  // per-slot routed outputs: fp16 for bf16 inputs (11-bit mantissa, summed in
+  // fp32 by the combine), fp32 for fp32 inputs
+  using TS = typename std::conditional<sizeof(T) == 2, f16, float>::type;
+  TS *ystage = (TS *)(ws + Lw.off[R_YSTAGE]);
   float *part = (float *)(ws + Lw.off[R_PART]);
   const int T_ = (int)d.T, n = (int)d.n, k = (int)d.k, L = (int)d.L, D = (int)d.D, ns = (int)d.n_shared;
   hipError_t e;
@@ -281,8 +350,8 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     a.A = hid; a.lda = D; a.B = w.w3; a.ldb = D; a.b_group_stride = (int64_t)L * D;
     a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles2; a.ntiles = ntiles + 1;
     a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w;
-    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, float, EPI_ROWSCALE, false, true>(a, st)));
-    else LMOE_TRY((launch_gemm<CfgW3, T, float, EPI_ROWSCALE, false, true>(a, st)));
+    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, TS, EPI_ROWSCALE, false, true>(a, st)));
+    else LMOE_TRY((launch_gemm<CfgW3, T, TS, EPI_ROWSCALE, false, true>(a, st)));
   }
   // 9 combine + RMSNorm
   LMOE_MARK(8);
@@ -290,9 +359,9 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     const int nch8 = L / 8;
     const float *us = ns > 0 ? ush : nullptr;
     const T *gain = (const T *)w.rms_gain;
-    if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, 1>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
-    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, 2>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
-    else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, 4>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
+    if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 1>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
+    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 2>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
+    else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 4>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
     LMOE_TRY(hipGetLastError());
   }
   // 10 y = v W_up^T

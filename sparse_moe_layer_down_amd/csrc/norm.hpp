@@ -1,6 +1,7 @@
 // Combine + RMSNorm: the aggregated latent of token t is the shared-expert part
-// (fp32, written by the shared W3 GEMM) plus the k routed rows of t (fp32, each
-// already scaled by its routing weight in the W3 epilogue).  The single
+// (fp32, written by the shared W3 GEMM) plus the k routed rows of t (staged by
+// the W3 epilogue already scaled by their routing weights: fp16 for bf16
+// inputs, fp32 for fp32 inputs), summed in fp32.  The single
 // retained RMSNorm then gives v = gain * u / sqrt(mean(u^2) + eps)
 // ("Kimi K3 Architecture Deep Dive" §2: one RMS norm before the
 // up-projection; LeiPhone report "Keeping the numbers in range": after
@@ -11,9 +12,9 @@
 
 namespace lmoe {
 
-template <typename T, int CPT>
+template <typename T, typename TS, int CPT>
 __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float *__restrict__ ushared,
-                                                              const float *__restrict__ ystage,
+                                                              const TS *__restrict__ ystage,
                                                               const int32_t *__restrict__ slot_row,
                                                               const T *__restrict__ gain, T *__restrict__ v,
                                                               int L, int k, float eps) {

@@ -13,6 +13,17 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long CPU test")
 
 
+# max|err| / RMS of every floating-point parity check, printed at the end of the run
+MARGINS = []
+
+
+def pytest_terminal_summary(terminalreporter):
+    if MARGINS:
+        terminalreporter.write_line("parity margins (max|err| / RMS(ref), tolerance):")
+        for label, v, t in MARGINS:
+            terminalreporter.write_line(f"  {label:40s} {v:.3e}  tol {t:.0e}  ({100 * v / t:.0f}% of tol)")
+
+
 def _ensure_host_libs():
     """Build the generator's host filler if nothing is built yet (gcc, seconds)."""
     lib = os.path.join(ROOT, "synth", "libsynth_host.so")

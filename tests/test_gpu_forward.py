@@ -28,11 +28,16 @@ def tol(dtype):
     return 1e-5 if dtype == "f32" else 2e-2
 
 
-def rel_err(got, want):
+def rel_err(got, want, label=None, t=None):
+    """max|got - want| / RMS(want); recorded for the run's margin summary when labelled."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     rms = np.sqrt(np.mean(want ** 2))
-    return np.abs(got - want).max() / rms if want.size else 0.0
+    e = np.abs(got - want).max() / rms if want.size else 0.0
+    if label is not None:
+        import conftest
+        conftest.MARGINS.append((label, float(e), t))
+    return e
 
 
 def run_gpu(cfg, x=None, weights=None, step=None):
@@ -72,8 +77,8 @@ def check_against_oracle(cfg, gpu, x_host, P, rows=None):
     assert np.array_equal(np.sort(own["idx"][clear], 1), np.sort(g_idx[clear], 1)), "top-k sets differ"
     # expert math on the GPU's routing
     forced = ref.forward(x_host, P, cfg.k, cfg.n_shared, dt, cfg.beta1, cfg.beta2, cfg.eps, forced_idx=g_idx)
-    assert rel_err(gpu["z"][sel], forced["z_pre"]) <= tol(dt), "z"
-    assert rel_err(gpu["s"][sel], forced["s"]) <= tol(dt), "scores"
+    assert rel_err(gpu["z"][sel], forced["z_pre"], f"{cfg.name} z", tol(dt)) <= tol(dt), "z"
+    assert rel_err(gpu["s"][sel], forced["s"], f"{cfg.name} s", tol(dt)) <= tol(dt), "scores"
     # routing weights from the GPU's own fp32 scores, order matching the GPU's list
     g_ref = ref.routing_weights(gpu["s"][sel], g_idx)
     assert np.abs(gpu["g"][sel] - g_ref).max() <= 1e-6
@@ -81,8 +86,8 @@ def check_against_oracle(cfg, gpu, x_host, P, rows=None):
     sb = gpu["s"][sel] + P.bias()[None, :]
     srt = np.take_along_axis(sb, g_idx, 1)
     assert np.all(np.diff(srt.astype(np.float32), axis=1) <= 0)
-    assert rel_err(gpu["v"][sel], forced["v_pre"]) <= tol(dt), "v"
-    assert rel_err(gpu["y"][sel], forced["y_pre"]) <= tol(dt), "y"
+    assert rel_err(gpu["v"][sel], forced["v_pre"], f"{cfg.name} v", tol(dt)) <= tol(dt), "v"
+    assert rel_err(gpu["y"][sel], forced["y_pre"], f"{cfg.name} y", tol(dt)) <= tol(dt), "y"
     return own, forced
 
 

@@ -32,10 +32,10 @@ def sampled_check(cfg, gpu, rows, P):
     g_idx = gpu["idx"][rows]
     assert np.array_equal(np.sort(own["idx"][clear], 1), np.sort(g_idx[clear], 1))
     forced = ref.forward(x, P, cfg.k, cfg.n_shared, cfg.dtype, cfg.beta1, cfg.beta2, cfg.eps, forced_idx=g_idx)
-    assert rel_err(gpu["z"][rows], forced["z_pre"]) <= tol(cfg.dtype)
-    assert rel_err(gpu["s"][rows], forced["s"]) <= tol(cfg.dtype)
-    assert rel_err(gpu["v"][rows], forced["v_pre"]) <= tol(cfg.dtype)
-    assert rel_err(gpu["y"][rows], forced["y_pre"]) <= tol(cfg.dtype)
+    assert rel_err(gpu["z"][rows], forced["z_pre"], f"{cfg.name} T={cfg.T} sampled z", tol(cfg.dtype)) <= tol(cfg.dtype)
+    assert rel_err(gpu["s"][rows], forced["s"], f"{cfg.name} T={cfg.T} sampled s", tol(cfg.dtype)) <= tol(cfg.dtype)
+    assert rel_err(gpu["v"][rows], forced["v_pre"], f"{cfg.name} T={cfg.T} sampled v", tol(cfg.dtype)) <= tol(cfg.dtype)
+    assert rel_err(gpu["y"][rows], forced["y_pre"], f"{cfg.name} T={cfg.T} sampled y", tol(cfg.dtype)) <= tol(cfg.dtype)
     return own
 
 
