@@ -28,6 +28,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-qb-protocol", action="store_true",
+                    help="skip the 20-step Quantile Balancing run on the skewed-routing workload")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel of known "
@@ -43,6 +45,50 @@ def routed_w12_bytes(cfg, counts):
     touched = int((counts > 0).sum())
     rows = int(counts.sum())
     return touched * 2 * cfg.D * cfg.L * es + rows * (cfg.L + cfg.D) * es, touched
+
+
+def qb_protocol(w, dev, lmoe, synth):
+    """Skewed-routing workload (K3 shapes, T=32768, Zipf(1.1) logit skew, same weights as the
+    prefill workload): forward -> expert loads -> lmoe_qb_update (1000-bin histograms, bias solve
+    for share k/n) -> next step's bias, for 20 steps; loads at step 0 (bias 0) and step 20
+    (bias from step 19, fresh batch).  Also times the histogram + solve launch."""
+    import torch
+    cfg = synth.get_config("C4")
+    w = dict(w)
+    w["router_logit_offset"] = torch.as_tensor(synth.zipf_logit_offset(cfg)).to(dev)
+    bias = torch.zeros(cfg.n, dtype=torch.float32, device=dev)
+    w["router_bias"] = bias
+    x = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
+    dims = lmoe.dims_of(x, w, cfg.k)
+    ws = lmoe.make_workspace(dims, x.dtype, dev)
+    y = torch.empty_like(x)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    s = torch.empty((cfg.T, cfg.n), dtype=torch.float32, device=dev)
+    hist = torch.empty((cfg.n, cfg.nbins), dtype=torch.int32, device=dev)
+    qws = torch.empty(lmoe.qb_workspace_size(cfg.nbins), dtype=torch.uint8, device=dev)
+    stats, qb_ms = {}, []
+    for t in range(cfg.qb_steps + 1):
+        x.copy_(synth.params.device_x(cfg, dev, step=t))
+        lmoe.forward(x, w, cfg.k, y=y, topk_idx=idx, scores=s, workspace=ws, beta1=cfg.beta1, beta2=cfg.beta2,
+                     eps=cfg.eps)
+        if t in (0, cfg.qb_steps):
+            load = torch.bincount(idx.flatten().long(), minlength=cfg.n).double()
+            m = load.mean()
+            stats[t] = (float(load.max() / m), float(load.min() / m))
+        if t < cfg.qb_steps:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lmoe.qb_update(s, cfg.k, hist, bias, accumulate=False, solve=True, workspace=qws)
+            e1.record()
+            torch.cuda.synchronize()
+            qb_ms.append(e0.elapsed_time(e1))
+    ms = float(sorted(qb_ms)[len(qb_ms) // 2])
+    return {"workload": f"C4: T={cfg.T}, K3 shapes, Zipf({cfg.zipf_s}) logit skew alpha={cfg.zipf_alpha}",
+            "steps": cfg.qb_steps, "nbins": cfg.nbins,
+            "load_max_over_mean": {"step0_bias0": stats[0][0], f"step{cfg.qb_steps}": stats[cfg.qb_steps][0]},
+            "load_min_over_mean": {"step0_bias0": stats[0][1], f"step{cfg.qb_steps}": stats[cfg.qb_steps][1]},
+            "qb_update_ms_median": ms,
+            "qb_scores_read_GBps": cfg.T * cfg.n * 4 / (ms * 1e-3) / 1e9}
 
 
 def cpu_baseline(cfg, n_tok):
@@ -157,6 +203,10 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": w12_bytes, "experts_touched": touched,
                      "avg_ms": w12_ms},
     }
+    if not args.no_qb_protocol and cfg.name == "C2":
+        del ws
+        torch.cuda.empty_cache()
+        out["qb_protocol"] = qb_protocol(w, dev, lmoe, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
     print(json.dumps(out))

@@ -69,9 +69,33 @@ LMOE_DEV void store8(float *p, const float *v) {
 
 // softcap(x; beta) = beta * tanh(x / beta); SiTU(x; beta) = softcap(x; beta) * sigmoid(x)
 // ("Kimi K3 Architecture Deep Dive" §1)
+// The router's sigmoid uses the library expf (its scores feed the top-k and
+// the QB histogram); the gate epilogue, evaluated for every hidden unit of
+// every dispatched row, uses the hardware exp2 / reciprocal:
+//   tanh(y) = sign(y) (1 - e^{-2|y|}) / (1 + e^{-2|y|})     for |y| >= 3/8,
+//   tanh(y) = y - y^3/3 + 2y^5/15 - 17y^7/315 + 62y^9/2835 - 1382y^11/155925  below
+// (the odd Taylor series; the truncation error there is under 2e-8 relative), so
+// the first form never cancels by more than a factor of 3.5; both stay within
+// about 3e-7 relative of tanh, NaN and +-inf included.
 LMOE_DEV float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
-LMOE_DEV float softcapf_(float x, float beta) { return beta * tanhf(x / beta); }
-LMOE_DEV float situf_(float x, float beta) { return softcapf_(x, beta) * sigmoidf_(x); }
+LMOE_DEV float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+LMOE_DEV float sigmoid_hw(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_hw(-x)); }
+LMOE_DEV float tanh_hw(float y) {
+  const float a = fabsf(y);
+  const float t = exp_hw(-2.0f * a);
+  const float big = (1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t);
+  const float y2 = y * y;
+  float q = -1382.0f / 155925.0f;
+  q = 62.0f / 2835.0f + y2 * q;
+  q = -17.0f / 315.0f + y2 * q;
+  q = 2.0f / 15.0f + y2 * q;
+  q = -1.0f / 3.0f + y2 * q;
+  q = 1.0f + y2 * q;
+  const float r = a < 0.375f ? a * q : big;
+  return copysignf(r, y);
+}
+LMOE_DEV float softcapf_(float x, float beta) { return beta * tanh_hw(x * (1.0f / beta)); }  // 1/beta is hoisted
+LMOE_DEV float situf_(float x, float beta) { return softcapf_(x, beta) * sigmoid_hw(x); }
 
 LMOE_DEV float wave_sum(float v) {
 #pragma unroll
