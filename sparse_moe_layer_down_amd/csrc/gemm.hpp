@@ -114,7 +114,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of the load pass");
   static_assert(BM % (32 * WM) == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(EPI != EPI_GLU || TN % 2 == 0, "GLU needs W1/W2 subtile pairs");
-  static_assert(PF == 1 || PF == 2, "prefetch distance");
+  static_assert(PF >= 1 && PF <= 4, "prefetch distance");
   static_assert(NG == 2 || NG == 4, "16-K groups per 128-byte K step");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -314,21 +314,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   // Pipeline (one barrier per K step).
   //  PF == 1: A(kt+1), B(kt+1) are loaded at the start of step kt and stored to
   //           the other LDS buffer after the step's MFMAs.
-  //  PF == 2: A(j), B(j) live in register set j % 2 and are loaded two steps
-  //           ahead; during step kt the loads of step kt+2 are issued first,
-  //           then the LDS store of step kt+1 (whose loads were issued a step
-  //           earlier, so vmcnt only waits for them) runs in the middle of the
-  //           step's MFMAs instead of after them.
-  // Across tiles: when every tile has an even number of K steps (p.xpf), the
-  // last steps of a tile already load the first steps of the work-group's next
-  // tile, so those loads are in flight while the tile's epilogue stores run;
-  // otherwise each tile starts with its own prologue.
+  //  PF >= 2: A(j), B(j) live in register set j % PF and are loaded PF steps
+  //           ahead; during step kt the loads of step kt+PF are issued first,
+  //           then the LDS store of step kt+1 (whose loads were issued PF-1
+  //           steps earlier, so vmcnt only waits for them) runs in the middle
+  //           of the step's MFMAs instead of after them.
+  // Across tiles: when every tile's number of K steps is a multiple of 2 and
+  // of PF (p.xpf), the last steps of a tile already load the first steps of
+  // the work-group's next tile, so those loads are in flight while the tile's
+  // epilogue stores run; otherwise each tile starts with its own prologue.
   auto prologue = [&](int nk) {
     gloadA(IC<0>{}, 0);
     gloadB(IC<0>{}, 0);
-    if (PF == 2 && 1 < nk) {
+    if (PF > 1 && 1 < nk) {
       gloadA(IC<1 % NSET>{}, 1);
       gloadB(IC<1 % NSET>{}, 1);
+    }
+    if (PF > 2 && 2 < nk) {
+      gloadA(IC<2 % NSET>{}, 2);
+      gloadB(IC<2 % NSET>{}, 2);
+    }
+    if (PF > 3 && 3 < nk) {
+      gloadA(IC<3 % NSET>{}, 3);
+      gloadB(IC<3 % NSET>{}, 3);
     }
     lstore(IC<0>{}, 0);
     __syncthreads();
@@ -390,12 +398,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
         compute(kt & 1, [] {});
         if (st_next) lstore(IC<0>{}, (kt + 1) & 1);
       } else {
-        loads(IC<S>{}, CHECKC, kt + 2);
+        loads(IC<S>{}, CHECKC, kt + PF);
         compute(kt & 1, [&] {
           if (st_next) lstore(IC<(S + 1) % NSET>{}, (kt + 1) & 1);
         });
       }
       __syncthreads();
+    };
+    // NSET consecutive steps (register set indices known at compile time)
+    auto steps = [&](auto CHECKC, int kt) {
+      constexpr bool CHECK = decltype(CHECKC)::value != 0;
+      step(IC<0>{}, CHECKC, kt);
+      if (NSET > 1 && (!CHECK || kt + 1 < nk)) step(IC<1 % NSET>{}, CHECKC, kt + 1);
+      if (NSET > 2 && (!CHECK || kt + 2 < nk)) step(IC<2 % NSET>{}, CHECKC, kt + 2);
+      if (NSET > 3 && (!CHECK || kt + 3 < nk)) step(IC<3 % NSET>{}, CHECKC, kt + 3);
     };
     // Every subtile is computed, valid rows or not (rows past the valid range
     // hold copies of a valid row and are never stored): the K loop stays free
@@ -403,14 +419,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     // stream its weights.
     {
       int kt = 0;
-      for (; kt + NSET + 2 <= nk; kt += NSET) {
-        step(IC<0>{}, IC<0>{}, kt);
-        if (NSET > 1) step(IC<1 % NSET>{}, IC<0>{}, kt + 1);
-      }
-      for (; kt < nk; kt += NSET) {
-        step(IC<0>{}, IC<1>{}, kt);
-        if (NSET > 1 && kt + 1 < nk) step(IC<1 % NSET>{}, IC<1>{}, kt + 1);
-      }
+      for (; kt + NSET + PF <= nk; kt += NSET) steps(IC<0>{}, kt);
+      for (; kt < nk; kt += NSET) steps(IC<1>{}, kt);
     }
 
     // ---- epilogue.  The MFMA takes the B fragment as its first operand, so

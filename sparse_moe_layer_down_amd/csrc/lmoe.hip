@@ -200,7 +200,10 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   a.n_logical = a.tiles_m * a.tiles_n * (GROUPED ? 1 : std::max(a.splits, 1));
   if (a.n_logical == 0) return hipSuccess;
   const int nk_all = a.K / bke;
-  a.xpf = (nk_all % 2 == 0) && (a.splits <= 1 || a.ksteps % 2 == 0);
+  // cross-tile prefetch needs every tile's step count to be a multiple of 2 (LDS
+  // buffer parity) and of the number of register sets
+  constexpr int xm = (C::PF % 2 == 0) ? C::PF : 2 * C::PF;
+  a.xpf = (nk_all % xm == 0) && (a.splits <= 1 || a.ksteps % xm == 0);
   int64_t grid = std::min<int64_t>(a.n_logical, (int64_t)device_cus() * occ);
   if (grid >= 8) grid = grid / 8 * 8;
   if (a.kb_len == 0) a.kb_len = a.K;
@@ -450,7 +453,7 @@ size_t lmoe_qb_workspace_size(int32_t nbins) {
 int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
                    int accumulate, float *bias, int solve, void *workspace, size_t workspace_bytes,
                    void *stream) {
-  if (T < 0 || n < 1 || n > ((int64_t)1 << 30) || k < 1 || k > n) return LMOE_ERR_SHAPE;
+  if (T < 0 || n < 1 || n > ((int64_t)1 << 20) || k < 1 || k > n) return LMOE_ERR_SHAPE;
   if (nbins < 1 || nbins > 16384) return LMOE_ERR_VALUE;
   if (!hist || (T > 0 && !scores) || (solve && (!bias || !workspace))) return LMOE_ERR_NULL;
   if (!aligned16(hist) || (scores && !aligned16(scores)) || (bias && !aligned16(bias)) ||
@@ -470,18 +473,20 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
     // experts per work-group: as many B-bin LDS histograms as fit in 64 KB (max 16)
     int eg = (int)std::min<int64_t>(16, std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4)));
     const int64_t groups = cdiv(n, eg);
-    // token runs: aim for ~4 work-groups per CU in total
-    int64_t runs = std::max<int64_t>(1, std::min<int64_t>(cdiv(1024, groups), cdiv(T, 256)));
+    // token runs: about two work-groups per CU in total (fewer runs -> fewer global merges)
+    int64_t runs = std::max<int64_t>(1, std::min<int64_t>(cdiv(2 * device_cus(), groups), cdiv(T, 256)));
     const int64_t tpb = cdiv(T, runs);
-    runs = cdiv(T, tpb);
-    if (groups > 65535 || runs > 65535) return LMOE_ERR_SHAPE;
+    runs = cdiv(T, tpb);  // <= 2 * CUs: within the grid's y limit
     hipLaunchKernelGGL(qb_hist_kernel, dim3((unsigned)groups, (unsigned)runs), dim3(256),
                        (size_t)eg * nbins * 4, st, scores, T, ni, kb, eg, tpb, hist);
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
   }
   if (solve) {
-    long long *pooled = (long long *)workspace;
-    hipLaunchKernelGGL(qb_pool_kernel, dim3((unsigned)cdiv(nbins, 64)), dim3(256), 0, st, hist, ni, kb, pooled);
+    unsigned long long *pooled = (unsigned long long *)workspace;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)cdiv(nbins, 256)), dim3(256), 0, st, pooled, (int64_t)nbins);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+    hipLaunchKernelGGL(qb_pool_kernel, dim3((unsigned)cdiv(nbins, 64), (unsigned)cdiv(n, QB_POOL_SLICE)), dim3(256), 0,
+                       st, hist, ni, kb, pooled);
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
     hipLaunchKernelGGL(qb_solve_kernel, dim3((unsigned)cdiv(n, 4)), dim3(256), 0, st, hist, pooled, ni, kb, (int)k,
                        bias);

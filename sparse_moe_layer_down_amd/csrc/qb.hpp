@@ -7,7 +7,7 @@
 //   qb_hist_kernel   LDS-privatised histogram: a work-group owns EG experts
 //                    x a run of tokens, counts in LDS with ds atomics, then adds
 //                    its non-zero bins to the global int32 histogram.
-//   qb_pool_kernel   pooled histogram sum_e H[e] (int64), one lane per bin.
+//   qb_pool_kernel   pooled histogram sum_e H[e] (int64), per expert slice, atomically summed.
 //   qb_solve_kernel  one wavefront per expert: tail sums G(j) by a wave scan,
 //                    j* = max{j : G(j) >= c}, q by linear interpolation inside
 //                    bin j*, bias = fp32(tau - q) with tau read the same way
@@ -31,7 +31,10 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
-// grid: (expert groups, token runs); dynamic LDS = eg * nbins * 4 bytes
+// grid: (expert groups, token runs); dynamic LDS = eg * nbins * 4 bytes.
+// When n and the group width are multiples of 4, each thread reads four
+// adjacent experts of a token as one 16-B load and four tokens per iteration;
+// otherwise one thread walks the group's experts of one token at a time.
 __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ scores, int64_t T, int n,
                                                       int nbins, int eg, int64_t tokens_per_block,
                                                       int32_t *__restrict__ hist) {
@@ -43,11 +46,34 @@ __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ 
   __syncthreads();
   const int64_t t0 = (int64_t)blockIdx.y * tokens_per_block;
   const int64_t t1 = min(T, t0 + tokens_per_block);
-  const int64_t cnt = (t1 - t0) * ne;
-  for (int64_t i = threadIdx.x; i < cnt; i += blockDim.x) {
-    const int64_t t = t0 + i / ne;
-    const int e = (int)(i % ne);
-    atomicAdd(&h[e * nbins + qb_bin(scores[t * n + e0 + e], nbins)], 1);
+  if ((n & 3) == 0 && (ne & 3) == 0) {
+    const int nq = ne >> 2;            // 16-B quads per token
+    const int rows = 256 / nq;          // tokens per pass
+    const int tr = threadIdx.x / nq, q = threadIdx.x - tr * nq;
+    if (tr < rows) {
+      const float *base = scores + e0 + q * 4;
+      int32_t *hq = h + q * 4 * nbins;
+      int64_t t = t0 + tr;
+      for (; t + 3 * rows < t1; t += 4 * rows) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *(const f32x4 *)(base + (t + u * rows) * n);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) atomicAdd(&hq[c * nbins + qb_bin(v[u][c], nbins)], 1);
+      }
+      for (; t < t1; t += rows) {
+        const f32x4 v = *(const f32x4 *)(base + t * n);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) atomicAdd(&hq[c * nbins + qb_bin(v[c], nbins)], 1);
+      }
+    }
+  } else {
+    for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+      const float *row = scores + t * n + e0;
+      for (int e = 0; e < ne; ++e) atomicAdd(&h[e * nbins + qb_bin(row[e], nbins)], 1);
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < ne * nbins; i += blockDim.x) {
@@ -56,19 +82,30 @@ __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ 
   }
 }
 
-// pooled[j] = sum_e hist[e][j]; block of 256 threads = 64 bins x 4 expert stripes
+// pooled[j] = sum_e hist[e][j]: grid (bin chunks of 64, expert slices); a
+// block of 256 threads = 64 bins x 4 expert stripes sums its slice and adds it
+// to pooled (zeroed beforehand) with one 64-bit atomic per bin.
+constexpr int QB_POOL_SLICE = 64;  // experts per block
 __global__ __launch_bounds__(256) void qb_pool_kernel(const int32_t *__restrict__ hist, int n, int nbins,
-                                                      long long *__restrict__ pooled) {
+                                                      unsigned long long *__restrict__ pooled) {
   __shared__ long long part[4][64];
   const int j = blockIdx.x * 64 + (threadIdx.x & 63);
   const int stripe = threadIdx.x >> 6;
+  const int ea = blockIdx.y * QB_POOL_SLICE, eb = min(n, ea + QB_POOL_SLICE);
   long long s = 0;
   if (j < nbins)
-    for (int e = stripe; e < n; e += 4) s += hist[(int64_t)e * nbins + j];
+    for (int e = ea + stripe; e < eb; e += 4) s += hist[(int64_t)e * nbins + j];
   part[stripe][threadIdx.x & 63] = s;
   __syncthreads();
-  if (stripe == 0 && j < nbins)
-    pooled[j] = part[0][threadIdx.x] + part[1][threadIdx.x] + part[2][threadIdx.x] + part[3][threadIdx.x];
+  if (stripe == 0 && j < nbins) {
+    const long long v = part[0][threadIdx.x] + part[1][threadIdx.x] + part[2][threadIdx.x] + part[3][threadIdx.x];
+    if (v) atomicAdd(&pooled[j], (unsigned long long)v);
+  }
+}
+
+__global__ void fill_u64_kernel(unsigned long long *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0ull;
 }
 
 // Upper-tail read of one histogram by a full wavefront.  Returns q, or a NaN
@@ -119,7 +156,7 @@ LMOE_DEV double qb_read_wave(const CT *h, int nbins, long long k, long long n) {
 }
 
 __global__ __launch_bounds__(256) void qb_solve_kernel(const int32_t *__restrict__ hist,
-                                                       const long long *__restrict__ pooled, int n, int nbins,
+                                                       const unsigned long long *__restrict__ pooled, int n, int nbins,
                                                        int k, float *__restrict__ bias) {
 #pragma clang fp contract(off)
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;

@@ -52,11 +52,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ s, 
   for (int t = wave; t < T; t += nwaves) {
     const float *row = s + (int64_t)t * n;
     uint64_t key[MAXJ];
+    float sv_[MAXJ], bv_[MAXJ];
+    // all loads first (clamped, unconditional), so they are in flight together
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int e = min(lane + 64 * j, n - 1);
+      sv_[j] = row[e];
+      bv_[j] = bias[e];
+    }
 #pragma unroll
     for (int j = 0; j < MAXJ; ++j) {
       const int e = lane + 64 * j;
-      key[j] = 0;  // padding ranks below every real expert (NaN included)
-      if (e < n) key[j] = ((uint64_t)ord_f32(row[e] + bias[e]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+      // padding ranks below every real expert (NaN included)
+      key[j] = e < n ? ((uint64_t)ord_f32(sv_[j] + bv_[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
     }
     uint64_t best = 0;
 #pragma unroll

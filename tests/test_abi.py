@@ -99,6 +99,7 @@ def test_qb_validation():
     q = lib().lmoe_qb_update
     assert q(FAKE, 10, 896, 0, 1000, FAKE, 0, FAKE, 1, FAKE, 1 << 20, None) == -2   # k = 0
     assert q(FAKE, 10, 896, 16, 0, FAKE, 0, FAKE, 1, FAKE, 1 << 20, None) == -7     # no bins
+    assert q(FAKE, 10, (1 << 20) + 1, 16, 1000, FAKE, 0, FAKE, 1, FAKE, 1 << 30, None) == -2  # too many experts
     assert q(FAKE, 10, 896, 16, 1000, None, 0, FAKE, 1, FAKE, 1 << 20, None) == -1  # no histogram
     assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, None, 1, FAKE, 1 << 20, None) == -1  # solve without bias
     assert q(FAKE, 10, 896, 16, 1000, FAKE + 4, 0, FAKE, 1, FAKE, 1 << 20, None) == -4
