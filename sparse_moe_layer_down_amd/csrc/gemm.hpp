@@ -95,6 +95,121 @@ LMOE_DEV int swz(int r, int c) { return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)
 
 template <int V> struct IC { static constexpr int value = V; };
 
+// One logical tile: rows [m0, m0 + rows) (grouped: of expert b_off / stride),
+// N tile nt, split ks covering K steps [kbeg, kbeg + nk).
+struct TileI {
+  int64_t m0, b_off;
+  int rows, nt, ks, kbeg, nk;
+};
+
+// Logical tile l -> TileI.  Grouped: entry l / tiles_n of the device tile table.
+// Dense: split-major, then groups of 8 M tiles walked down before across.
+template <int BM, bool GROUPED>
+LMOE_DEV TileI decode_tile(const GemmArgs &p, int l, int nk_all) {
+  TileI t;
+  t.ks = 0;
+  t.b_off = 0;
+  if (GROUPED) {
+    const int j = l / p.tiles_n;
+    t.nt = l % p.tiles_n;
+    const int4 e = p.tiles[j];
+    t.m0 = e.y;
+    t.rows = e.z - e.y;
+    t.b_off = (int64_t)e.x * p.b_group_stride;
+  } else {
+    constexpr int GM = 8;
+    const int per_split = p.tiles_m * p.tiles_n;
+    t.ks = l / per_split;
+    const int lm = l % per_split;
+    const int span = GM * p.tiles_n;
+    const int g = lm / span, first = g * GM;
+    const int gsz = min(p.tiles_m - first, GM);
+    const int mt = first + (lm % span) % gsz;
+    t.nt = (lm % span) / gsz;
+    t.m0 = (int64_t)mt * BM;
+    t.rows = min(BM, p.M - (int)t.m0);
+  }
+  t.kbeg = t.ks * p.ksteps;
+  t.nk = (p.splits > 1) ? min(p.ksteps, nk_all - t.kbeg) : nk_all;
+  return t;
+}
+
+// Epilogue of one output tile.  The MFMA takes the B fragment as its first
+// operand, so acc[a][b] is the (B subtile b) x (A subtile a) block: lane l owns
+// A row l32 of subtile a (tile row (a * WM + wm) * 32 + l32) and, in registers
+// 4g .. 4g+3, the four consecutive B columns 8g + 4 * half .. +3 of subtile b,
+// which leave in one vector store.
+template <typename TO, int EPI, int BN, int WTN, int WM, int TM, int TN>
+LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, int rows_valid, int nt, int ks,
+                         int wm, int wn, int half, int l32) {
+  TO *C = (TO *)p.C;
+  const bool vec = (p.ldc % 4) == 0;
+#pragma unroll
+  for (int a = 0; a < TM; ++a) {
+    const int rl = (a * WM + wm) * 32 + l32;
+    if (rl >= rows_valid) continue;
+    const int64_t grow = m0 + rl;
+    const float rs = (EPI == EPI_ROWSCALE) ? p.row_scale[grow] : 1.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (EPI == EPI_GLU) {
+#pragma unroll
+        for (int b = 0; b < TN; b += 2) {
+          const int64_t h0 = (int64_t)nt * (BN / 2) + wn * (WTN / 2) + (b / 2) * 32 + g * 8 + half * 4;
+          float o[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            o[c] = situf_(acc[a][b][4 * g + c], p.beta1) * softcapf_(acc[a][b + 1][4 * g + c], p.beta2);
+          TO *dst = C + grow * p.ldc + h0;
+          if (vec && h0 + 3 < p.N / 2) {
+            store4(dst, o);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (h0 + c < p.N / 2) dst[c] = from_f32<TO>(o[c]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const int64_t c0 = (int64_t)nt * BN + wn * WTN + b * 32 + g * 8 + half * 4;
+          float o[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            float v = acc[a][b][4 * g + c];
+            if (EPI == EPI_SIGMOID) {
+              if (p.col_bias) v += p.col_bias[min(c0 + c, (int64_t)p.N - 1)];
+              v = sigmoidf_(v);
+            } else if (EPI == EPI_ROWSCALE) {
+              v *= rs;
+            }
+            o[c] = v;
+          }
+          if (EPI == EPI_PARTIAL) {
+            float *dst = (float *)p.C + ((int64_t)ks * p.M + grow) * p.ldc + c0;
+            if (vec && c0 + 3 < p.N) {
+              store4(dst, o);
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                if (c0 + c < p.N) dst[c] = o[c];
+            }
+          } else {
+            TO *dst = C + grow * p.ldc + c0;
+            if (vec && c0 + 3 < p.N) {
+              store4(dst, o);
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                if (c0 + c < p.N) dst[c] = from_f32<TO>(o[c]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // Tile configuration: BM x BN outputs per work-group of WM x WN waves; PF =
 // how many K steps ahead the global loads run (PF register sets).  M subtiles of 32 rows are interleaved over the
 // wave rows (wave wm owns subtiles wm, wm + WM, ...) so that a partially
@@ -147,39 +262,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   int lt = xcd * chunk + blockIdx.x / nx;
   if (lt >= lt_end) return;
 
-  struct TileI {
-    int64_t m0, b_off;
-    int rows, nt, ks, kbeg, nk;
-  };
   const int nk_all = p.K / BKE;
-  auto decode = [&](int l) {
-    TileI t;
-    t.ks = 0;
-    t.b_off = 0;
-    if (GROUPED) {
-      const int j = l / p.tiles_n;
-      t.nt = l % p.tiles_n;
-      const int4 e = p.tiles[j];
-      t.m0 = e.y;
-      t.rows = e.z - e.y;
-      t.b_off = (int64_t)e.x * p.b_group_stride;
-    } else {
-      constexpr int GM = 8;  // M tiles per group: consecutive tiles walk down a group, then across
-      const int per_split = p.tiles_m * p.tiles_n;
-      t.ks = l / per_split;
-      const int lm = l % per_split;
-      const int span = GM * p.tiles_n;
-      const int g = lm / span, first = g * GM;
-      const int gsz = min(p.tiles_m - first, GM);
-      const int mt = first + (lm % span) % gsz;
-      t.nt = (lm % span) / gsz;
-      t.m0 = (int64_t)mt * BM;
-      t.rows = min(BM, p.M - (int)t.m0);
-    }
-    t.kbeg = t.ks * p.ksteps;
-    t.nk = (p.splits > 1) ? min(p.ksteps, nk_all - t.kbeg) : nk_all;
-    return t;
-  };
+  auto decode = [&](int l) { return decode_tile<BM, GROUPED>(p, l, nk_all); };
 
   // ---- per-thread source rows of the tile being loaded (32-bit row indices;
   // addresses are formed per K step).  Rows past the valid range are clamped
@@ -423,81 +507,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       for (; kt < nk; kt += NSET) steps(IC<1>{}, kt);
     }
 
-    // ---- epilogue.  The MFMA takes the B fragment as its first operand, so
-    // acc[a][b] is the (B subtile b) x (A subtile a) block: lane l owns A row l32
-    // of subtile a and, in registers 4g .. 4g+3, the four consecutive B columns
-    // 8g + 4 * half .. +3 of subtile b, which leave in one vector store.
-    {
-      const int rows_valid = cur.rows;
-      const int64_t m0 = cur.m0;
-      const int nt = cur.nt;
-      TO *C = (TO *)p.C;
-      const bool vec = (p.ldc % 4) == 0;
-#pragma unroll
-      for (int a = 0; a < TM; ++a) {
-        const int rl = (a * WM + wm) * 32 + l32;
-        if (rl >= rows_valid) continue;
-        const int64_t grow = m0 + rl;
-        const float rs = (EPI == EPI_ROWSCALE) ? p.row_scale[grow] : 1.0f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          if (EPI == EPI_GLU) {
-#pragma unroll
-            for (int b = 0; b < TN; b += 2) {
-              const int64_t h0 = (int64_t)nt * (BN / 2) + wn * (WTN / 2) + (b / 2) * 32 + g * 8 + half * 4;
-              float o[4];
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                o[c] = situf_(acc[a][b][4 * g + c], p.beta1) * softcapf_(acc[a][b + 1][4 * g + c], p.beta2);
-              TO *dst = C + grow * p.ldc + h0;
-              if (vec && h0 + 3 < p.N / 2) {
-                store4(dst, o);
-              } else {
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                  if (h0 + c < p.N / 2) dst[c] = from_f32<TO>(o[c]);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int b = 0; b < TN; ++b) {
-              const int64_t c0 = (int64_t)nt * BN + wn * WTN + b * 32 + g * 8 + half * 4;
-              float o[4];
-#pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                float v = acc[a][b][4 * g + c];
-                if (EPI == EPI_SIGMOID) {
-                  if (p.col_bias) v += p.col_bias[min(c0 + c, (int64_t)p.N - 1)];
-                  v = sigmoidf_(v);
-                } else if (EPI == EPI_ROWSCALE) {
-                  v *= rs;
-                }
-                o[c] = v;
-              }
-              if (EPI == EPI_PARTIAL) {
-                float *dst = (float *)p.C + ((int64_t)cur.ks * p.M + grow) * p.ldc + c0;
-                if (vec && c0 + 3 < p.N) {
-                  store4(dst, o);
-                } else {
-#pragma unroll
-                  for (int c = 0; c < 4; ++c)
-                    if (c0 + c < p.N) dst[c] = o[c];
-                }
-              } else {
-                TO *dst = C + grow * p.ldc + c0;
-                if (vec && c0 + 3 < p.N) {
-                  store4(dst, o);
-                } else {
-#pragma unroll
-                  for (int c = 0; c < 4; ++c)
-                    if (c0 + c < p.N) dst[c] = from_f32<TO>(o[c]);
-                }
-              }
-            }
-          }
-        }
-      }
-    }
+    // ---- epilogue
+    store_tile<TO, EPI, BN, WTN, WM, TM, TN>(p, acc, cur.m0, cur.rows, cur.nt, cur.ks, wm, wn, half, l32);
 
     if (!has_next) break;
     lt = lt_next;
