@@ -37,14 +37,14 @@ def parse():
     return ap.parse_args()
 
 
-def routed_w12_bytes(cfg, counts):
-    """Algorithmic HBM bytes of the routed W1/W2 + SiTU-GLU kernel for one launch:
-    each touched expert's W1 and W2 once, each dispatched latent row once, each
-    gated hidden row written once."""
+def experts_w12_bytes(cfg, counts):
+    """Algorithmic HBM bytes of the W1/W2 + SiTU-GLU grouped GEMM (routed and shared experts)
+    for one launch: each touched routed expert's and each shared expert's W1 and W2 once, each
+    expert row's latent input once, each gated hidden row written once."""
     es = 2 if cfg.dtype == "bf16" else 4
     touched = int((counts > 0).sum())
-    rows = int(counts.sum())
-    return touched * 2 * cfg.D * cfg.L * es + rows * (cfg.L + cfg.D) * es, touched
+    rows = int(counts.sum()) + cfg.n_shared * cfg.T
+    return (touched + cfg.n_shared) * 2 * cfg.D * cfg.L * es + rows * (cfg.L + cfg.D) * es, touched
 
 
 def qb_protocol(w, dev, lmoe, synth):
@@ -171,12 +171,12 @@ def main():
     # HBM traffic of the routed W1/W2 launch from the committed rocprofv3 counter summary, if it was
     # taken on these exact kernel sources and this workload
     from sparse_moe_layer_down_amd import profsum
-    tb, sha = profsum.read_counters(os.path.join(ROOT, "profiles", f"routed_w12_{cfg.name.lower()}_hbm_counters.md"))
+    tb, sha = profsum.read_counters(os.path.join(ROOT, "profiles", f"experts_w12_{cfg.name.lower()}_hbm_counters.md"))
     traffic = tb if (tb is not None and sha == profsum.source_sha256()) else None
     flops = cfg.flops_per_token() * cfg.T
     tflops = flops / (ms * 1e-3) / 1e12
-    w12_bytes, touched = routed_w12_bytes(cfg, counts)
-    w12_ms = float(stage_ms[lmoe.STAGES.index("routed_w12")])
+    w12_bytes, touched = experts_w12_bytes(cfg, counts)
+    w12_ms = float(stage_ms[lmoe.STAGES.index("experts_w12")])
     achieved = w12_bytes / (w12_ms * 1e-3) / 1e9
 
     out = {
@@ -198,7 +198,7 @@ def main():
         "tflops": tflops,
         "mfma_peak_frac": tflops / PEAK_BF16_TFLOPS,
         "stage_ms": {name: float(v) for name, v in zip(lmoe.STAGES, stage_ms)},
-        "roofline": {"kernel": "routed experts W1/W2 + SiTU-GLU grouped GEMM", "bound": "hbm",
+        "roofline": {"kernel": "expert W1/W2 + SiTU-GLU grouped GEMM (routed + shared)", "bound": "hbm",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic, "algorithmic_bytes": w12_bytes, "experts_touched": touched,
                      "avg_ms": w12_ms},

@@ -108,11 +108,15 @@ typedef enum {
   LMOE_WS_Z = 0,         /* [T, L] work dtype: latent z = x w_down^T                    */
   LMOE_WS_COUNTS = 1,    /* [n] int32: tokens routed to each expert                      */
   LMOE_WS_OFFS = 2,      /* [n+1] int32: exclusive prefix sum of counts                  */
-  LMOE_WS_ROW_TOKEN = 3, /* [T*k] int32: token of each dispatched row, rows ordered by
-                                   (expert, token)                                        */
+  LMOE_WS_ROW_TOKEN = 3, /* [T*(k+n_shared)] int32: token of each expert row.  Rows 0 ..
+                                   T*k-1 are the dispatched (token, expert) pairs ordered
+                                   by (expert, token); row T*k + s*T + t is token t of
+                                   shared expert s                                        */
   LMOE_WS_ROW_SLOT = 4,  /* [T*k] int32: dispatched row of (token t, slot r) at t*k+r      */
-  LMOE_WS_HIDDEN = 5,    /* [T*k, D] work dtype: gated hidden a of each dispatched row     */
-  LMOE_WS_U = 6,         /* [T, L] fp32: shared-expert part of the aggregated latent u    */
+  LMOE_WS_HIDDEN = 5,    /* [T*(k+n_shared), D] work dtype: gated hidden a of each row     */
+  LMOE_WS_ROWS = 6,      /* [T*(k+n_shared), L] staged expert outputs: routed rows scaled
+                                   by g, shared rows by 1; fp16 for bf16 work dtype, fp32
+                                   for fp32                                               */
   LMOE_WS_V = 7          /* [T, L] work dtype: v = RMSNorm(u)                             */
 } lmoe_ws_region;
 
@@ -148,12 +152,12 @@ int lmoe_forward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const 
                  size_t workspace_bytes, void *stream);
 
 /* Stages of lmoe_forward, in launch order (for lmoe_forward_timed). */
-#define LMOE_N_STAGES 10
-/*  0 down-projection GEMM            5 routed experts' W1/W2 + SiTU-GLU (grouped)
- *  1 router GEMM + sigmoid           6 shared experts' W3 (fp32 shared part of u)
- *  2 top-k + routing weights         7 routed experts' W3 scaled by g (grouped)
- *  3 dispatch permutation (3 kernels) 8 combine + RMSNorm
- *  4 shared experts' W1/W2 + SiTU-GLU 9 up-projection GEMM                      */
+#define LMOE_N_STAGES 8
+/*  0 down-projection GEMM             4 W1/W2 + SiTU-GLU of every expert row
+ *  1 router GEMM + sigmoid              (routed and shared, one grouped GEMM)
+ *  2 top-k + routing weights          5 W3 of every expert row, scaled (grouped)
+ *  3 dispatch permutation (3 kernels) 6 combine + RMSNorm
+ *                                     7 up-projection GEMM                      */
 
 /* lmoe_forward with per-stage timing: events is an array of n_events ==
  * LMOE_N_STAGES + 1 hipEvent_t handles created by the caller; events[i] is

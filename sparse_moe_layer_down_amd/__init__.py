@@ -49,10 +49,12 @@ def workspace_view(workspace, dims, dtype, region):
     off = int(lib().lmoe_workspace_offset(dims, code, WS_REGIONS[region]))
     if off < 0:
         raise ValueError(region)
-    T, L, n, k, D = dims.T, dims.L, dims.n, dims.k, dims.D
+    T, L, n, k, D, ns = dims.T, dims.L, dims.n, dims.k, dims.D, dims.n_shared
+    R = T * (k + ns)  # expert rows: dispatched, then each shared expert's T
+    stage_dt = torch.float16 if dtype == torch.bfloat16 else torch.float32
     shapes = {"z": ((T, L), dtype), "counts": ((n,), torch.int32), "offs": ((n + 1,), torch.int32),
-              "row_token": ((T * k,), torch.int32), "row_slot": ((T * k,), torch.int32),
-              "hidden": ((T * k, D), dtype), "u_shared": ((T, L), torch.float32), "v": ((T, L), dtype)}
+              "row_token": ((R,), torch.int32), "row_slot": ((T * k,), torch.int32),
+              "hidden": ((R, D), dtype), "rows": ((R, L), stage_dt), "v": ((T, L), dtype)}
     shape, dt = shapes[region]
     nbytes = torch.tensor([], dtype=dt).element_size()
     cnt = 1

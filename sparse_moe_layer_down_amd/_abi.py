@@ -11,15 +11,14 @@ LMOE_BF16 = 1
 STATUS = {0: "LMOE_OK", -1: "LMOE_ERR_NULL", -2: "LMOE_ERR_SHAPE", -3: "LMOE_ERR_DTYPE", -4: "LMOE_ERR_ALIGN",
           -5: "LMOE_ERR_WORKSPACE", -6: "LMOE_ERR_HIP", -7: "LMOE_ERR_VALUE"}
 
-WS_REGIONS = {"z": 0, "counts": 1, "offs": 2, "row_token": 3, "row_slot": 4, "hidden": 5, "u_shared": 6, "v": 7}
+WS_REGIONS = {"z": 0, "counts": 1, "offs": 2, "row_token": 3, "row_slot": 4, "hidden": 5, "rows": 6, "v": 7}
 
 # every function the header declares
 EXPORTS = ("lmoe_workspace_size", "lmoe_workspace_offset", "lmoe_forward", "lmoe_forward_timed",
            "lmoe_qb_update", "lmoe_qb_workspace_size", "lmoe_strerror")
 
-N_STAGES = 10
-STAGES = ("down_proj", "router", "topk", "permute", "shared_w12", "routed_w12", "shared_w3", "routed_w3",
-          "combine_norm", "up_proj")
+N_STAGES = 8
+STAGES = ("down_proj", "router", "topk", "permute", "experts_w12", "experts_w3", "combine_norm", "up_proj")
 
 
 class Dims(ctypes.Structure):

@@ -43,6 +43,9 @@ struct GemmArgs {
   const void *B2;           // GLU: W2 rows
   int64_t ldb;
   int64_t b_group_stride;   // GROUPED: elements between experts' B matrices
+  const void *Bsh;          // GROUPED: the shared experts' bank (expert ids >= n_routed), same stride
+  const void *B2sh;         //   and its second matrix (GLU: W2)
+  int n_routed;             // GROUPED: expert ids below this index B / B2
   int64_t kb_len;           // B is split along K into batches of kb_len columns,
   int64_t kb_stride;        //   batch s starts at B + s * kb_stride
   void *C;
@@ -95,27 +98,33 @@ LMOE_DEV int swz(int r, int c) { return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)
 
 template <int V> struct IC { static constexpr int value = V; };
 
-// One logical tile: rows [m0, m0 + rows) (grouped: of expert b_off / stride),
-// N tile nt, split ks covering K steps [kbeg, kbeg + nk).
+// One logical tile: rows [m0, m0 + rows) against the B matrices at B / B2
+// (grouped: one expert's), N tile nt, split ks covering K steps [kbeg, kbeg + nk).
 struct TileI {
-  int64_t m0, b_off;
+  const void *B, *B2;
+  int64_t m0;
   int rows, nt, ks, kbeg, nk;
 };
 
 // Logical tile l -> TileI.  Grouped: entry l / tiles_n of the device tile table.
 // Dense: split-major, then groups of 8 M tiles walked down before across.
-template <int BM, bool GROUPED>
+template <typename T, int BM, bool GROUPED>
 LMOE_DEV TileI decode_tile(const GemmArgs &p, int l, int nk_all) {
   TileI t;
   t.ks = 0;
-  t.b_off = 0;
+  t.B = p.B;
+  t.B2 = p.B2;
   if (GROUPED) {
     const int j = l / p.tiles_n;
     t.nt = l % p.tiles_n;
     const int4 e = p.tiles[j];
     t.m0 = e.y;
     t.rows = e.z - e.y;
-    t.b_off = (int64_t)e.x * p.b_group_stride;
+    const bool sh = e.x >= p.n_routed;  // a shared expert: rows are all tokens, weights from the shared bank
+    const int64_t off = (int64_t)(sh ? e.x - p.n_routed : e.x) * p.b_group_stride;
+    const T *b1 = (const T *)(sh ? p.Bsh : p.B), *b2 = (const T *)(sh ? p.B2sh : p.B2);
+    t.B = b1 + off;
+    t.B2 = b2 ? b2 + off : nullptr;
   } else {
     constexpr int GM = 8;
     const int per_split = p.tiles_m * p.tiles_n;
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   if (lt >= lt_end) return;
 
   const int nk_all = p.K / BKE;
-  auto decode = [&](int l) { return decode_tile<BM, GROUPED>(p, l, nk_all); };
+  auto decode = [&](int l) { return decode_tile<T, BM, GROUPED>(p, l, nk_all); };
 
   // ---- per-thread source rows of the tile being loaded (32-bit row indices;
   // addresses are formed per K step).  Rows past the valid range are clamped
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   int a_row[A_LD];
   int b_row[B_LD];  // row of B (GLU: hidden unit)
   bool b_w2[B_LD];  // GLU / split-K: row comes from B2
-  int64_t lb_off;   // expert offset of B
+  const T *lb1, *lb2;  // B (and B2) of the tile being loaded, at this thread's 16-B chunk
   int lkbeg;        // first K step
   auto rows_of = [&](const TileI &t, int (&out)[A_LD]) {
 #pragma unroll
@@ -300,12 +309,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
         b_w2[i] = false;
       }
     }
-    lb_off = t.b_off;
+    lb1 = (const T *)t.B + lchunk * EPT;
+    lb2 = ((EPI == EPI_GLU || EPI == EPI_PARTIAL) && t.B2) ? (const T *)t.B2 + lchunk * EPT : lb1;
     lkbeg = t.kbeg;
   };
   const T *const Abase = (const T *)p.A + lchunk * EPT;
-  const T *const B1base = (const T *)p.B + lchunk * EPT;
-  const T *const B2base = (EPI == EPI_GLU || EPI == EPI_PARTIAL) && p.B2 ? (const T *)p.B2 + lchunk * EPT : B1base;
 
   // register sets of staged global loads (see the pipeline below)
   u32x4 ra[NSET][A_LD], rb[NSET][B_LD];
@@ -314,14 +322,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   auto gloadB = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
     const int k0 = (lkbeg + kt) * BKE;
-    int64_t boff = lb_off + k0;
-    if (kbatch) {  // uniform; only the shared-expert W3 splits B along K
+    int64_t boff = k0;
+    if (kbatch) {  // uniform; only a K-batched B (several matrices side by side along K)
       const int s = k0 / (int)p.kb_len;
-      boff = lb_off + (int64_t)s * p.kb_stride + (k0 - s * (int)p.kb_len);
+      boff = (int64_t)s * p.kb_stride + (k0 - s * (int)p.kb_len);
     }
 #pragma unroll
     for (int i = 0; i < B_LD; ++i)
-      rb[S][i] = *(const u32x4 *)((b_w2[i] ? B2base : B1base) + (int64_t)b_row[i] * p.ldb + boff);
+      rb[S][i] = *(const u32x4 *)((b_w2[i] ? lb2 : lb1) + (int64_t)b_row[i] * p.ldb + boff);
   };
   auto gloadA = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;

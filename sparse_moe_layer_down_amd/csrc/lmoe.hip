@@ -61,12 +61,15 @@ struct WsLayout {
 };
 
 enum {
-  R_Z = 0, R_COUNTS, R_OFFS, R_ROW_TOKEN, R_SLOT_ROW, R_HIDDEN, R_USH, R_V,
-  R_SCORES, R_IDX, R_W, R_MASKS, R_CBASE, R_TILES1, R_TILES2, R_NTILES, R_ROW_W, R_HSH, R_YSTAGE, R_PART, R_COUNT_
+  R_Z = 0, R_COUNTS, R_OFFS, R_ROW_TOKEN, R_SLOT_ROW, R_HIDDEN, R_ROWS, R_V,
+  R_SCORES, R_IDX, R_W, R_MASKS, R_CBASE, R_TILES1, R_TILES2, R_NTILES, R_ROW_W, R_PART, R_COUNT_
 };
 
 // upper bound of sum_e ceil(count_e / bm) over any routing
-int64_t max_tiles(const lmoe_dims &d, int bm) { return d.n + cdiv(d.T * d.k, bm); }
+// upper bound of the table: routed tiles plus each shared expert's cdiv(T, bm)
+int64_t max_tiles(const lmoe_dims &d, int bm) { return d.n + cdiv(d.T * d.k, bm) + d.n_shared * cdiv(d.T, bm); }
+// expert rows: T*k routed (dispatch order), then T per shared expert
+int64_t expert_rows(const lmoe_dims &d) { return d.T * (d.k + d.n_shared); }
 
 bool small_experts(const lmoe_dims &d) { return d.T * d.k <= SMALL_ROWS_PER_EXPERT * d.n; }
 int w12_bm(const lmoe_dims &d) { return small_experts(d) ? CfgW12Small::BM : CfgW12::BM; }
@@ -119,10 +122,11 @@ WsLayout layout(const lmoe_dims &d, int dtype) {
   sz[R_Z] = d.T * d.L * es;
   sz[R_COUNTS] = d.n * 4;
   sz[R_OFFS] = (d.n + 1) * 4;
-  sz[R_ROW_TOKEN] = d.T * d.k * 4;
+  sz[R_ROW_TOKEN] = expert_rows(d) * 4;
   sz[R_SLOT_ROW] = d.T * d.k * 4;
-  sz[R_HIDDEN] = d.T * d.k * d.D * es;
-  sz[R_USH] = d.T * d.L * 4;
+  sz[R_HIDDEN] = expert_rows(d) * d.D * es;
+  // staged expert outputs, one row per expert row: fp16 (bf16 inputs) or fp32
+  sz[R_ROWS] = expert_rows(d) * d.L * (es == 2 ? 2 : 4);
   sz[R_V] = d.T * d.L * es;
   sz[R_SCORES] = d.T * d.n * 4;
   sz[R_IDX] = d.T * d.k * 4;
@@ -132,13 +136,9 @@ WsLayout layout(const lmoe_dims &d, int dtype) {
   sz[R_TILES1] = max_tiles(d, w12_bm(d)) * 16;
   sz[R_TILES2] = max_tiles(d, w3_bm(d)) * 16;
   sz[R_NTILES] = 8;
-  sz[R_ROW_W] = d.T * d.k * 4;
-  sz[R_HSH] = d.T * d.n_shared * d.D * es;
-  sz[R_YSTAGE] = d.T * d.k * d.L * (es == 2 ? 2 : 4);  // per-slot routed rows: fp16 (bf16 inputs) or fp32
+  sz[R_ROW_W] = expert_rows(d) * 4;
   // split-K partial sums: the dense GEMMs run one after another and share one buffer
   int64_t part = std::max(part_bytes<CfgDense>(d.T, d.L, d.d, bke), part_bytes<CfgRouter>(d.T, d.n, d.L, bke));
-  part = std::max(part, part_bytes<CfgDense>(d.T, 2 * d.n_shared * d.D, d.L, bke));
-  part = std::max(part, part_bytes<CfgDense>(d.T, d.L, d.n_shared * d.D, bke));
   part = std::max(part, part_bytes<CfgDense>(d.T, d.d, d.L, bke));
   sz[R_PART] = part;
   WsLayout w;
@@ -161,7 +161,7 @@ int check_dims(const lmoe_dims *d) {
   if (d->d % 128 || d->D % 64) return LMOE_ERR_SHAPE;
   if (d->n > 1024 || d->k > d->n || d->k > 64 || d->n_shared > 8) return LMOE_ERR_SHAPE;
   if (d->L > 8192 || d->d > 65536 || d->D > 65536) return LMOE_ERR_SHAPE;
-  if (d->T * d->k >= (int64_t)1 << 31 || d->T >= (int64_t)1 << 31) return LMOE_ERR_SHAPE;
+  if (d->T * (d->k + d->n_shared) >= (int64_t)1 << 31) return LMOE_ERR_SHAPE;
   return LMOE_OK;
 }
 
@@ -257,7 +257,6 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   int32_t *row_token = (int32_t *)(ws + Lw.off[R_ROW_TOKEN]);
   int32_t *slot_row = (int32_t *)(ws + Lw.off[R_SLOT_ROW]);
   T *hid = (T *)(ws + Lw.off[R_HIDDEN]);
-  float *ush = (float *)(ws + Lw.off[R_USH]);
   T *v = (T *)(ws + Lw.off[R_V]);
   float *s = scores ? scores : (float *)(ws + Lw.off[R_SCORES]);
   int32_t *idx = topk_idx ? topk_idx : (int32_t *)(ws + Lw.off[R_IDX]);
@@ -268,11 +267,10 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   int4 *tiles2 = (int4 *)(ws + Lw.off[R_TILES2]);
   int32_t *ntiles = (int32_t *)(ws + Lw.off[R_NTILES]);
   float *row_w = (float *)(ws + Lw.off[R_ROW_W]);
-  T *hsh = (T *)(ws + Lw.off[R_HSH]);
-  // per-slot routed outputs: fp16 for bf16 inputs (11-bit mantissa, summed in
-  // fp32 by the combine), fp32 for fp32 inputs
+  // staged expert outputs, one row per expert row: fp16 for bf16 inputs
+  // (11-bit mantissa, summed in fp32 by the combine), fp32 for fp32 inputs
   using TS = typename std::conditional<sizeof(T) == 2, f16, float>::type;
-  TS *ystage = (TS *)(ws + Lw.off[R_YSTAGE]);
+  TS *ystage = (TS *)(ws + Lw.off[R_ROWS]);
   float *part = (float *)(ws + Lw.off[R_PART]);
   const int T_ = (int)d.T, n = (int)d.n, k = (int)d.k, L = (int)d.L, D = (int)d.D, ns = (int)d.n_shared;
   hipError_t e;
@@ -306,76 +304,61 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     else hipLaunchKernelGGL(topk_kernel<16>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
     LMOE_TRY(hipGetLastError());
   }
-  // 4 permutation
+  // 4 permutation (+ the shared experts' rows and tiles)
   LMOE_MARK(3);
   {
     const int nch = (int)cdiv(d.T, PERM_CHUNK);
     hipLaunchKernelGGL(perm_mask_kernel, dim3(nch), dim3(PERM_CHUNK), (size_t)n * 32, st, idx, T_, n, k, masks, cbase);
     LMOE_TRY(hipGetLastError());
-    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cbase, nch, n, counts, offs, w12_bm(d), tiles1,
-                       w3_bm(d), tiles2, ntiles);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cbase, nch, n, T_, k, ns, counts, offs, w12_bm(d),
+                       tiles1, w3_bm(d), tiles2, ntiles);
     LMOE_TRY(hipGetLastError());
-    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch), dim3(PERM_CHUNK), 0, st, idx, gw, T_, n, k, masks, cbase,
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch), dim3(PERM_CHUNK), 0, st, idx, gw, T_, n, k, ns, masks, cbase,
                        row_token, row_w, slot_row);
     LMOE_TRY(hipGetLastError());
   }
-  // 5 shared experts' gated hidden: [T, ns*D]
+  // 5 gated hidden of every expert row: routed experts on their dispatched rows,
+  // shared experts (ids n ..) on all tokens, one grouped launch
   LMOE_MARK(4);
-  if (ns > 0) {
-    GemmArgs a = gargs();
-    a.A = z; a.lda = L; a.B = w.ws1; a.B2 = w.ws2; a.ldb = L; a.C = hsh; a.ldc = (int64_t)ns * D;
-    a.M = T_; a.N = 2 * ns * D; a.K = L; a.beta1 = w.beta1; a.beta2 = w.beta2;
-    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_GLU>(a, part, st)));
-  }
-  // 6 routed experts' gated hidden: [T*k, D] in dispatched order
-  LMOE_MARK(5);
   {
     GemmArgs a = gargs();
     a.A = z; a.lda = L; a.a_rows = row_token; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
+    a.Bsh = w.ws1; a.B2sh = w.ws2; a.n_routed = n;
     a.b_group_stride = (int64_t)D * L; a.C = hid; a.ldc = D;
     a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, w12_bm(d));
     a.beta1 = w.beta1; a.beta2 = w.beta2;
     if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_GLU, true, true>(a, st)));
     else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU, true, true>(a, st)));
   }
-  // 7 shared W3 (the shared experts summed through one K = ns*D contraction)
-  LMOE_MARK(6);
-  if (ns > 0) {
-    GemmArgs a = gargs();
-    a.A = hsh; a.lda = (int64_t)ns * D; a.B = w.ws3; a.ldb = D; a.kb_len = D; a.kb_stride = (int64_t)L * D;
-    a.C = ush; a.ldc = L; a.M = T_; a.N = L; a.K = ns * D;
-    LMOE_TRY((launch_dense<CfgDense, T, float, EPI_STORE>(a, part, st)));
-  }
-  // 8 routed W3, scaled by g, one row per dispatched (token, slot)
-  LMOE_MARK(7);
+  // 6 W3 of every expert row, scaled by its weight (g, or 1 for shared rows)
+  LMOE_MARK(5);
   {
     GemmArgs a = gargs();
-    a.A = hid; a.lda = D; a.B = w.w3; a.ldb = D; a.b_group_stride = (int64_t)L * D;
+    a.A = hid; a.lda = D; a.B = w.w3; a.Bsh = w.ws3; a.n_routed = n; a.ldb = D; a.b_group_stride = (int64_t)L * D;
     a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles2; a.ntiles = ntiles + 1;
     a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w;
     if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, TS, EPI_ROWSCALE, false, true>(a, st)));
     else LMOE_TRY((launch_gemm<CfgW3, T, TS, EPI_ROWSCALE, false, true>(a, st)));
   }
-  // 9 combine + RMSNorm
-  LMOE_MARK(8);
+  // 7 combine + RMSNorm
+  LMOE_MARK(6);
   {
     const int nch8 = L / 8;
-    const float *us = ns > 0 ? ush : nullptr;
     const T *gain = (const T *)w.rms_gain;
-    if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 1>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
-    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 2>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
-    else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 4>), dim3(T_), dim3(256), 0, st, us, ystage, slot_row, gain, v, L, k, w.rms_eps);
+    if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 1>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
+    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 2>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
+    else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 4>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
     LMOE_TRY(hipGetLastError());
   }
-  // 10 y = v W_up^T
-  LMOE_MARK(9);
+  // 8 y = v W_up^T
+  LMOE_MARK(7);
   {
     GemmArgs a = gargs();
     a.A = v; a.lda = L; a.B = w.w_up; a.ldb = L; a.C = y; a.ldc = d.d;
     a.M = T_; a.N = (int)d.d; a.K = L;
     LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
   }
-  LMOE_MARK(10);
+  LMOE_MARK(8);
 #undef LMOE_MARK
 #undef LMOE_TRY
   return hipSuccess;

@@ -1,7 +1,7 @@
-// Combine + RMSNorm: the aggregated latent of token t is the shared-expert part
-// (fp32, written by the shared W3 GEMM) plus the k routed rows of t (staged by
-// the W3 epilogue already scaled by their routing weights: fp16 for bf16
-// inputs, fp32 for fp32 inputs), summed in fp32.  The single
+// Combine + RMSNorm: the aggregated latent of token t is the sum, in fp32, of
+// its k routed rows (staged by the W3 epilogue already scaled by their routing
+// weights) and its n_shared shared-expert rows (rows T*k + s*T + t), all staged
+// in fp16 for bf16 inputs and fp32 for fp32 inputs.  The single
 // retained RMSNorm then gives v = gain * u / sqrt(mean(u^2) + eps)
 // ("Kimi K3 Architecture Deep Dive" §2: one RMS norm before the
 // up-projection; LeiPhone report "Keeping the numbers in range": after
@@ -13,11 +13,10 @@
 namespace lmoe {
 
 template <typename T, typename TS, int CPT>
-__global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float *__restrict__ ushared,
-                                                              const TS *__restrict__ ystage,
+__global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS *__restrict__ ystage,
                                                               const int32_t *__restrict__ slot_row,
                                                               const T *__restrict__ gain, T *__restrict__ v,
-                                                              int L, int k, float eps) {
+                                                              int T_, int L, int k, int n_shared, float eps) {
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const int nch = L / 8;
@@ -29,7 +28,13 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float *__res
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[q][i] = 0.0f;
     if (ch < nch) {
-      if (ushared) load8_f32(ushared + t * L + ch * 8, u[q]);
+      for (int sh = 0; sh < n_shared; ++sh) {
+        const int64_t row = (int64_t)T_ * k + (int64_t)sh * T_ + t;
+        float y[8];
+        load8_f32(ystage + row * L + ch * 8, y);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[q][i] += y[i];
+      }
       for (int r = 0; r < k; ++r) {
         const int64_t row = slot_row[t * k + r];
         float y[8];

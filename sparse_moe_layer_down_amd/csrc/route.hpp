@@ -119,12 +119,20 @@ __global__ __launch_bounds__(256) void perm_mask_kernel(const int32_t *__restric
 
 // Single work-group: per-(chunk, expert) bases, expert counts/offsets, and two
 // grouped-GEMM tile tables (M-tile heights bm1 and bm2): entry j of a table is
-// {expert, first row, end row} of one M tile; ntiles[0], ntiles[1] = lengths.
+// {expert, first row, end row} of one M tile.  The n_shared shared experts are
+// appended as experts n .. n + n_shared - 1 whose rows are all T tokens (rows
+// T*k + s*T .. + T, see perm_scatter_kernel); their tiles are interleaved
+// evenly among the routed ones so that every contiguous range of the table
+// (one XCD's share) gets the same mix.  ntiles[0], ntiles[1] = table lengths.
+LMOE_DEV int interleave_pos(int i, bool shared, int nr, int ns, int q) {
+  if (!shared) return i + min(i / q, ns);
+  return (i + 1) * q <= nr ? (i + 1) * q + i : nr + i;
+}
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ cbase /* in: counts, out: bases */,
-                                                         int nchunks, int n, int32_t *__restrict__ counts,
-                                                         int32_t *__restrict__ offs, int bm1, int4 *__restrict__ tiles1,
-                                                         int bm2, int4 *__restrict__ tiles2,
-                                                         int32_t *__restrict__ ntiles) {
+                                                         int nchunks, int n, int T, int k, int n_shared,
+                                                         int32_t *__restrict__ counts, int32_t *__restrict__ offs,
+                                                         int bm1, int4 *__restrict__ tiles1, int bm2,
+                                                         int4 *__restrict__ tiles2, int32_t *__restrict__ ntiles) {
   __shared__ int32_t s_tot[1024];
   __shared__ int32_t s_t1[1024];
   __shared__ int32_t s_t2[1024];
@@ -154,31 +162,46 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ c
     s_t2[e] += c;
     __syncthreads();
   }
+  const int R = T * k;  // routed rows; shared expert s owns rows R + s*T .. R + (s+1)*T
+  const int nr1 = s_t1[1023], nr2 = s_t2[1023];
+  const int mt1 = (T + bm1 - 1) / bm1, mt2 = (T + bm2 - 1) / bm2;
+  const int ns1 = n_shared * mt1, ns2 = n_shared * mt2;
+  const int q1 = ns1 > 0 ? max(1, nr1 / ns1) : 1, q2 = ns2 > 0 ? max(1, nr2 / ns2) : 1;
   if (e < n) {
     const int off = s_tot[e] - tot;
     counts[e] = tot;
     offs[e] = off;
     if (e == n - 1) {
       offs[n] = s_tot[e];
-      ntiles[0] = s_t1[e];
-      ntiles[1] = s_t2[e];
+      ntiles[0] = nr1 + ns1;
+      ntiles[1] = nr2 + ns2;
     }
     for (int c = 0; c < nchunks; ++c) cbase[(int64_t)c * n + e] += off;
     const int s1 = s_t1[e] - t1, s2 = s_t2[e] - t2;
     for (int j = 0; j < t1; ++j) {
       const int r0 = off + j * bm1;
-      tiles1[s1 + j] = make_int4(e, r0, min(r0 + bm1, off + tot), 0);
+      tiles1[interleave_pos(s1 + j, false, nr1, ns1, q1)] = make_int4(e, r0, min(r0 + bm1, off + tot), 0);
     }
     for (int j = 0; j < t2; ++j) {
       const int r0 = off + j * bm2;
-      tiles2[s2 + j] = make_int4(e, r0, min(r0 + bm2, off + tot), 0);
+      tiles2[interleave_pos(s2 + j, false, nr2, ns2, q2)] = make_int4(e, r0, min(r0 + bm2, off + tot), 0);
     }
+  }
+  for (int j = e; j < ns1; j += blockDim.x) {
+    const int sh = j / mt1, r0 = R + sh * T + (j % mt1) * bm1;
+    tiles1[interleave_pos(j, true, nr1, ns1, q1)] = make_int4(n + sh, r0, min(r0 + bm1, R + (sh + 1) * T), 0);
+  }
+  for (int j = e; j < ns2; j += blockDim.x) {
+    const int sh = j / mt2, r0 = R + sh * T + (j % mt2) * bm2;
+    tiles2[interleave_pos(j, true, nr2, ns2, q2)] = make_int4(n + sh, r0, min(r0 + bm2, R + (sh + 1) * T), 0);
   }
 }
 
+// Scatter (token, slot) to its dispatched row; also the shared experts' rows:
+// row T*k + s*T + t is token t with weight 1 for shared expert s.
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__restrict__ idx,
                                                            const float *__restrict__ w, int T, int n, int k,
-                                                           const uint64_t *__restrict__ masks,
+                                                           int n_shared, const uint64_t *__restrict__ masks,
                                                            const int32_t *__restrict__ cbase,
                                                            int32_t *__restrict__ row_token,
                                                            float *__restrict__ row_w,
@@ -187,6 +210,11 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
   const int tl = threadIdx.x;
   const int t = c * PERM_CHUNK + tl;
   if (t >= T) return;
+  for (int sh = 0; sh < n_shared; ++sh) {
+    const int64_t r = (int64_t)T * k + (int64_t)sh * T + t;
+    row_token[r] = t;
+    row_w[r] = 1.0f;
+  }
   const int wsel = tl >> 6;
   const uint64_t below = (1ull << (tl & 63)) - 1ull;
   for (int r = 0; r < k; ++r) {

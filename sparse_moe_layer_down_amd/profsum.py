@@ -8,7 +8,7 @@ The counters summary records, for every kernel of the forward, the mean
 FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as the counters read), the same
 counters for the 1 GiB device copy that `bench.py --copy-calibration` runs, the
 calibration factors they give, and a SHA-256 of the library's kernel sources.
-`bench.py` reports the routed W1/W2 kernel's traffic from this file only while
+`bench.py` reports the expert W1/W2 kernel's traffic from this file only while
 that hash matches the sources it runs.
 """
 import csv
@@ -52,11 +52,9 @@ def label(name):
 
 
 def stage(lab, name):
-    rules = [("SiTU-GLU out=bf16 gather=1 grouped=1", "routed W1/W2 + SiTU-GLU"),
-             ("rowscale", "routed W3 x routing weight"),
+    rules = [("SiTU-GLU out=bf16 gather=1 grouped=1", "expert W1/W2 + SiTU-GLU"),
+             ("rowscale", "expert W3 x row weight"),
              ("epi=sigmoid", "router scores"),
-             ("SiTU-GLU out=bf16 gather=0", "shared W1/W2 + SiTU-GLU"),
-             ("store out=fp32 gather=0 grouped=0", "shared W3"),
              ("store out=bf16 gather=0 grouped=0", "W_down / W_up"),
              ("split-K", "split-K partial sums"),
              ("splitk_finalize", "split-K finalize"),
@@ -120,24 +118,24 @@ def counters(fetch_dir, write_dir, out, cmd):
                 continue
             w = write.get(k, 0.0)
             gb = (fetch[k] * ff + w * wf) * 1024 / 1e9
-            key = "routed_w12: " if st == "routed W1/W2 + SiTU-GLU" else ""
+            key = "experts_w12: " if st == "expert W1/W2 + SiTU-GLU" else ""
             f.write(f"| `{lab}` | {key}{st} | {nf[k]} | {fetch[k]:.0f} | {w:.0f} | {gb:.3f} |\n")
-        rw = [k for k in fetch if stage(label(k), k) == "routed W1/W2 + SiTU-GLU"]
+        rw = [k for k in fetch if stage(label(k), k) == "expert W1/W2 + SiTU-GLU"]
         if rw:
             k = rw[0]
             tb = (fetch[k] * ff + write.get(k, 0.0) * wf) * 1024
-            f.write(f"\nrouted_w12_traffic_bytes: {tb:.0f}\n")
+            f.write(f"\nexperts_w12_traffic_bytes: {tb:.0f}\n")
 
 
 def read_counters(path):
-    """(traffic bytes of the routed W1/W2 launch, recorded source hash) or (None, None)."""
+    """(traffic bytes of the expert W1/W2 launch, recorded source hash) or (None, None)."""
     if not os.path.exists(path):
         return None, None
     sha, tb = None, None
     for line in open(path):
         if line.startswith("source_sha256:"):
             sha = line.split(":", 1)[1].strip()
-        elif line.startswith("routed_w12_traffic_bytes:"):
+        elif line.startswith("experts_w12_traffic_bytes:"):
             tb = float(line.split(":", 1)[1])
     return tb, sha
 

@@ -93,9 +93,12 @@ def check_against_oracle(cfg, gpu, x_host, P, rows=None):
 
 def check_dispatch(cfg, gpu):
     counts, offs, row_token, row_slot = ref.dispatch(gpu["idx"], cfg.n)
+    T = gpu["idx"].shape[0]
     assert np.array_equal(gpu["counts"], counts)
     assert np.array_equal(gpu["offs"], offs)
-    assert np.array_equal(gpu["row_token"], row_token)
+    assert np.array_equal(gpu["row_token"][:T * cfg.k], row_token)
+    # the shared experts' rows follow: row T*k + s*T + t is token t
+    assert np.array_equal(gpu["row_token"][T * cfg.k:], np.tile(np.arange(T), cfg.n_shared))
     # row_slot region holds the dispatched row of each (token, slot)
     inv = np.empty_like(row_token)
     inv[row_token * cfg.k + row_slot] = np.arange(row_token.size)
@@ -121,6 +124,12 @@ def check_hidden(cfg, gpu, P, x_host):
         a = ref.expert_hidden(z[toks], P.w1(e), P.w2(e), cfg.beta1, cfg.beta2, "f64")
         rms = np.sqrt(np.mean(a ** 2))
         assert np.all(np.abs(gpu["hidden"][lo:hi] - a) <= rel * np.abs(a) + floor * rms), f"expert {e}"
+    T = z.shape[0]
+    for j in range(cfg.n_shared):  # shared expert j: rows T*k + j*T .. + T, one per token
+        a = ref.expert_hidden(z, P.ws1(j), P.ws2(j), cfg.beta1, cfg.beta2, "f64")
+        rms = np.sqrt(np.mean(a ** 2))
+        got = gpu["hidden"][T * cfg.k + j * T:T * cfg.k + (j + 1) * T]
+        assert np.all(np.abs(got - a) <= rel * np.abs(a) + floor * rms), f"shared expert {j}"
     assert np.all(np.abs(gpu["hidden"]) <= cfg.beta1 * cfg.beta2)
 
 
