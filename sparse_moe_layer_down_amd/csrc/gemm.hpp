@@ -148,10 +148,78 @@ LMOE_DEV TileI decode_tile(const GemmArgs &p, int l, int nk_all) {
 // A row l32 of subtile a (tile row (a * WM + wm) * 32 + l32) and, in registers
 // 4g .. 4g+3, the four consecutive B columns 8g + 4 * half .. +3 of subtile b,
 // which leave in one vector store.
+// Epilogue staging through LDS for 16-bit outputs: each lane's 4-column pieces
+// cover only 8 bytes of a line per store, so a wave's slice of 32 rows (64
+// output columns, or 32 hidden units for SiTU-GLU) is first written to a
+// wave-private 4 KB LDS area (rows of 128 bytes, 16-byte chunks XOR-swizzled by
+// row) and read back as whole rows, which leave as 16-byte stores covering full
+// lines.
+template <typename TO, int EPI, int WTN, int TN>
+struct StagedStore {
+  static constexpr bool value = (EPI == EPI_ROWSCALE || EPI == EPI_STORE || EPI == EPI_GLU) &&
+                                sizeof(TO) == 2 && WTN == 64 && TN == 2;
+};
+constexpr int STAGE_BYTES_PER_WAVE = 32 * 128;
+
 template <typename TO, int EPI, int BN, int WTN, int WM, int TM, int TN>
 LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, int rows_valid, int nt, int ks,
-                         int wm, int wn, int half, int l32) {
+                         int wm, int wn, int half, int l32, unsigned char *stage) {
   TO *C = (TO *)p.C;
+  if constexpr (StagedStore<TO, EPI, WTN, TN>::value) {
+    constexpr bool GLU = EPI == EPI_GLU;
+    constexpr int CPR = GLU ? 4 : 8;  // 16-byte chunks per staged row (32 or 64 outputs)
+    const int lane = half * 32 + l32;
+    const int nout = GLU ? p.N / 2 : p.N;
+    const int64_t c_base = GLU ? (int64_t)nt * (BN / 2) + wn * (WTN / 2) : (int64_t)nt * BN + wn * WTN;
+    const bool full = (p.ldc % 8) == 0 && c_base + CPR * 8 <= nout;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int r0 = (a * WM + wm) * 32;  // first tile row of this subtile
+      if (r0 >= rows_valid) continue;     // wave-uniform
+      const float rs = (EPI == EPI_ROWSCALE) ? p.row_scale[m0 + min(r0 + l32, rows_valid - 1)] : 1.0f;
+      if (full) {
+        // write: lane (half, l32) owns row l32, outputs (chunk j) * 8 + half*4 .. +3
+#pragma unroll
+        for (int j = 0; j < CPR; ++j) {
+          const int b = j / 4, g = j % 4;
+          float o[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (GLU)
+              o[c] = situf_(acc[a][0][4 * g + c], p.beta1) * softcapf_(acc[a][1][4 * g + c], p.beta2);
+            else
+              o[c] = acc[a][b][4 * g + c] * rs;
+          }
+          store4((TO *)(stage + l32 * 128 + ((j ^ (l32 & 7)) << 4) + half * 8), o);
+        }
+        // read back whole rows: CPR lanes per row
+        constexpr int RPI = 64 / CPR;  // rows per pass
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int r = lane / CPR + RPI * i, c = lane % CPR;
+          const u32x4 v = *(const u32x4 *)(stage + r * 128 + ((c ^ (r & 7)) << 4));
+          if (r0 + r < rows_valid) *(u32x4 *)(C + (m0 + r0 + r) * p.ldc + c_base + c * 8) = v;
+        }
+        continue;
+      }
+      // partial column range: per-element stores
+      const int rl = r0 + l32;
+      if (rl >= rows_valid) continue;
+#pragma unroll
+      for (int j = 0; j < CPR; ++j) {
+        const int b = j / 4, g = j % 4;
+        const int64_t c0 = c_base + j * 8 + half * 4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (c0 + c >= nout) continue;
+          const float v = GLU ? situf_(acc[a][0][4 * g + c], p.beta1) * softcapf_(acc[a][1][4 * g + c], p.beta2)
+                              : acc[a][b][4 * g + c] * rs;
+          C[(m0 + rl) * p.ldc + c0 + c] = from_f32<TO>(v);
+        }
+      }
+    }
+    return;
+  }
   const bool vec = (p.ldc % 4) == 0;
 #pragma unroll
   for (int a = 0; a < TM; ++a) {
@@ -244,6 +312,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char *const sA0 = smem;
   unsigned char *const sB0 = smem + 2 * BM * 128;
+  // wave-private epilogue staging area (only for the staged-store epilogue)
+  unsigned char *const sE = smem + 2 * (BM + BN) * 128 + (threadIdx.x >> 6) * STAGE_BYTES_PER_WAVE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform by construction; readfirstlane lets the compiler keep it (and
@@ -516,7 +586,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     }
 
     // ---- epilogue
-    store_tile<TO, EPI, BN, WTN, WM, TM, TN>(p, acc, cur.m0, cur.rows, cur.nt, cur.ks, wm, wn, half, l32);
+    store_tile<TO, EPI, BN, WTN, WM, TM, TN>(p, acc, cur.m0, cur.rows, cur.nt, cur.ks, wm, wn, half, l32, sE);
 
     if (!has_next) break;
     lt = lt_next;

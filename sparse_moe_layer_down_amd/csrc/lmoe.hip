@@ -182,8 +182,9 @@ int device_cus() {
 // CU), each walking its share of the logical tiles.
 template <typename C, typename T, typename TO, int EPI, bool GATHER, bool GROUPED>
 hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
-  constexpr int lds = 2 * (C::BM + C::BN) * 128;
   constexpr int threads = 64 * C::WM * C::WN;
+  constexpr bool staged = StagedStore<TO, EPI, C::BN / C::WN, C::BN / C::WN / 32>::value;
+  constexpr int lds = 2 * (C::BM + C::BN) * 128 + (staged ? (threads / 64) * STAGE_BYTES_PER_WAVE : 0);
   auto kern = gemm_kernel<T, TO, C::BM, C::BN, C::WM, C::WN, C::PF, EPI, GATHER, GROUPED>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
