@@ -3,7 +3,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "liblmoe.so")
+# LMOE_LIBRARY may name another build of the same library (e.g. to compare two builds)
+LIB_PATH = os.environ.get("LMOE_LIBRARY") or os.path.join(HERE, "liblmoe.so")
 
 LMOE_F32 = 0
 LMOE_BF16 = 1
