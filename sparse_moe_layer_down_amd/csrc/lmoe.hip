@@ -46,6 +46,7 @@ using CfgRouter = Cfg<128, 128, 2, 2, 1>;  // N = n is narrow: smaller tiles kee
 using CfgMid = Cfg<128, 128, 2, 2, 1>;     // dense GEMMs whose 256 x 256 tiles would not fill the GPU
 using CfgSkinny = Cfg<64, 256, 1, 4, 2>;   // dense GEMMs with M <= 64 (decode), always split-K
 using CfgW12 = Cfg<192, 256, 2, 4, 2>;
+using CfgUp = Cfg<192, 256, 2, 4, 2>;      // W_up (N = d): 192-row tiles divide its tile rounds better
 using CfgW3 = Cfg<192, 256, 2, 4, 2>;
 // experts with few rows each (decode): 32-row tiles
 using CfgW12Small = Cfg<32, 256, 1, 4, 2>;
@@ -139,7 +140,7 @@ WsLayout layout(const lmoe_dims &d, int dtype) {
   sz[R_ROW_W] = expert_rows(d) * 4;
   // split-K partial sums: the dense GEMMs run one after another and share one buffer
   int64_t part = std::max(part_bytes<CfgDense>(d.T, d.L, d.d, bke), part_bytes<CfgRouter>(d.T, d.n, d.L, bke));
-  part = std::max(part, part_bytes<CfgDense>(d.T, d.d, d.L, bke));
+  part = std::max(part, part_bytes<CfgUp>(d.T, d.d, d.L, bke));
   sz[R_PART] = part;
   WsLayout w;
   int64_t o = 0;
@@ -357,7 +358,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     GemmArgs a = gargs();
     a.A = v; a.lda = L; a.B = w.w_up; a.ldb = L; a.C = y; a.ldc = d.d;
     a.M = T_; a.N = (int)d.d; a.K = L;
-    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
+    LMOE_TRY((launch_dense<CfgUp, T, T, EPI_STORE>(a, part, st)));
   }
   LMOE_MARK(8);
 #undef LMOE_MARK

@@ -20,28 +20,42 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS *__restri
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const int nch = L / 8;
+  const int nrows = k + n_shared;
   float u[CPT][8];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[q][i] = 0.0f;
+  // rows four at a time so their loads are in flight together: the k routed
+  // rows of t (through slot_row), then its shared-expert rows
+  for (int r0 = 0; r0 < nrows; r0 += 4) {
+    int64_t row[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = min(r0 + j, nrows - 1);
+      row[j] = r < k ? (int64_t)slot_row[t * k + r] : (int64_t)T_ * k + (int64_t)(r - k) * T_ + t;
+    }
+    float y[4][CPT][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < CPT; ++q) {
+        const int ch = min((int)threadIdx.x + q * 256, nch - 1);
+        load8_f32(ystage + row[j] * L + ch * 8, y[j][q]);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (r0 + j >= nrows) break;
+#pragma unroll
+      for (int q = 0; q < CPT; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[q][i] += y[j][q][i];
+    }
+  }
   float ss = 0.0f;
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
-    const int ch = threadIdx.x + q * 256;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) u[q][i] = 0.0f;
-    if (ch < nch) {
-      for (int sh = 0; sh < n_shared; ++sh) {
-        const int64_t row = (int64_t)T_ * k + (int64_t)sh * T_ + t;
-        float y[8];
-        load8_f32(ystage + row * L + ch * 8, y);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) u[q][i] += y[i];
-      }
-      for (int r = 0; r < k; ++r) {
-        const int64_t row = slot_row[t * k + r];
-        float y[8];
-        load8_f32(ystage + row * L + ch * 8, y);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) u[q][i] += y[i];
-      }
+    if ((int)threadIdx.x + q * 256 < nch) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) ss += u[q][i] * u[q][i];
     }

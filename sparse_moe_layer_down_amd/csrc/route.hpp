@@ -31,15 +31,36 @@ LMOE_DEV uint32_t ord_f32(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// 64-bit value of another lane of the same 16-lane row, by DPP pattern CTRL
+template <int CTRL>
+LMOE_DEV uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the wavefront, returned wave-uniform: DPP within each row of 16
+// lanes (swap neighbours, swap pairs, mirror halves, mirror the row), then the
+// four row maxima through scalar lane reads.
 LMOE_DEV uint64_t wave_max_u64(uint64_t v) {
+  uint64_t w;
+  w = dpp_u64<0xB1>(v);  // quad_perm [1,0,3,2]
+  v = w > v ? w : v;
+  w = dpp_u64<0x4E>(v);  // quad_perm [2,3,0,1]
+  v = w > v ? w : v;
+  w = dpp_u64<0x141>(v);  // row_half_mirror
+  v = w > v ? w : v;
+  w = dpp_u64<0x140>(v);  // row_mirror
+  v = w > v ? w : v;
+  uint64_t r = 0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * q);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * q);
+    const uint64_t x = ((uint64_t)hi << 32) | lo;
+    r = x > r ? x : r;
   }
-  return v;
+  return r;
 }
 
 template <int MAXJ>
@@ -217,16 +238,36 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
   }
   const int wsel = tl >> 6;
   const uint64_t below = (1ull << (tl & 63)) - 1ull;
-  for (int r = 0; r < k; ++r) {
-    const int64_t f = (int64_t)t * k + r;
-    const int e = idx[f];
-    const uint64_t *m = masks + ((int64_t)c * n + e) * 4;
-    int rank = __popcll(m[wsel] & below);
-    for (int q = 0; q < wsel; ++q) rank += __popcll(m[q]);
-    const int pos = cbase[(int64_t)c * n + e] + rank;
-    row_token[pos] = t;
-    row_w[pos] = w[f];
-    slot_row[f] = pos;
+  // four slots at a time, so their dependent loads (expert -> mask words, base) overlap
+  for (int r0 = 0; r0 < k; r0 += 4) {
+    int e[4], base[4];
+    uint64_t mw[4][4];
+    float wv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = min(r0 + u, k - 1);
+      e[u] = idx[(int64_t)t * k + r];
+      wv[u] = w[(int64_t)t * k + r];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t *m = masks + ((int64_t)c * n + e[u]) * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mw[u][q] = m[q];
+      base[u] = cbase[(int64_t)c * n + e[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (r0 + u >= k) break;
+      const uint64_t mine = wsel == 0 ? mw[u][0] : wsel == 1 ? mw[u][1] : wsel == 2 ? mw[u][2] : mw[u][3];
+      const int rank = __popcll(mine & below) + (wsel > 0 ? __popcll(mw[u][0]) : 0) +
+                       (wsel > 1 ? __popcll(mw[u][1]) : 0) + (wsel > 2 ? __popcll(mw[u][2]) : 0);
+      const int pos = base[u] + rank;
+      const int64_t f = (int64_t)t * k + r0 + u;
+      row_token[pos] = t;
+      row_w[pos] = wv[u];
+      slot_row[f] = pos;
+    }
   }
 }
 
