@@ -37,9 +37,9 @@ def source_sha256():
 
 def label(name):
     """Readable name for a kernel symbol (mangled or demangled)."""
-    m = re.search(r"gemm_kernelI(DF16b|f)(DF16b|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELi(\d)ELi(\d)ELb(\d)ELb(\d)E", name)
+    m = re.search(r"gemm_kernelI(DF16b|f)(DF16b|DF16_|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELi(\d)ELi(\d)ELb(\d)ELb(\d)E", name)
     if m:
-        out = "fp32" if m.group(2) == "f" else "bf16"
+        out = {"f": "fp32", "DF16b": "bf16", "DF16_": "fp16"}[m.group(2)]
         return (f"gemm {m.group(3)}x{m.group(4)} waves {m.group(5)}x{m.group(6)} pf{m.group(7)} "
                 f"epi={EPI[int(m.group(8))]} out={out} gather={m.group(9)} grouped={m.group(10)}")
     m = re.search(r"gemm_kernel<[^,]*, (\d+), (\d+), (\d), (\d), (\d), (\d), (\w+), (\w+)>", name)
