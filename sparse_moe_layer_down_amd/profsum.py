@@ -1,8 +1,8 @@
 """Turn rocprofv3 CSV output of `bench.py` into the short text summaries kept
 under profiles/.
 
-  python -m sparse_moe_layer_down_amd.profsum trace  <kernel_stats.csv> <out.md> "<command>"
-  python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <out.md> "<commands>"
+  python -m sparse_moe_layer_down_amd.profsum trace  <kernel_stats.csv> <out.md> "<command>" ["<title>"]
+  python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <out.md> "<commands>" ["<title>"]
 
 The counters summary records, for every kernel of the forward, the mean
 FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as the counters read), the same
@@ -61,6 +61,9 @@ def stage(lab, name):
              ("combine", "combine + RMSNorm"),
              ("topk", "top-k + routing weights"),
              ("perm_", "permutation"),
+             ("qb_hist", "QB histogram"),
+             ("qb_pool", "QB pooled histogram"),
+             ("qb_solve", "QB bias solve"),
              ("synth", "input synthesis (outside the timed region)")]
     for key, st in rules:
         if key in lab or key in name:
@@ -68,10 +71,13 @@ def stage(lab, name):
     return ""
 
 
-def trace(stats_csv, out, cmd):
+PREFILL = "K3-shaped prefill forward (T=8192, d=7168, 896 experts choose 16), bf16"
+
+
+def trace(stats_csv, out, cmd, title=PREFILL):
     rows = list(csv.DictReader(open(stats_csv)))
     with open(out, "w") as f:
-        f.write("# Kernel trace: K3-shaped prefill forward (T=8192, d=7168, 896 experts choose 16), bf16\n\n")
+        f.write(f"# Kernel trace: {title}\n\n")
         f.write(f"Kernel-source SHA-256: `{source_sha256()}`\n\n")
         f.write(f"Command (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
         f.write("| kernel | stage | calls | avg (us) | min (us) | max (us) | share |\n|---|---|---|---|---|---|---|\n")
@@ -90,7 +96,7 @@ def _means(d, counter):
     return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
 
 
-def counters(fetch_dir, write_dir, out, cmd):
+def counters(fetch_dir, write_dir, out, cmd, title=PREFILL):
     fetch, nf = _means(fetch_dir, "FETCH_SIZE")
     write, _ = _means(write_dir, "WRITE_SIZE")
     copy = [k for k in fetch if "copyBuffer" in k]
@@ -102,7 +108,7 @@ def counters(fetch_dir, write_dir, out, cmd):
     ff = COPY_BYTES / (cf * 1024.0)
     wf = COPY_BYTES / (cw * 1024.0)
     with open(out, "w") as f:
-        f.write("# HBM counters per dispatch: K3-shaped prefill forward (T=8192, d=7168, 896 experts choose 16), bf16\n\n")
+        f.write(f"# HBM counters per dispatch: {title}\n\n")
         f.write(f"source_sha256: {source_sha256()}\n")
         f.write(f"fetch_factor: {ff:.4f}\nwrite_factor: {wf:.4f}\n\n")
         f.write("FETCH_SIZE and WRITE_SIZE are in KiB per dispatch as rocprofv3 reports them. The factors scale them to "
@@ -142,9 +148,9 @@ def read_counters(path):
 
 if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "trace":
-        trace(sys.argv[2], sys.argv[3], sys.argv[4])
+        trace(*sys.argv[2:6])
     elif len(sys.argv) >= 6 and sys.argv[1] == "counters":
-        counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+        counters(*sys.argv[2:7])
     else:
         print(__doc__)
         sys.exit(2)
