@@ -173,7 +173,7 @@ int lmoe_forward_timed(const lmoe_dims *dims, const lmoe_weights *w, int dtype, 
  * [RB] "Keeping the numbers in range": each expert's threshold is moved to
  * where it receives its target share).
  *   scores [T, n] fp32    unbiased router scores (as written by lmoe_forward);
- *                         1 <= n <= 2^20, 1 <= k <= n
+ *                         0 <= T < 2^31, 1 <= n <= 2^20, 1 <= k <= n
  *   nbins                 B, 1..16384 (1000 by default on the pages)
  *   hist [n, nbins] int32 per-expert histogram, in/out.  With accumulate == 0 it
  *                         is overwritten by this batch's counts; with

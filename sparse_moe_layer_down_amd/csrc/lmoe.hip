@@ -438,7 +438,7 @@ size_t lmoe_qb_workspace_size(int32_t nbins) {
 int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
                    int accumulate, float *bias, int solve, void *workspace, size_t workspace_bytes,
                    void *stream) {
-  if (T < 0 || n < 1 || n > ((int64_t)1 << 20) || k < 1 || k > n) return LMOE_ERR_SHAPE;
+  if (T < 0 || T >= ((int64_t)1 << 31) || n < 1 || n > ((int64_t)1 << 20) || k < 1 || k > n) return LMOE_ERR_SHAPE;
   if (nbins < 1 || nbins > 16384) return LMOE_ERR_VALUE;
   if (!hist || (T > 0 && !scores) || (solve && (!bias || !workspace))) return LMOE_ERR_NULL;
   if (!aligned16(hist) || (scores && !aligned16(scores)) || (bias && !aligned16(bias)) ||
