@@ -3,6 +3,7 @@ under profiles/.
 
   python -m sparse_moe_layer_down_amd.profsum trace  <kernel_stats.csv> <out.md> "<command>" ["<title>"]
   python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <out.md> "<commands>" ["<title>"]
+  python -m sparse_moe_layer_down_amd.profsum mfma <pmc_dir> <out.md> "<command>" ["<title>"]
 
 The counters summary records, for every kernel of the forward, the mean
 FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as the counters read), the same
@@ -133,6 +134,30 @@ def counters(fetch_dir, write_dir, out, cmd, title=PREFILL):
             f.write(f"\nexperts_w12_traffic_bytes: {tb:.0f}\n")
 
 
+def mfma(pmc_dir, out, cmd, title=PREFILL, cus=256, simds=4, xcds=8):
+    """MFMA utilisation per kernel from SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs),
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (units of 512 flops) and GRBM_GUI_ACTIVE (GPU clocks,
+    summed over the XCDs)."""
+    busy, _ = _means(pmc_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    mops, n = _means(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    gui, _ = _means(pmc_dir, "GRBM_GUI_ACTIVE")
+    with open(out, "w") as f:
+        f.write(f"# MFMA utilisation per dispatch: {title}\n\n")
+        f.write("busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs x %d CUs x %d SIMDs): the share of "
+                "SIMD cycles with the matrix core busy while the kernel ran. bf16 MFMA flops = "
+                "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, including MFMAs on padding rows.\n\n" % (xcds, cus, simds))
+        f.write(f"Command (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
+        f.write("| kernel | stage | dispatches | GPU clocks | MFMA busy | bf16 MFMA GFLOP |\n|---|---|---|---|---|---|\n")
+        for k in sorted(busy, key=lambda k: -busy[k]):
+            if busy[k] <= 0:
+                continue
+            lab = label(k)
+            clocks = gui.get(k, 0.0) / xcds
+            frac = busy[k] / (clocks * cus * simds) if clocks else 0.0
+            f.write(f"| `{lab}` | {stage(lab, k)} | {n.get(k, 0)} | {clocks:.0f} | {100 * frac:.1f}% | "
+                    f"{mops.get(k, 0.0) * 512 / 1e9:.1f} |\n")
+
+
 def read_counters(path):
     """(traffic bytes of the expert W1/W2 launch, recorded source hash) or (None, None)."""
     if not os.path.exists(path):
@@ -151,6 +176,8 @@ if __name__ == "__main__":
         trace(*sys.argv[2:6])
     elif len(sys.argv) >= 6 and sys.argv[1] == "counters":
         counters(*sys.argv[2:7])
+    elif len(sys.argv) >= 5 and sys.argv[1] == "mfma":
+        mfma(*sys.argv[2:6])
     else:
         print(__doc__)
         sys.exit(2)
