@@ -198,7 +198,14 @@ LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, i
         for (int i = 0; i < 32 / RPI; ++i) {
           const int r = lane / CPR + RPI * i, c = lane % CPR;
           const u32x4 v = *(const u32x4 *)(stage + r * 128 + ((c ^ (r & 7)) << 4));
-          if (r0 + r < rows_valid) *(u32x4 *)(C + (m0 + r0 + r) * p.ldc + c_base + c * 8) = v;
+          if (r0 + r < rows_valid) {
+            u32x4 *dst = (u32x4 *)(C + (m0 + r0 + r) * p.ldc + c_base + c * 8);
+            // staged expert rows are read once, by the combine: stream them
+            if (EPI == EPI_ROWSCALE)
+              __builtin_nontemporal_store(v, dst);
+            else
+              *dst = v;
+          }
         }
         continue;
       }
@@ -397,9 +404,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       const int s = k0 / (int)p.kb_len;
       boff = (int64_t)s * p.kb_stride + (k0 - s * (int)p.kb_len);
     }
+    // Expert weights (grouped) are streamed once per forward: non-temporal
+    // loads keep them from displacing the gathered rows and other reused data
+    // in the caches.  Dense B is re-read by every M tile and stays cached.
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      rb[S][i] = *(const u32x4 *)((b_w2[i] ? lb2 : lb1) + (int64_t)b_row[i] * p.ldb + boff);
+    for (int i = 0; i < B_LD; ++i) {
+      const u32x4 *bp = (const u32x4 *)((b_w2[i] ? lb2 : lb1) + (int64_t)b_row[i] * p.ldb + boff);
+      rb[S][i] = GROUPED ? __builtin_nontemporal_load(bp) : *bp;
+    }
   };
   auto gloadA = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;

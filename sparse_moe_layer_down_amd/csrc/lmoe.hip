@@ -347,8 +347,12 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   {
     const int nch8 = L / 8;
     const T *gain = (const T *)w.rms_gain;
-    if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 1>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
-    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 2>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
+    const dim3 wg((unsigned)cdiv(d.T, 4));
+    if (nch8 <= 64) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 1>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
+    else if (nch8 <= 128) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 2>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
+    else if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 4>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
+    else if (nch8 <= 448) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 7>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
+    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 8>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
     else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 4>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
     LMOE_TRY(hipGetLastError());
   }
