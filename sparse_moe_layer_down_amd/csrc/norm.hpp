@@ -46,12 +46,14 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_wave_kernel(const TS *__r
   for (int q = 0; q < CPT; ++q)
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[q][i] = 0.0f;
+  // the k routed row indices of t, one per lane (k <= 64), read up front
+  const int my_row = lane < k ? slot_row[t * k + lane] : 0;
   for (int r0 = 0; r0 < nrows; r0 += RIF) {
     int64_t row[RIF];
 #pragma unroll
     for (int j = 0; j < RIF; ++j) {
       const int r = min(r0 + j, nrows - 1);
-      row[j] = r < k ? (int64_t)slot_row[t * k + r] : (int64_t)T_ * k + (int64_t)(r - k) * T_ + t;
+      row[j] = r < k ? (int64_t)__builtin_amdgcn_readlane(my_row, r) : (int64_t)T_ * k + (int64_t)(r - k) * T_ + t;
     }
     float y[RIF][CPT][8];
 #pragma unroll
