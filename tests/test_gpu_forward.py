@@ -24,8 +24,15 @@ pytestmark = pytest.mark.gpu
 GAP = 1e-4
 
 
-def tol(dtype):
-    return 1e-5 if dtype == "f32" else 2e-2
+def tol(dtype, K=1024):
+    """1e-5 for fp32 (the tiny fp32 configuration), 2e-2 for bf16.  For fp32 the
+    rounding error of a K-term fp32 dot product grows like sqrt(K) * 2^-24 of the
+    terms' RMS, so shapes whose longest contraction K (= d, the W_down length)
+    exceeds 1024 get 1e-5 * sqrt(K / 1024); bf16 is dominated by the operand
+    rounding and keeps 2e-2."""
+    if dtype != "f32":
+        return 2e-2
+    return 1e-5 * max(1.0, (K / 1024.0) ** 0.5)
 
 
 def rel_err(got, want, label=None, t=None):
@@ -77,8 +84,9 @@ def check_against_oracle(cfg, gpu, x_host, P, rows=None):
     assert np.array_equal(np.sort(own["idx"][clear], 1), np.sort(g_idx[clear], 1)), "top-k sets differ"
     # expert math on the GPU's routing
     forced = ref.forward(x_host, P, cfg.k, cfg.n_shared, dt, cfg.beta1, cfg.beta2, cfg.eps, forced_idx=g_idx)
-    assert rel_err(gpu["z"][sel], forced["z_pre"], f"{cfg.name} z", tol(dt)) <= tol(dt), "z"
-    assert rel_err(gpu["s"][sel], forced["s"], f"{cfg.name} s", tol(dt)) <= tol(dt), "scores"
+    tl = tol(dt, cfg.d)
+    assert rel_err(gpu["z"][sel], forced["z_pre"], f"{cfg.name} z", tl) <= tl, "z"
+    assert rel_err(gpu["s"][sel], forced["s"], f"{cfg.name} s", tl) <= tl, "scores"
     # routing weights from the GPU's own fp32 scores, order matching the GPU's list
     g_ref = ref.routing_weights(gpu["s"][sel], g_idx)
     assert np.abs(gpu["g"][sel] - g_ref).max() <= 1e-6
@@ -86,8 +94,8 @@ def check_against_oracle(cfg, gpu, x_host, P, rows=None):
     sb = gpu["s"][sel] + P.bias()[None, :]
     srt = np.take_along_axis(sb, g_idx, 1)
     assert np.all(np.diff(srt.astype(np.float32), axis=1) <= 0)
-    assert rel_err(gpu["v"][sel], forced["v_pre"], f"{cfg.name} v", tol(dt)) <= tol(dt), "v"
-    assert rel_err(gpu["y"][sel], forced["y_pre"], f"{cfg.name} y", tol(dt)) <= tol(dt), "y"
+    assert rel_err(gpu["v"][sel], forced["v_pre"], f"{cfg.name} v", tl) <= tl, "v"
+    assert rel_err(gpu["y"][sel], forced["y_pre"], f"{cfg.name} y", tl) <= tl, "y"
     return own, forced
 
 
@@ -115,21 +123,26 @@ def check_hidden(cfg, gpu, P, x_host):
     half an ulp of an element above 10 RMS is already more than 2e-2 RMS.)
     """
     z = gpu["z"]
-    rel, floor = (2.0 ** -8, 1e-3) if cfg.dtype == "bf16" else (1e-6, 1e-5)
+    # fp32: the W1/W2 contraction has L terms, whose rounding error grows like sqrt(L)
+    rel, floor = (2.0 ** -8, 1e-3) if cfg.dtype == "bf16" else (1e-6, 1e-5 * max(1.0, (cfg.L / 1024.0) ** 0.5))
+
+    def worst(got, a):
+        rms = np.sqrt(np.mean(a ** 2))
+        return float(np.max(np.abs(got - a) / (rel * np.abs(a) + floor * rms)))
+
     for e in range(cfg.n):
         lo, hi = gpu["offs"][e], gpu["offs"][e + 1]
         if lo == hi:
             continue
         toks = gpu["row_token"][lo:hi]
         a = ref.expert_hidden(z[toks], P.w1(e), P.w2(e), cfg.beta1, cfg.beta2, "f64")
-        rms = np.sqrt(np.mean(a ** 2))
-        assert np.all(np.abs(gpu["hidden"][lo:hi] - a) <= rel * np.abs(a) + floor * rms), f"expert {e}"
+        r = worst(gpu["hidden"][lo:hi], a)
+        assert r <= 1.0, f"expert {e}: error {r:.3g} x the bound"
     T = z.shape[0]
     for j in range(cfg.n_shared):  # shared expert j: rows T*k + j*T .. + T, one per token
         a = ref.expert_hidden(z, P.ws1(j), P.ws2(j), cfg.beta1, cfg.beta2, "f64")
-        rms = np.sqrt(np.mean(a ** 2))
-        got = gpu["hidden"][T * cfg.k + j * T:T * cfg.k + (j + 1) * T]
-        assert np.all(np.abs(got - a) <= rel * np.abs(a) + floor * rms), f"shared expert {j}"
+        r = worst(gpu["hidden"][T * cfg.k + j * T:T * cfg.k + (j + 1) * T], a)
+        assert r <= 1.0, f"shared expert {j}: error {r:.3g} x the bound"
     assert np.all(np.abs(gpu["hidden"]) <= cfg.beta1 * cfg.beta2)
 
 
@@ -171,6 +184,11 @@ def test_c1_small_bf16_full_parity():
     dict(T=257, d=256, L=128, n=64, k=64, n_shared=1, D=64, dtype="f32"),       # k = n = 64: every expert
     dict(T=1, d=128, L=64, n=1, k=1, n_shared=1, D=64, dtype="f32"),            # one token, one expert
     dict(T=130, d=384, L=192, n=1024, k=3, n_shared=2, D=192, dtype="bf16"),    # largest expert count
+    # latent widths that take each combine + RMSNorm layout: 4 and 8 chunks of
+    # 8 elements per lane (one wavefront per token), then one work-group per token
+    dict(T=70, d=4096, L=2048, n=16, k=2, n_shared=1, D=64, dtype="bf16"),
+    dict(T=40, d=8192, L=4096, n=8, k=2, n_shared=1, D=64, dtype="f32"),
+    dict(T=20, d=16384, L=8192, n=8, k=2, n_shared=1, D=64, dtype="bf16"),      # widest latent accepted
 ])
 def test_ragged_and_edge_shapes(shape):
     cfg = synth.get_config("C0").with_(x_seed=21, w_seed=21, bias_std=0.05, **shape)
