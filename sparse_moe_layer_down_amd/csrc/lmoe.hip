@@ -303,6 +303,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     else if (n <= 128) hipLaunchKernelGGL(topk_kernel<2>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
     else if (n <= 256) hipLaunchKernelGGL(topk_kernel<4>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
     else if (n <= 512) hipLaunchKernelGGL(topk_kernel<8>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
+    else if (n <= 896) hipLaunchKernelGGL(topk_kernel<14>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
     else hipLaunchKernelGGL(topk_kernel<16>, dim3(blocks), dim3(256), 0, st, s, w.router_bias, T_, n, k, idx, gw);
     LMOE_TRY(hipGetLastError());
   }

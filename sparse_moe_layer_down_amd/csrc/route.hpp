@@ -158,13 +158,18 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ c
   __shared__ int32_t s_t1[1024];
   __shared__ int32_t s_t2[1024];
   const int e = threadIdx.x;
+  constexpr int CB = 16;  // chunk counts loaded together, so their latencies overlap
   int tot = 0;
   if (e < n) {
-    for (int c = 0; c < nchunks; ++c) {
-      const int64_t i = (int64_t)c * n + e;
-      const int v = cbase[i];
-      cbase[i] = tot;
-      tot += v;
+    for (int c0 = 0; c0 < nchunks; c0 += CB) {
+      int v[CB];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) v[j] = c0 + j < nchunks ? cbase[(int64_t)(c0 + j) * n + e] : 0;
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        if (c0 + j < nchunks) cbase[(int64_t)(c0 + j) * n + e] = tot;
+        tot += v[j];
+      }
     }
   }
   const int t1 = (tot + bm1 - 1) / bm1, t2 = (tot + bm2 - 1) / bm2;
@@ -197,7 +202,14 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ c
       ntiles[0] = nr1 + ns1;
       ntiles[1] = nr2 + ns2;
     }
-    for (int c = 0; c < nchunks; ++c) cbase[(int64_t)c * n + e] += off;
+    for (int c0 = 0; c0 < nchunks; c0 += CB) {
+      int v[CB];
+#pragma unroll
+      for (int j = 0; j < CB; ++j) v[j] = c0 + j < nchunks ? cbase[(int64_t)(c0 + j) * n + e] : 0;
+#pragma unroll
+      for (int j = 0; j < CB; ++j)
+        if (c0 + j < nchunks) cbase[(int64_t)(c0 + j) * n + e] = v[j] + off;
+    }
     const int s1 = s_t1[e] - t1, s2 = s_t2[e] - t2;
     for (int j = 0; j < t1; ++j) {
       const int r0 = off + j * bm1;
