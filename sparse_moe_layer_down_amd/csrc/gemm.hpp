@@ -62,6 +62,7 @@ struct GemmArgs {
   int splits;               // dense split-K: number of K ranges (1 = none)
   int ksteps;               // K steps per range
   int b_split_row;          // EPI_PARTIAL: B rows >= this come from B2
+  int32_t *sched;           // GROUPED: 8 tile counters, zero at launch (null: static tile walk)
 };
 
 template <typename T> struct Mma;
@@ -338,7 +339,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   // ---- persistent walk over the logical tiles.  Each XCD (work-groups are
   // dispatched round-robin over the 8 XCDs) takes one contiguous range of
   // logical tiles, so the tiles that share A rows (one expert's N tiles, or a
-  // group of dense M tiles) meet in that XCD's L2.
+  // group of dense M tiles) meet in that XCD's L2.  The first `per` tiles of a
+  // range go one to each of the XCD's work-groups.  Dense GEMMs then walk their
+  // range with a stride; grouped GEMMs (tiles of uneven cost) take the rest in
+  // order from a per-XCD counter, so an expert's N tiles start close together
+  // (its gathered rows are fetched into L2 once) and a work-group that finishes
+  // early takes more; once its own range is used up it takes from the other
+  // XCDs' ranges.  Thread 0 takes the tile after next at the start of a tile
+  // and publishes it through LDS after the first K step, so the next tile is
+  // always known when its loads are issued.
   const int nvalid = GROUPED ? min(*p.ntiles, p.tiles_m) * p.tiles_n : p.n_logical;
   const int nx = (gridDim.x % 8 == 0) ? 8 : 1;
   const int per = gridDim.x / nx;
@@ -347,6 +356,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   const int lt_end = min(nvalid, (xcd + 1) * chunk);
   int lt = xcd * chunk + blockIdx.x / nx;
   if (lt >= lt_end) return;
+  const bool dyn = GROUPED && p.sched != nullptr;
+  int *const qslot = (int *)(smem + 2 * (BM + BN) * 128 +
+                             (StagedStore<TO, EPI, WTN, TN>::value ? (NT / 64) * STAGE_BYTES_PER_WAVE : 0));
+  int steal = 0;  // thread 0: ranges (own XCD's first) found used up
+  auto grab = [&]() -> int {
+    while (steal < nx) {
+      const int xi = (xcd + steal) % nx;
+      const int j = xi * chunk + per + atomicAdd(&p.sched[xi], 1);
+      if (j < min(nvalid, (xi + 1) * chunk)) return j;
+      ++steal;
+    }
+    return -1;
+  };
+  int q_next = -1;  // dyn: the tile after the current one (-1: none)
+  if (GROUPED && dyn) {
+    if (tid == 0) qslot[0] = grab();
+    __syncthreads();
+    q_next = qslot[0];
+    __syncthreads();
+  }
+  int tile_par = 0;  // dyn: parity of the tile count, selects the LDS slot
 
   const int nk_all = p.K / BKE;
   auto decode = [&](int l) { return decode_tile<T, BM, GROUPED>(p, l, nk_all); };
@@ -531,8 +561,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       lrow = t_o >> 3;
       lchunk = t_o & 7;
     }
-    const int lt_next = lt + per;
-    const bool has_next = lt_next < lt_end;
+    const int lt_next = dyn ? q_next : lt + per;
+    const bool has_next = dyn ? lt_next >= 0 : lt_next < lt_end;
+    int grabbed = -1;  // thread 0: the tile after lt_next
+    if (GROUPED && dyn && tid == 0) grabbed = has_next ? grab() : -1;
     const bool xnext = xpf && has_next;
     TileI nxt = cur;
     int n_row[A_LD];
@@ -577,6 +609,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
           if (st_next) lstore(IC<(S + 1) % NSET>{}, (kt + 1) & 1);
         });
       }
+      if (GROUPED && dyn && kt == 0 && tid == 0) qslot[tile_par] = grabbed;
       __syncthreads();
     };
     // NSET consecutive steps (register set indices known at compile time)
@@ -595,6 +628,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       int kt = 0;
       for (; kt + NSET + PF <= nk; kt += NSET) steps(IC<0>{}, kt);
       for (; kt < nk; kt += NSET) steps(IC<1>{}, kt);
+    }
+
+    // published after step 0 of this tile; the slot is rewritten two tiles later,
+    // past a barrier every thread reaches only after this read
+    if (GROUPED && dyn) {
+      q_next = qslot[tile_par];
+      tile_par ^= 1;
     }
 
     // ---- epilogue

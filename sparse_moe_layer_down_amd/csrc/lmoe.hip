@@ -136,7 +136,7 @@ WsLayout layout(const lmoe_dims &d, int dtype) {
   sz[R_CBASE] = nch * d.n * 4;
   sz[R_TILES1] = max_tiles(d, w12_bm(d)) * 16;
   sz[R_TILES2] = max_tiles(d, w3_bm(d)) * 16;
-  sz[R_NTILES] = 8;
+  sz[R_NTILES] = (2 + 2 * SCHED_COUNTERS) * 4;  // two table lengths, then each grouped GEMM's tile counters
   sz[R_ROW_W] = expert_rows(d) * 4;
   // split-K partial sums: the dense GEMMs run one after another and share one buffer
   int64_t part = std::max(part_bytes<CfgDense>(d.T, d.L, d.d, bke), part_bytes<CfgRouter>(d.T, d.n, d.L, bke));
@@ -185,7 +185,9 @@ template <typename C, typename T, typename TO, int EPI, bool GATHER, bool GROUPE
 hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   constexpr int threads = 64 * C::WM * C::WN;
   constexpr bool staged = StagedStore<TO, EPI, C::BN / C::WN, C::BN / C::WN / 32>::value;
-  constexpr int lds = 2 * (C::BM + C::BN) * 128 + (staged ? (threads / 64) * STAGE_BYTES_PER_WAVE : 0);
+  // grouped GEMMs: two more ints of LDS publish the next tile taken from the counters
+  constexpr int lds = 2 * (C::BM + C::BN) * 128 + (staged ? (threads / 64) * STAGE_BYTES_PER_WAVE : 0) +
+                      (GROUPED ? 16 : 0);
   auto kern = gemm_kernel<T, TO, C::BM, C::BN, C::WM, C::WN, C::PF, EPI, GATHER, GROUPED>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -329,6 +331,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     a.Bsh = w.ws1; a.B2sh = w.ws2; a.n_routed = n;
     a.b_group_stride = (int64_t)D * L; a.C = hid; a.ldc = D;
     a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, w12_bm(d));
+    a.sched = ntiles + 2;
     a.beta1 = w.beta1; a.beta2 = w.beta2;
     if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_GLU, true, true>(a, st)));
     else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU, true, true>(a, st)));
@@ -340,6 +343,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     a.A = hid; a.lda = D; a.B = w.w3; a.Bsh = w.ws3; a.n_routed = n; a.ldb = D; a.b_group_stride = (int64_t)L * D;
     a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles2; a.ntiles = ntiles + 1;
     a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w;
+    a.sched = ntiles + 2 + SCHED_COUNTERS;
     if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, TS, EPI_ROWSCALE, false, true>(a, st)));
     else LMOE_TRY((launch_gemm<CfgW3, T, TS, EPI_ROWSCALE, false, true>(a, st)));
   }

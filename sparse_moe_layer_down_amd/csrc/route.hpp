@@ -23,6 +23,7 @@
 namespace lmoe {
 
 constexpr int PERM_CHUNK = 256;  // tokens per permutation chunk (4 mask words)
+constexpr int SCHED_COUNTERS = 8;  // tile counters per grouped GEMM launch (one per XCD)
 
 LMOE_DEV uint32_t ord_f32(float f) {
   f = f + 0.0f;  // -0 -> +0
@@ -144,7 +145,8 @@ __global__ __launch_bounds__(256) void perm_mask_kernel(const int32_t *__restric
 // appended as experts n .. n + n_shared - 1 whose rows are all T tokens (rows
 // T*k + s*T .. + T, see perm_scatter_kernel); their tiles are interleaved
 // evenly among the routed ones so that every contiguous range of the table
-// (one XCD's share) gets the same mix.  ntiles[0], ntiles[1] = table lengths.
+// (one XCD's share) gets the same mix.  ntiles[0], ntiles[1] = table lengths;
+// ntiles[2 ..] = the grouped GEMMs' tile counters, zeroed here.
 LMOE_DEV int interleave_pos(int i, bool shared, int nr, int ns, int q) {
   if (!shared) return i + min(i / q, ns);
   return (i + 1) * q <= nr ? (i + 1) * q + i : nr + i;
@@ -188,6 +190,7 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ c
     s_t2[e] += c;
     __syncthreads();
   }
+  if (e < 2 * SCHED_COUNTERS) ntiles[2 + e] = 0;  // the grouped GEMMs' tile counters start at zero
   const int R = T * k;  // routed rows; shared expert s owns rows R + s*T .. R + (s+1)*T
   const int nr1 = s_t1[1023], nr2 = s_t2[1023];
   const int mt1 = (T + bm1 - 1) / bm1, mt2 = (T + bm2 - 1) / bm2;
