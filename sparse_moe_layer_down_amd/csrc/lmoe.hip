@@ -26,7 +26,6 @@
 
 #include "../../include/lmoe.h"
 #include "gemm.hpp"
-#include "gemm_dl.hpp"
 #include "norm.hpp"
 #include "qb.hpp"
 #include "route.hpp"
@@ -216,29 +215,6 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// bf16 dense GEMMs large enough for 256 x 256 tiles run the 4-wave kernel
-// that loads its operands straight into LDS.
-constexpr bool DENSE_DL = false;  // measured slower than the 8-wave kernel (see the design notes)
-
-template <typename TO, int EPI>
-hipError_t launch_dl(GemmArgs a, hipStream_t st) {
-  constexpr int lds = 4 * (256 + 256) * 64;  // four stages of 32 K
-  auto kern = gemm_dl_kernel<TO, EPI>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  a.tiles_n = (int)cdiv(a.N, 256);
-  a.tiles_m = (int)cdiv(a.M, 256);
-  a.splits = 1;
-  a.ksteps = a.K / 32;
-  a.n_logical = a.tiles_m * a.tiles_n;
-  if (a.n_logical == 0) return hipSuccess;
-  int64_t grid = std::min<int64_t>(a.n_logical, (int64_t)device_cus());  // one 128 KB work-group per CU
-  if (grid >= 8) grid = grid / 8 * 8;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, a);
-  return hipGetLastError();
-}
-
 // Dense GEMM with the tiling chosen by dense_plan.  Split-K writes fp32
 // partials to `part`, then the finalize kernel sums them and applies the
 // epilogue.
@@ -246,10 +222,7 @@ template <typename C, typename T, typename TO, int EPI>
 hipError_t launch_dense(GemmArgs a, float *part, hipStream_t st) {
   constexpr int bke = 128 / (int)sizeof(T);
   const DensePlan pl = dense_plan<C>(a.M, a.N, a.K, bke);
-  if (pl.mode == DM_LARGE) {
-    if constexpr (DENSE_DL && std::is_same<T, bf16>::value && EPI == EPI_STORE) return launch_dl<TO, EPI>(a, st);
-    return launch_gemm<C, T, TO, EPI, false, false>(a, st);
-  }
+  if (pl.mode == DM_LARGE) return launch_gemm<C, T, TO, EPI, false, false>(a, st);
   if (pl.mode == DM_MID) return launch_gemm<CfgMid, T, TO, EPI, false, false>(a, st);
   GemmArgs b = a;
   b.C = part;
