@@ -251,3 +251,28 @@ def test_empty_batch():
     x = torch.empty((0, cfg.d), dtype=torch.float32, device=dev)
     y = lmoe.forward(x, w, cfg.k)
     assert y.shape == (0, cfg.d)
+
+
+def test_stale_workspace_counters_are_reset():
+    """The grouped GEMMs hand out tiles beyond the first round from counters that
+    live in the caller's workspace; every forward resets them, so a workspace
+    holding stale bytes gives the same result as a zeroed one.  0x40 bytes make a
+    counter that was not reset hand out no tile at all (so a regression shows as
+    missing output, never as an out-of-range tile).  Eight routed experts, 20
+    tokens and an 8192-wide latent put 288 expert W3 tiles on 256 work-groups, so
+    the counters are used, and n < 16 covers counters past the expert count."""
+    cfg = synth.get_config("C0").with_(x_seed=21, w_seed=21, bias_std=0.05, T=20, d=16384, L=8192, n=8, k=2,
+                                       n_shared=1, D=64, dtype="bf16")
+    dev = torch.device("cuda:0")
+    w = synth.device_params(cfg, device=dev)
+    x = w.pop("x")
+    dims = lmoe.dims_of(x, w, cfg.k)
+    ws0 = lmoe.make_workspace(dims, x.dtype, dev).zero_()
+    y0 = lmoe.forward(x, w, cfg.k, workspace=ws0).clone()
+    ws1 = lmoe.make_workspace(dims, x.dtype, dev).fill_(0x40)
+    y1 = lmoe.forward(x, w, cfg.k, workspace=ws1).clone()
+    y2 = lmoe.forward(x, w, cfg.k, workspace=ws1)  # the same workspace again
+    torch.cuda.synchronize()
+    assert torch.isfinite(y0.float()).all()
+    assert torch.equal(y0, y1)
+    assert torch.equal(y0, y2)
