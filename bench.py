@@ -5,7 +5,7 @@ One step = one lmoe_forward over one batch of the K3-shaped prefill workload
 expert hidden 512, bf16, every weight resident in HBM), seeded synthetic
 inputs already in device memory.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config C2] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--config C2] [--no-cpu-baseline] [--no-qb-protocol] [--no-decode]
 """
 import argparse
 import json
@@ -30,6 +30,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qb-protocol", action="store_true",
                     help="skip the 20-step Quantile Balancing run on the skewed-routing workload")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-shaped (T=64) forwards on the same weights")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel of known "
@@ -89,6 +91,54 @@ def qb_protocol(w, dev, lmoe, synth):
             "load_min_over_mean": {"step0_bias0": stats[0][1], f"step{cfg.qb_steps}": stats[cfg.qb_steps][1]},
             "qb_update_ms_median": ms,
             "qb_scores_read_GBps": cfg.T * cfg.n * 4 / (ms * 1e-3) / 1e9}
+
+
+def decode_protocol(w, dev, lmoe, synth, steps):
+    """Decode-shaped forward (K3 shapes, T=64 tokens, the prefill workload's weights, which are
+    already resident): weight-read bound.  A 512 MB buffer is written between forwards so that
+    the 256 MB MALL cannot keep the dense weights (131 MB) from one forward to the next; each
+    forward is timed alone with events on the library's stream.  Algorithmic bytes: each touched
+    routed expert's W1, W2, W3 once, the shared experts, W_down, W_up and W_router once, x and y."""
+    import numpy as np
+    import torch
+    cfg = synth.get_config("C3")
+    x = synth.params.device_x(cfg, dev)
+    dims = lmoe.dims_of(x, w, cfg.k)
+    ws = lmoe.make_workspace(dims, x.dtype, dev)
+    y = torch.empty_like(x)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def fwd():
+        lmoe.forward(x, w, cfg.k, y=y, workspace=ws, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps)
+
+    for _ in range(3):
+        flush.fill_(1)
+        fwd()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(steps):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fwd()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    counts = lmoe.workspace_view(ws, dims, x.dtype, "counts").cpu().numpy()
+    touched = int((counts > 0).sum())
+    es = 2
+    expert_bytes = 3 * cfg.D * cfg.L * es
+    dense_bytes = (2 * cfg.d * cfg.L + cfg.n * cfg.L) * es
+    nbytes = (touched + cfg.n_shared) * expert_bytes + dense_bytes + 2 * cfg.T * cfg.d * es
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del flush, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"C3: K3-shaped decode forward, T={cfg.T}, prefill weights",
+            "ms_per_forward_median": ms, "tokens_per_s": cfg.T / (ms * 1e-3), "steps": steps,
+            "experts_touched": touched, "algorithmic_bytes": nbytes, "achieved_GBps": gbs,
+            "hbm_peak_frac": gbs / PEAK_HBM_GBS,
+            "cache_state": "512 MB written between forwards (MALL and L2 hold no weights at the start)"}
 
 
 def cpu_baseline(cfg, n_tok):
@@ -203,6 +253,8 @@ def main():
                      "traffic": traffic, "algorithmic_bytes": w12_bytes, "experts_touched": touched,
                      "avg_ms": w12_ms},
     }
+    if not args.no_decode and cfg.name == "C2":
+        out["decode"] = decode_protocol(w, dev, lmoe, synth, steps=20)
     if not args.no_qb_protocol and cfg.name == "C2":
         del ws
         torch.cuda.empty_cache()
