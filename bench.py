@@ -53,44 +53,51 @@ def qb_protocol(w, dev, lmoe, synth):
     """Skewed-routing workload (K3 shapes, T=32768, Zipf(1.1) logit skew, same weights as the
     prefill workload): forward -> expert loads -> lmoe_qb_update (1000-bin histograms, bias solve
     for share k/n) -> next step's bias, for 20 steps; loads at step 0 (bias 0) and step 20
-    (bias from step 19, fresh batch).  Also times the histogram + solve launch."""
+    (bias from step 19, fresh batch).  Also times the histogram + solve launch.  The same 20 steps
+    with 10000-bin histograms are reported beside it (the pages find 1000 bins as good as 10000)."""
     import torch
     cfg = synth.get_config("C4")
     w = dict(w)
     w["router_logit_offset"] = torch.as_tensor(synth.zipf_logit_offset(cfg)).to(dev)
-    bias = torch.zeros(cfg.n, dtype=torch.float32, device=dev)
-    w["router_bias"] = bias
     x = torch.empty((cfg.T, cfg.d), dtype=torch.bfloat16, device=dev)
     dims = lmoe.dims_of(x, w, cfg.k)
     ws = lmoe.make_workspace(dims, x.dtype, dev)
     y = torch.empty_like(x)
     idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
     s = torch.empty((cfg.T, cfg.n), dtype=torch.float32, device=dev)
-    hist = torch.empty((cfg.n, cfg.nbins), dtype=torch.int32, device=dev)
-    qws = torch.empty(lmoe.qb_workspace_size(cfg.nbins), dtype=torch.uint8, device=dev)
-    stats, qb_ms = {}, []
-    for t in range(cfg.qb_steps + 1):
-        x.copy_(synth.params.device_x(cfg, dev, step=t))
-        lmoe.forward(x, w, cfg.k, y=y, topk_idx=idx, scores=s, workspace=ws, beta1=cfg.beta1, beta2=cfg.beta2,
-                     eps=cfg.eps)
-        if t in (0, cfg.qb_steps):
-            load = torch.bincount(idx.flatten().long(), minlength=cfg.n).double()
-            m = load.mean()
-            stats[t] = (float(load.max() / m), float(load.min() / m))
-        if t < cfg.qb_steps:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            lmoe.qb_update(s, cfg.k, hist, bias, accumulate=False, solve=True, workspace=qws)
-            e1.record()
-            torch.cuda.synchronize()
-            qb_ms.append(e0.elapsed_time(e1))
-    ms = float(sorted(qb_ms)[len(qb_ms) // 2])
-    return {"workload": f"C4: T={cfg.T}, K3 shapes, Zipf({cfg.zipf_s}) logit skew alpha={cfg.zipf_alpha}",
-            "steps": cfg.qb_steps, "nbins": cfg.nbins,
-            "load_max_over_mean": {"step0_bias0": stats[0][0], f"step{cfg.qb_steps}": stats[cfg.qb_steps][0]},
-            "load_min_over_mean": {"step0_bias0": stats[0][1], f"step{cfg.qb_steps}": stats[cfg.qb_steps][1]},
-            "qb_update_ms_median": ms,
-            "qb_scores_read_GBps": cfg.T * cfg.n * 4 / (ms * 1e-3) / 1e9}
+
+    def run(nbins):
+        bias = torch.zeros(cfg.n, dtype=torch.float32, device=dev)
+        w["router_bias"] = bias
+        hist = torch.empty((cfg.n, nbins), dtype=torch.int32, device=dev)
+        qws = torch.empty(lmoe.qb_workspace_size(nbins), dtype=torch.uint8, device=dev)
+        stats, qb_ms = {}, []
+        for t in range(cfg.qb_steps + 1):
+            x.copy_(synth.params.device_x(cfg, dev, step=t))
+            lmoe.forward(x, w, cfg.k, y=y, topk_idx=idx, scores=s, workspace=ws, beta1=cfg.beta1,
+                         beta2=cfg.beta2, eps=cfg.eps)
+            if t in (0, cfg.qb_steps):
+                load = torch.bincount(idx.flatten().long(), minlength=cfg.n).double()
+                m = load.mean()
+                stats[t] = (float(load.max() / m), float(load.min() / m))
+            if t < cfg.qb_steps:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                lmoe.qb_update(s, cfg.k, hist, bias, accumulate=False, solve=True, workspace=qws)
+                e1.record()
+                torch.cuda.synchronize()
+                qb_ms.append(e0.elapsed_time(e1))
+        ms = float(sorted(qb_ms)[len(qb_ms) // 2])
+        return {"load_max_over_mean": {"step0_bias0": stats[0][0], f"step{cfg.qb_steps}": stats[cfg.qb_steps][0]},
+                "load_min_over_mean": {"step0_bias0": stats[0][1], f"step{cfg.qb_steps}": stats[cfg.qb_steps][1]},
+                "qb_update_ms_median": ms}
+
+    out = {"workload": f"C4: T={cfg.T}, K3 shapes, Zipf({cfg.zipf_s}) logit skew alpha={cfg.zipf_alpha}",
+           "steps": cfg.qb_steps, "nbins": cfg.nbins}
+    out.update(run(cfg.nbins))
+    out["qb_scores_read_GBps"] = cfg.T * cfg.n * 4 / (out["qb_update_ms_median"] * 1e-3) / 1e9
+    out["bins_10000"] = run(10000)
+    return out
 
 
 def decode_protocol(w, dev, lmoe, synth, steps):
