@@ -318,7 +318,8 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, cbase, nch, n, T_, k, ns, counts, offs, w12_bm(d),
                        tiles1, w3_bm(d), tiles2, ntiles);
     LMOE_TRY(hipGetLastError());
-    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch), dim3(PERM_CHUNK), 0, st, idx, gw, T_, n, k, ns, masks, cbase,
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch, (unsigned)cdiv(k, 4)), dim3(PERM_CHUNK), 0, st, idx, gw, T_, n, k,
+                       ns, masks, cbase,
                        row_token, row_w, slot_row);
     LMOE_TRY(hipGetLastError());
   }

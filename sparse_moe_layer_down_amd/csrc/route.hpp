@@ -234,7 +234,9 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ c
 }
 
 // Scatter (token, slot) to its dispatched row; also the shared experts' rows:
-// row T*k + s*T + t is token t with weight 1 for shared expert s.
+// row T*k + s*T + t is token t with weight 1 for shared expert s.  Grid: chunks
+// x groups of four slots (the slots of a token are independent), so a few
+// chunks still spread over many work-groups.
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__restrict__ idx,
                                                            const float *__restrict__ w, int T, int n, int k,
                                                            int n_shared, const uint64_t *__restrict__ masks,
@@ -246,15 +248,19 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
   const int tl = threadIdx.x;
   const int t = c * PERM_CHUNK + tl;
   if (t >= T) return;
-  for (int sh = 0; sh < n_shared; ++sh) {
-    const int64_t r = (int64_t)T * k + (int64_t)sh * T + t;
-    row_token[r] = t;
-    row_w[r] = 1.0f;
+  if (blockIdx.y == 0) {
+    for (int sh = 0; sh < n_shared; ++sh) {
+      const int64_t r = (int64_t)T * k + (int64_t)sh * T + t;
+      row_token[r] = t;
+      row_w[r] = 1.0f;
+    }
   }
   const int wsel = tl >> 6;
   const uint64_t below = (1ull << (tl & 63)) - 1ull;
-  // four slots at a time, so their dependent loads (expert -> mask words, base) overlap
-  for (int r0 = 0; r0 < k; r0 += 4) {
+  // this work-group's four slots together, so their dependent loads (expert ->
+  // mask words, base) overlap
+  {
+    const int r0 = 4 * blockIdx.y;
     int e[4], base[4];
     uint64_t mw[4][4];
     float wv[4];
