@@ -88,20 +88,35 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ s, 
       // padding ranks below every real expert (NaN included)
       key[j] = e < n ? ((uint64_t)ord_f32(sv_[j] + bv_[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
     }
-    uint64_t best = 0;
+    // Each lane keeps its two largest remaining keys (best, second).  Keys are
+    // unique and a lane's wins come in decreasing order, so its remaining keys
+    // are exactly those below its last win: when the winner's cached second is
+    // used up it rescans for the two largest keys below the win (no key is
+    // ever cleared), which happens on a lane's second, fourth, ... win only.
+    uint64_t best = 0, second = 0;
+    auto top2_below = [&](uint64_t lim) {
+      best = 0;
+      second = 0;
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) best = key[j] > best ? key[j] : best;
+      for (int j = 0; j < MAXJ; ++j) {
+        const uint64_t v = key[j] < lim ? key[j] : 0ull;
+        const bool gt_best = v > best;
+        second = gt_best ? best : (v > second ? v : second);
+        best = gt_best ? v : best;
+      }
+    };
+    top2_below(~0ull);
     int my_e = 0;
     for (int r = 0; r < k; ++r) {
       const uint64_t g = wave_max_u64(best);
       const int e = (int)(0xFFFFFFFFu - (uint32_t)g);
       if (lane == r) my_e = e;
-      if (best == g) {  // the owning lane drops the winner and refreshes its max
-        best = 0;
-#pragma unroll
-        for (int j = 0; j < MAXJ; ++j) {
-          if (key[j] == g) key[j] = 0;
-          best = key[j] > best ? key[j] : best;
+      if (best == g) {  // the owning lane drops the winner
+        if (second != 0) {
+          best = second;
+          second = 0;
+        } else {
+          top2_below(g);
         }
       }
     }
