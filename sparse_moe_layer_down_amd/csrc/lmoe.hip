@@ -42,7 +42,7 @@ template <int BM_, int BN_, int WM_, int WN_, int PF_> struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, PF = PF_;
 };
 using CfgDense = Cfg<256, 256, 2, 4, 1>;
-using CfgRouter = Cfg<128, 128, 2, 2, 1>;  // N = n is narrow: smaller tiles keep every CU busy
+using CfgRouter = Cfg<128, 256, 2, 4, 2>;  // N = n = 896 gives 4 N tiles, 64 x 4 = 256 tiles at T = 8192
 using CfgMid = Cfg<128, 128, 2, 2, 1>;     // dense GEMMs whose 256 x 256 tiles would not fill the GPU
 using CfgSkinny = Cfg<64, 256, 1, 4, 2>;   // dense GEMMs with M <= 64 (decode), always split-K
 using CfgW12 = Cfg<192, 256, 2, 4, 2>;
