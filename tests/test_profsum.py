@@ -1,0 +1,49 @@
+"""Host logic behind the bench's roofline traffic: the profile-summary tool's
+kernel labels, the copy-calibrated scaling of the HBM byte counters, and the
+source hash that decides whether a committed counter summary still applies."""
+import csv
+
+from sparse_moe_layer_down_amd import profsum
+
+W12 = "_ZN4lmoe11gemm_kernelIDF16bDF16bLi192ELi256ELi2ELi4ELi2ELi2ELb1ELb1EEEvNS_8GemmArgsE"
+W3 = "_ZN4lmoe11gemm_kernelIDF16bDF16_Li192ELi256ELi2ELi4ELi2ELi3ELb0ELb1EEEvNS_8GemmArgsE"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def test_labels_and_stages():
+    lab = profsum.label(W12)
+    assert lab == "gemm 192x256 waves 2x4 pf2 epi=SiTU-GLU out=bf16 gather=1 grouped=1"
+    assert profsum.stage(lab, W12) == "expert W1/W2 + SiTU-GLU"
+    lab3 = profsum.label(W3)
+    assert lab3 == "gemm 192x256 waves 2x4 pf2 epi=rowscale out=fp16 gather=0 grouped=1"
+    assert profsum.stage(lab3, W3) == "expert W3 x row weight"
+    assert profsum.stage(profsum.label("void lmoe::topk_kernel<14>(...)"), "topk_kernel") == "top-k + routing weights"
+
+
+def _write_pass(d, counter, values):
+    d.mkdir()
+    with open(d / "p_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, vals in values.items():
+            for v in vals:
+                w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_counter_scaling_and_round_trip(tmp_path):
+    # a 1 GiB copy split over two dispatches reads half its bytes in FETCH_SIZE and writes all of them
+    _write_pass(tmp_path / "f", "FETCH_SIZE", {COPY: [262144, 262144], W12: [1000, 3000]})
+    _write_pass(tmp_path / "w", "WRITE_SIZE", {COPY: [524288, 524288], W12: [100, 300]})
+    out = tmp_path / "summary.md"
+    profsum.counters(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "cmd")
+    text = out.read_text()
+    assert "fetch_factor: 2.0000" in text and "write_factor: 1.0000" in text
+    tb, sha = profsum.read_counters(str(out))
+    assert tb == (2000 * 2.0 + 200 * 1.0) * 1024  # per-dispatch means, scaled, in bytes
+    assert sha == profsum.source_sha256()
+
+
+def test_missing_summary_and_stable_hash(tmp_path):
+    assert profsum.read_counters(str(tmp_path / "none.md")) == (None, None)
+    h = profsum.source_sha256()
+    assert h == profsum.source_sha256() and len(h) == 64
