@@ -14,8 +14,10 @@
  *   - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) unless
  *     stated; matrices are row-major with the PyTorch [out, in] weight layout.
  *   - The caller owns every buffer.  The library never allocates or frees
- *     memory and keeps no state between calls, so calls on different streams
- *     with different workspaces may run concurrently.
+ *     memory and keeps no state between calls (beyond launch settings it
+ *     looks up once per kernel and device, thread-safely), so calls on
+ *     different streams, devices or host threads with different workspaces
+ *     may run concurrently.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     asynchronously; no entry point synchronises with the host.
  *   - Arguments are validated before anything is enqueued; on a validation

@@ -2,7 +2,8 @@
 //
 // The host code validates every argument, carves the caller's workspace and
 // enqueues the kernels on the caller's stream.  It never allocates, never
-// synchronises with the device and keeps no state.
+// synchronises with the device and keeps no state beyond launch settings
+// looked up once per kernel and device.
 //
 // Forward launch sequence ("Kimi K3 Architecture Deep Dive" §1-§3; "Inside
 // K3"; LeiPhone report "LatentMoE: paying for a bigger pool" and "Keeping the
@@ -20,8 +21,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/lmoe.h"
@@ -167,16 +170,25 @@ int check_dims(const lmoe_dims *d) {
 }
 
 // Compute units of the current device (cached per device).
-int device_cus() {
-  static int cus[64] = {0};
+constexpr int MAX_DEVICES = 64;
+
+// Current device, or -1 if it cannot be used as a cache index.
+int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return -1;
+  return dev;
+}
+
+int device_cus() {
+  static std::atomic<int> cus[MAX_DEVICES];  // 0 until queried
+  const int dev = current_device();
+  if (dev < 0) return 256;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 // Persistent launch: one work-group per resident slot (CUs x work-groups per
@@ -189,15 +201,27 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   constexpr int lds = 2 * (C::BM + C::BN) * 128 + (staged ? (threads / 64) * STAGE_BYTES_PER_WAVE : 0) +
                       (GROUPED ? 16 : 0);
   auto kern = gemm_kernel<T, TO, C::BM, C::BN, C::WM, C::WN, C::PF, EPI, GATHER, GROUPED>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  static int occ = 0;
-  if (occ == 0) {
+  // once per device (and per kernel): raise the kernel's LDS limit and query
+  // how many of its work-groups fit on a CU
+  struct PerDevice {
+    std::once_flag once;
+    hipError_t attr = hipSuccess;
+    int occ = 1;
+  };
+  static PerDevice per_dev[MAX_DEVICES];
+  const int dev = current_device();
+  if (dev < 0) return hipErrorInvalidDevice;
+  PerDevice &pd = per_dev[dev];
+  std::call_once(pd.once, [&] {
+    pd.attr = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, lds) != hipSuccess || o <= 0) o = 1;
-    occ = o;
-  }
+    if (pd.attr == hipSuccess &&
+        (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, threads, lds) != hipSuccess || o <= 0))
+      o = 1;
+    pd.occ = std::max(o, 1);
+  });
+  if (pd.attr != hipSuccess) return pd.attr;
+  const int occ = pd.occ;
   constexpr int bke = 128 / (int)sizeof(T);
   a.tiles_n = (int)cdiv(a.N, C::BN);
   if (!GROUPED) a.tiles_m = (int)cdiv(a.M, C::BM);

@@ -276,3 +276,42 @@ def test_stale_workspace_counters_are_reset():
     assert torch.isfinite(y0.float()).all()
     assert torch.equal(y0, y1)
     assert torch.equal(y0, y2)
+
+
+def test_concurrent_calls_from_two_host_threads():
+    """Two host threads, each with its own stream and workspace, call the forward
+    at the same time (the binding releases the interpreter lock during the call,
+    and the library's once-per-device launch setup is thread-safe); every result
+    equals a sequential forward bit for bit."""
+    import threading
+    cfg = synth.get_config("C1").with_(T=512)
+    dev = torch.device("cuda:0")
+    w = synth.device_params(cfg, device=dev)
+    x = w.pop("x")
+    ref_y = lmoe.forward(x, w, cfg.k).clone()
+    torch.cuda.synchronize()
+    dims = lmoe.dims_of(x, w, cfg.k)
+    outs, errors = [], []
+
+    def worker():
+        try:
+            s = torch.cuda.Stream(device=dev)
+            ws = lmoe.make_workspace(dims, x.dtype, dev)
+            ys = [torch.empty_like(x) for _ in range(3)]
+            with torch.cuda.stream(s):
+                for y in ys:
+                    lmoe.forward(x, w, cfg.k, y=y, workspace=ws, stream=s.cuda_stream)
+            s.synchronize()
+            outs.extend(ys)
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker) for _ in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    assert len(outs) == 6
+    for y in outs:
+        assert torch.equal(y, ref_y)
