@@ -2,11 +2,13 @@
 under profiles/.
 
   python -m sparse_moe_layer_down_amd.profsum trace  <kernel_stats.csv> <out.md> "<command>" ["<title>"]
-  python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <out.md> "<commands>" ["<title>"]
+  python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <out.md> "<commands>" ["<title>"] [<kernel_stats.csv>]
   python -m sparse_moe_layer_down_amd.profsum mfma <pmc_dir> <out.md> "<command>" ["<title>"]
 
 The counters summary records, for every kernel of the forward, the mean
-FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as the counters read), the same
+FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as the counters read), with a
+kernel trace of the same workload also the achieved GB/s (scaled bytes over the
+kernel's average duration in that trace), the same
 counters for the 1 GiB device copy that `bench.py --copy-calibration` runs, the
 calibration factors they give, and a SHA-256 of the library's kernel sources.
 `bench.py` reports the expert W1/W2 kernel's traffic from this file only while
@@ -97,7 +99,15 @@ def _means(d, counter):
     return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
 
 
-def counters(fetch_dir, write_dir, out, cmd, title=PREFILL):
+def _durations(stats_csv):
+    """Average duration (s) per kernel label from a rocprofv3 kernel_stats.csv."""
+    if not stats_csv:
+        return {}
+    return {label(r["Name"]): float(r["AverageNs"]) * 1e-9 for r in csv.DictReader(open(stats_csv))}
+
+
+def counters(fetch_dir, write_dir, out, cmd, title=PREFILL, stats_csv=None):
+    dur = _durations(stats_csv)
     fetch, nf = _means(fetch_dir, "FETCH_SIZE")
     write, _ = _means(write_dir, "WRITE_SIZE")
     copy = [k for k in fetch if "copyBuffer" in k]
@@ -116,8 +126,11 @@ def counters(fetch_dir, write_dir, out, cmd, title=PREFILL):
                 f"bytes moved: a 1 GiB device-to-device copy read {cf:.0f} KiB (FETCH_SIZE) and wrote {cw:.0f} KiB "
                 "(WRITE_SIZE), summed over its dispatches.\n\n")
         f.write(f"Commands (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
-        f.write("| kernel | stage | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled traffic (GB) |\n"
-                "|---|---|---|---|---|---|\n")
+        if dur:
+            f.write("GB/s = scaled traffic over the kernel's average duration in the kernel trace of the same "
+                    "workload (a separate run of the same command without counters).\n\n")
+        f.write("| kernel | stage | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled traffic (GB) | GB/s |\n"
+                "|---|---|---|---|---|---|---|\n")
         for k in sorted(fetch, key=lambda k: -fetch[k]):
             lab = label(k)
             st = "1 GiB calibration copy" if k in copy else stage(lab, k)
@@ -126,7 +139,8 @@ def counters(fetch_dir, write_dir, out, cmd, title=PREFILL):
             w = write.get(k, 0.0)
             gb = (fetch[k] * ff + w * wf) * 1024 / 1e9
             key = "experts_w12: " if st == "expert W1/W2 + SiTU-GLU" else ""
-            f.write(f"| `{lab}` | {key}{st} | {nf[k]} | {fetch[k]:.0f} | {w:.0f} | {gb:.3f} |\n")
+            rate = f"{gb / dur[lab]:.0f}" if dur.get(lab) and k not in copy else ""
+            f.write(f"| `{lab}` | {key}{st} | {nf[k]} | {fetch[k]:.0f} | {w:.0f} | {gb:.3f} | {rate} |\n")
         rw = [k for k in fetch if stage(label(k), k) == "expert W1/W2 + SiTU-GLU"]
         if rw:
             k = rw[0]
@@ -175,7 +189,7 @@ if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "trace":
         trace(*sys.argv[2:6])
     elif len(sys.argv) >= 6 and sys.argv[1] == "counters":
-        counters(*sys.argv[2:7])
+        counters(*sys.argv[2:8])
     elif len(sys.argv) >= 5 and sys.argv[1] == "mfma":
         mfma(*sys.argv[2:6])
     else:

@@ -47,3 +47,18 @@ def test_missing_summary_and_stable_hash(tmp_path):
     assert profsum.read_counters(str(tmp_path / "none.md")) == (None, None)
     h = profsum.source_sha256()
     assert h == profsum.source_sha256() and len(h) == 64
+
+
+def test_achieved_rate_from_kernel_trace(tmp_path):
+    _write_pass(tmp_path / "f", "FETCH_SIZE", {COPY: [524288], W12: [1000]})
+    _write_pass(tmp_path / "w", "WRITE_SIZE", {COPY: [1048576], W12: [0]})
+    stats = tmp_path / "k_kernel_stats.csv"
+    with open(stats, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
+        w.writeheader()
+        w.writerow({"Name": W12, "Calls": 1, "AverageNs": 1000.0, "MinNs": 1000.0, "MaxNs": 1000.0, "Percentage": 100})
+    out = tmp_path / "summary.md"
+    profsum.counters(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "cmd", "title", str(stats))
+    row = [ln for ln in out.read_text().splitlines() if "SiTU-GLU" in ln][0]
+    gb = 1000 * 2.0 * 1024 / 1e9  # scaled bytes in GB
+    assert row.rstrip(" |").split("|")[-1].strip() == f"{gb / 1e-6:.0f}"  # over 1 us
