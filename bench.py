@@ -196,24 +196,36 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K plain forwards
+    # timed region: K forwards, each recording HIP events on the library's stream around the
+    # dominant kernel (expert W1/W2 + SiTU-GLU) only, so its roofline duration is measured in
+    # these same forwards at the cost of two event records per forward
+    w12 = lmoe.STAGES.index("experts_w12")
+
+    def w12_events():
+        ev = [None] * (lmoe.N_STAGES + 1)
+        ev[w12], ev[w12 + 1] = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        return ev
+
+    evs = [w12_events() for _ in range(args.steps)]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(evs[i])
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    w12_ms = float(np.mean([ev[w12].elapsed_time(ev[w12 + 1]) for ev in evs]))
 
-    # per-stage durations: K more forwards with HIP events recorded between stages on the same stream
+    # per-stage breakdown (reported, not used for the roofline): K more forwards with events at
+    # every stage boundary
     stage_ms = np.zeros(lmoe.N_STAGES)
     for _ in range(args.steps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(lmoe.N_STAGES + 1)]
-        step(evs)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(lmoe.N_STAGES + 1)]
+        step(ev)
         torch.cuda.synchronize()
-        stage_ms += np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(lmoe.N_STAGES)])
+        stage_ms += np.array([ev[j].elapsed_time(ev[j + 1]) for j in range(lmoe.N_STAGES)])
     stage_ms /= args.steps
 
     if args.copy_calibration:
@@ -233,7 +245,6 @@ def main():
     flops = cfg.flops_per_token() * cfg.T
     tflops = flops / (ms * 1e-3) / 1e12
     w12_bytes, touched = experts_w12_bytes(cfg, counts)
-    w12_ms = float(stage_ms[lmoe.STAGES.index("experts_w12")])
     achieved = w12_bytes / (w12_ms * 1e-3) / 1e9
 
     out = {

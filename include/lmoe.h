@@ -165,7 +165,10 @@ int lmoe_forward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const 
  * LMOE_N_STAGES + 1 hipEvent_t handles created by the caller; events[i] is
  * recorded on `stream` before stage i and events[LMOE_N_STAGES] after the last
  * one, so hipEventElapsedTime(events[i], events[i+1]) is stage i's duration.
- * Computes exactly what lmoe_forward computes (same kernels, same results). */
+ * An entry may be NULL: that boundary is not recorded (each record costs a few
+ * microseconds of stream time, so a caller timing one stage passes two).
+ * Computes exactly what lmoe_forward computes (same kernels, same results).
+ * Errors: events NULL -> LMOE_ERR_NULL; n_events wrong -> LMOE_ERR_VALUE. */
 int lmoe_forward_timed(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
                        int32_t *topk_idx, float *topk_w, float *scores, void *workspace,
                        size_t workspace_bytes, void *const *events, int n_events, void *stream);

@@ -90,10 +90,13 @@ def forward(x, weights, k, y=None, topk_idx=None, topk_w=None, scores=None, work
                                 _ptr(scores), _ptr(workspace), workspace.numel(), stream)
         check(rc, "lmoe_forward")
     else:
-        # stage_events: N_STAGES + 1 torch.cuda.Event(enable_timing=True); their hipEvent_t handles
+        # stage_events: N_STAGES + 1 entries, each a torch.cuda.Event(enable_timing=True) or None
+        # (that stage boundary is not recorded); their hipEvent_t handles
         for ev in stage_events:
-            ev.record()  # materialise the underlying hipEvent_t on this device
-        handles = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
+            if ev is not None:
+                ev.record()  # materialise the underlying hipEvent_t on this device
+        handles = (ctypes.c_void_p * len(stage_events))(*[None if ev is None else ev.cuda_event
+                                                           for ev in stage_events])
         rc = lib().lmoe_forward_timed(dims, W, _dtype_code(x.dtype), _ptr(x), _ptr(y), _ptr(topk_idx),
                                       _ptr(topk_w), _ptr(scores), _ptr(workspace), workspace.numel(), handles,
                                       len(stage_events), stream)

@@ -303,7 +303,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   const int T_ = (int)d.T, n = (int)d.n, k = (int)d.k, L = (int)d.L, D = (int)d.D, ns = (int)d.n_shared;
   hipError_t e;
 #define LMOE_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
-#define LMOE_MARK(i) do { if (ev) LMOE_TRY(hipEventRecord((hipEvent_t)ev[i], st)); } while (0)
+#define LMOE_MARK(i) do { if (ev && ev[i]) LMOE_TRY(hipEventRecord((hipEvent_t)ev[i], st)); } while (0)
 
   // 1 z = x W_down^T
   LMOE_MARK(0);
@@ -459,8 +459,6 @@ int lmoe_forward_timed(const lmoe_dims *dims, const lmoe_weights *w, int dtype, 
                        void *const *events, int n_events, void *stream) {
   if (!events) return LMOE_ERR_NULL;
   if (n_events != LMOE_N_STAGES + 1) return LMOE_ERR_VALUE;
-  for (int i = 0; i < n_events; ++i)
-    if (!events[i]) return LMOE_ERR_NULL;
   return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, workspace, workspace_bytes, stream, events);
 }
 

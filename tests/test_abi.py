@@ -91,6 +91,21 @@ def test_other_errors():
     assert lib().lmoe_forward(None, ctypes.byref(fake_weights()), 1, FAKE, FAKE, None, None, None, FAKE, 1, None) == -1
 
 
+def test_timed_forward_validation():
+    """lmoe_forward_timed: the event array itself is required and must hold
+    LMOE_N_STAGES + 1 entries; NULL entries are allowed (that boundary is not
+    recorded), so an all-NULL array reaches the forward's own validation."""
+    t = lib().lmoe_forward_timed
+    d, w = c2dims(), fake_weights()
+    arr = (ctypes.c_void_p * 9)()
+    args = (ctypes.byref(d), ctypes.byref(w), 1, FAKE, FAKE, None, None, None)
+    assert t(*args, FAKE, 1 << 40, None, 9, None) == -1            # no event array
+    assert t(*args, FAKE, 1 << 40, arr, 8, None) == -7             # wrong count
+    assert t(*args, FAKE, 1000, arr, 9, None) == -5                # NULL entries pass; workspace too small
+    assert t(ctypes.byref(c2dims(T=0)), ctypes.byref(w), 1, None, None, None, None, None, None, 0, arr, 9,
+             None) == 0                                           # empty batch, nothing recorded
+
+
 def test_empty_batch_is_a_noop():
     assert call(c2dims(T=0), fake_weights(), x=None, y=None, ws=None, wsb=0) == 0
 

@@ -344,3 +344,20 @@ def test_forward_replays_from_a_hip_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, want), f"replay {i}"
+
+
+def test_timed_forward_with_null_events_equals_forward():
+    """lmoe_forward_timed with only some stage boundaries given (the rest NULL)
+    computes what lmoe_forward computes, and the given events time their stage."""
+    cfg = synth.get_config("C1").with_(T=512)
+    dev = torch.device("cuda:0")
+    w = synth.device_params(cfg, device=dev)
+    x = w.pop("x")
+    ref_y = lmoe.forward(x, w, cfg.k).clone()
+    ev = [None] * (lmoe.N_STAGES + 1)
+    i = lmoe.STAGES.index("experts_w12")
+    ev[i], ev[i + 1] = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    y = lmoe.forward(x, w, cfg.k, stage_events=ev)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref_y)
+    assert ev[i].elapsed_time(ev[i + 1]) > 0.0
