@@ -490,10 +490,18 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
     // experts per work-group: as many B-bin LDS histograms as fit in 64 KB (max 16)
     int eg = (int)std::min<int64_t>(16, std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4)));
     const int64_t groups = cdiv(n, eg);
-    // token runs: about two work-groups per CU in total (fewer runs -> fewer global merges)
-    int64_t runs = std::max<int64_t>(1, std::min<int64_t>(cdiv(2 * device_cus(), groups), cdiv(T, 256)));
+    // token runs: every work-group merges its eg * nbins LDS bins into the global
+    // histogram with device atomics, so fewer runs mean fewer merges.  Groups of
+    // at least four experts (16-byte loads of four experts per token) are bound
+    // by those merges: about one work-group per CU.  Narrower groups (wide
+    // histograms, e.g. 10000 bins: one expert per group) walk their tokens with
+    // scalar loads and want more runs: about four work-groups per CU.  (Measured
+    // at 32768 tokens x 896 experts: 1000 bins 0.110 -> 0.096 ms, 10000 bins
+    // 0.49 -> 0.42 ms against two work-groups per CU.)
+    const int64_t target = (eg >= 4 ? 1 : 4) * (int64_t)device_cus();
+    int64_t runs = std::max<int64_t>(1, std::min<int64_t>(cdiv(target, groups), cdiv(T, 256)));
     const int64_t tpb = cdiv(T, runs);
-    runs = cdiv(T, tpb);  // <= 2 * CUs: within the grid's y limit
+    runs = cdiv(T, tpb);  // <= 4 * CUs: within the grid's y limit
     hipLaunchKernelGGL(qb_hist_kernel, dim3((unsigned)groups, (unsigned)runs), dim3(256),
                        (size_t)eg * nbins * 4, st, scores, T, ni, kb, eg, tpb, hist);
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;

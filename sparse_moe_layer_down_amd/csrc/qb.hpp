@@ -76,9 +76,21 @@ __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ 
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < ne * nbins; i += blockDim.x) {
-    const int v = h[i];
-    if (v) atomicAdd(&hist[(int64_t)(e0 + i / nbins) * nbins + (i % nbins)], v);
+  if ((nbins & 1) == 0) {
+    // two adjacent bins of one expert per 64-bit atomic: the pair is 8-byte
+    // aligned (even bin, even row length, 16-byte aligned histogram) and the low
+    // count cannot carry into the high one while both stay non-negative int32
+    for (int i = 2 * threadIdx.x; i < ne * nbins; i += 2 * blockDim.x) {
+      const uint32_t a = (uint32_t)h[i], b = (uint32_t)h[i + 1];
+      if (a | b)
+        atomicAdd((unsigned long long *)&hist[(int64_t)(e0 + i / nbins) * nbins + (i % nbins)],
+                  ((unsigned long long)b << 32) | a);
+    }
+  } else {
+    for (int i = threadIdx.x; i < ne * nbins; i += blockDim.x) {
+      const int v = h[i];
+      if (v) atomicAdd(&hist[(int64_t)(e0 + i / nbins) * nbins + (i % nbins)], v);
+    }
   }
 }
 
