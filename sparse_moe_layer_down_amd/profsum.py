@@ -4,6 +4,7 @@ under profiles/.
   python -m sparse_moe_layer_down_amd.profsum trace  <kernel_stats.csv> <out.md> "<command>" ["<title>"]
   python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <out.md> "<commands>" ["<title>"] [<kernel_stats.csv>]
   python -m sparse_moe_layer_down_amd.profsum mfma <pmc_dir> <out.md> "<command>" ["<title>"]
+  python -m sparse_moe_layer_down_amd.profsum lds <pmc_dir> <out.md> "<command>" ["<title>"]
 
 The counters summary records, for every kernel of the forward, the mean
 FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as the counters read), with a
@@ -172,6 +173,40 @@ def mfma(pmc_dir, out, cmd, title=PREFILL, cus=256, simds=4, xcds=8):
                     f"{mops.get(k, 0.0) * 512 / 1e9:.1f} |\n")
 
 
+def lds(pmc_dir, out, cmd, title=PREFILL, cus=256, xcds=8):
+    """LDS traffic per kernel: SQ_INSTS_LDS_LOAD_BANDWIDTH and _STORE_BANDWIDTH count
+    64-byte units (checked against the expert W1/W2 kernel's fragment reads, 160 KB per
+    K step and CU); bytes per clock and CU over GRBM_GUI_ACTIVE / XCDs; bank-conflict
+    cycles as a share of SQ_LDS_IDX_ACTIVE; SQ_WAIT_INST_LDS as a share of
+    SQ_WAVE_CYCLES."""
+    c = {k: _means(pmc_dir, k)[0] for k in ("SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_INSTS_LDS_STORE_BANDWIDTH",
+                                            "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS",
+                                            "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE")}
+    n = _means(pmc_dir, "GRBM_GUI_ACTIVE")[1]
+    ld, st = c["SQ_INSTS_LDS_LOAD_BANDWIDTH"], c["SQ_INSTS_LDS_STORE_BANDWIDTH"]
+    with open(out, "w") as f:
+        f.write(f"# LDS traffic per dispatch: {title}\n\n")
+        f.write("LDS read / written GB = SQ_INSTS_LDS_LOAD_BANDWIDTH / _STORE_BANDWIDTH x 64 B; B/clk/CU = both over "
+                "GRBM_GUI_ACTIVE / %d XCDs x %d CUs; bank conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; "
+                "LDS issue wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES.\n\n" % (xcds, cus))
+        f.write(f"Command (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
+        f.write("| kernel | stage | dispatches | LDS read (GB) | LDS written (GB) | B/clk/CU | bank conflicts | "
+                "LDS issue wait |\n|---|---|---|---|---|---|---|---|\n")
+        for k in sorted(ld, key=lambda k: -(ld[k] + st.get(k, 0.0))):
+            tot = ld[k] + st.get(k, 0.0)
+            if tot <= 0:
+                continue
+            lab = label(k)
+            clocks = c["GRBM_GUI_ACTIVE"].get(k, 0.0) / xcds
+            bpc = tot * 64 / (clocks * cus) if clocks else 0.0
+            act = c["SQ_LDS_IDX_ACTIVE"].get(k, 0.0)
+            bank = c["SQ_LDS_BANK_CONFLICT"].get(k, 0.0) / act if act else 0.0
+            wc = c["SQ_WAVE_CYCLES"].get(k, 0.0)
+            wait = c["SQ_WAIT_INST_LDS"].get(k, 0.0) / wc if wc else 0.0
+            f.write(f"| `{lab}` | {stage(lab, k)} | {n.get(k, 0)} | {ld[k] * 64 / 1e9:.2f} | "
+                    f"{st.get(k, 0.0) * 64 / 1e9:.2f} | {bpc:.1f} | {100 * bank:.1f}% | {100 * wait:.1f}% |\n")
+
+
 def read_counters(path):
     """(traffic bytes of the expert W1/W2 launch, recorded source hash) or (None, None)."""
     if not os.path.exists(path):
@@ -192,6 +227,8 @@ if __name__ == "__main__":
         counters(*sys.argv[2:8])
     elif len(sys.argv) >= 5 and sys.argv[1] == "mfma":
         mfma(*sys.argv[2:6])
+    elif len(sys.argv) >= 5 and sys.argv[1] == "lds":
+        lds(*sys.argv[2:6])
     else:
         print(__doc__)
         sys.exit(2)

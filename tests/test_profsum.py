@@ -62,3 +62,21 @@ def test_achieved_rate_from_kernel_trace(tmp_path):
     row = [ln for ln in out.read_text().splitlines() if "SiTU-GLU" in ln][0]
     gb = 1000 * 2.0 * 1024 / 1e9  # scaled bytes in GB
     assert row.rstrip(" |").split("|")[-1].strip() == f"{gb / 1e-6:.0f}"  # over 1 us
+
+
+def test_lds_summary(tmp_path):
+    d = tmp_path / "l"
+    d.mkdir()
+    rows = {"SQ_INSTS_LDS_LOAD_BANDWIDTH": 1000, "SQ_INSTS_LDS_STORE_BANDWIDTH": 600, "SQ_LDS_IDX_ACTIVE": 400,
+            "SQ_LDS_BANK_CONFLICT": 4, "SQ_WAIT_INST_LDS": 10, "SQ_WAVE_CYCLES": 100, "GRBM_GUI_ACTIVE": 8 * 50}
+    with open(d / "p_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for c, v in rows.items():
+            w.writerow({"Kernel_Name": W12, "Counter_Name": c, "Counter_Value": v})
+    out = tmp_path / "lds.md"
+    profsum.lds(str(d), str(out), "cmd", cus=4)
+    row = [ln for ln in out.read_text().splitlines() if "SiTU-GLU" in ln][0].split("|")
+    assert row[4].strip() == f"{1000 * 64 / 1e9:.2f}" and row[5].strip() == f"{600 * 64 / 1e9:.2f}"
+    assert row[6].strip() == f"{1600 * 64 / (50 * 4):.1f}"   # bytes per clock and CU
+    assert row[7].strip() == "1.0%" and row[8].strip() == "10.0%"
