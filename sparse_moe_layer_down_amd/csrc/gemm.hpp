@@ -299,7 +299,22 @@ LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, i
 // how many K steps ahead the global loads run (PF register sets).  M subtiles of 32 rows are interleaved over the
 // wave rows (wave wm owns subtiles wm, wm + WM, ...) so that a partially
 // filled M tile still spreads its valid rows over the waves.
-template <typename T, typename TO, int BM, int BN, int WM, int WN, int PF, int EPI, bool GATHER, bool GROUPED>
+// s_waitcnt with lgkmcnt(0), expcnt untouched and vmcnt(N), N < 64
+template <int N> LMOE_DEV void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | (7 << 4) | (N & 15));
+}
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// BDMA (grouped GEMMs): both operands go straight from global memory into LDS
+// (the gfx950 global-load-to-LDS path) instead of through registers: B through
+// a ring of three stages, two steps ahead, A through two stages, one step
+// ahead; a lane loads the 16-byte chunk of its row that the swizzle expects at
+// its LDS slot.  With no LDS stores left in the K loop, each step waits only
+// for the loads of the next one (an LDS store after such loads would make the
+// compiler wait for all of them).
+template <typename T, typename TO, int BM, int BN, int WM, int WN, int PF, int EPI, bool GATHER, bool GROUPED,
+          bool BDMA = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTN = BN / WN;
@@ -316,12 +331,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   static_assert(EPI != EPI_GLU || TN % 2 == 0, "GLU needs W1/W2 subtile pairs");
   static_assert(PF >= 1 && PF <= 4, "prefetch distance");
   static_assert(NG == 2 || NG == 4, "16-K groups per 128-byte K step");
+  static_assert(!BDMA || (GROUPED && PF == 2 && RPP == 64), "B to LDS: grouped, two-step pipeline, 8 waves");
+  constexpr int NSB = BDMA ? 3 : 2;  // LDS stages of B
+  constexpr bool STAGED = StagedStore<TO, EPI, WTN, TN>::value;
+  static_assert(!BDMA || !STAGED || (NT / 64) * STAGE_BYTES_PER_WAVE <= BN * 128, "staging fits one B stage");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char *const sA0 = smem;
   unsigned char *const sB0 = smem + 2 * BM * 128;
-  // wave-private epilogue staging area (only for the staged-store epilogue)
-  unsigned char *const sE = smem + 2 * (BM + BN) * 128 + (threadIdx.x >> 6) * STAGE_BYTES_PER_WAVE;
+  // wave-private epilogue staging area (only for the staged-store epilogue); with
+  // BDMA it lives in the B stage the tile's last step has just consumed
+  unsigned char *sE = smem + 2 * (BM + BN) * 128 + (threadIdx.x >> 6) * STAGE_BYTES_PER_WAVE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform by construction; readfirstlane lets the compiler keep it (and
@@ -335,6 +355,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   // live through the epilogue and spill).
   int half = lane >> 5, l32 = lane & 31;
   int lrow = tid >> 3, lchunk = tid & 7;
+  // BDMA: the chunk this lane loads so that its LDS slot (lane & 7 of row lrow)
+  // holds what swz() expects: slot ^ (row & 7) ^ ((row >> 3) & 1)
+  int lbc = (tid & 7) ^ ((tid >> 3) & 7) ^ ((tid >> 6) & 1);
 
   // ---- persistent walk over the logical tiles.  Each XCD (work-groups are
   // dispatched round-robin over the 8 XCDs) takes one contiguous range of
@@ -357,8 +380,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   int lt = xcd * chunk + blockIdx.x / nx;
   if (lt >= lt_end) return;
   const bool dyn = GROUPED && p.sched != nullptr;
-  int *const qslot = (int *)(smem + 2 * (BM + BN) * 128 +
-                             (StagedStore<TO, EPI, WTN, TN>::value ? (NT / 64) * STAGE_BYTES_PER_WAVE : 0));
+  int *const qslot = (int *)(smem + (BDMA ? 2 * BM * 128 + NSB * BN * 128
+                                          : 2 * (BM + BN) * 128 + (STAGED ? (NT / 64) * STAGE_BYTES_PER_WAVE : 0)));
   int steal = 0;  // thread 0: ranges (own XCD's first) found used up
   auto grab = [&]() -> int {
     while (steal < nx) {
@@ -416,11 +439,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
         b_w2[i] = false;
       }
     }
-    lb1 = (const T *)t.B + lchunk * EPT;
-    lb2 = ((EPI == EPI_GLU || EPI == EPI_PARTIAL) && t.B2) ? (const T *)t.B2 + lchunk * EPT : lb1;
+    const int bc = BDMA ? lbc : lchunk;
+    lb1 = (const T *)t.B + bc * EPT;
+    lb2 = ((EPI == EPI_GLU || EPI == EPI_PARTIAL) && t.B2) ? (const T *)t.B2 + bc * EPT : lb1;
     lkbeg = t.kbeg;
   };
   const T *const Abase = (const T *)p.A + lchunk * EPT;
+  const T *const AbaseD = (const T *)p.A + lbc * EPT;  // BDMA: this lane's swizzled chunk
 
   // register sets of staged global loads (see the pipeline below)
   u32x4 ra[NSET][A_LD], rb[NSET][B_LD];
@@ -443,6 +468,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       rb[S][i] = GROUPED ? __builtin_nontemporal_load(bp) : *bp;
     }
   };
+  // BDMA: B of tile step kt into the LDS stage of global step g; instruction i of
+  // wave w writes tile rows 8w + 64i .. +7 (1 KB), one row chunk per lane
+  auto dmaB = [&](int kt, int g) {
+    const int k0 = (lkbeg + kt) * BKE;
+    int64_t boff = k0;
+    if (kbatch) {
+      const int s = k0 / (int)p.kb_len;
+      boff = (int64_t)s * p.kb_stride + (k0 - s * (int)p.kb_len);
+    }
+    unsigned char *dst = sB0 + (g % NSB) * BN * 128 + wave * 8 * 128;
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const T *src = (b_w2[i] ? lb2 : lb1) + (int64_t)b_row[i] * p.ldb + boff;
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(dst + i * RPP * 128), 16, 0, 2 /* nt */);
+    }
+  };
+  // BDMA: A of tile step kt into the LDS stage of global step g (rows as for B)
+  auto dmaA = [&](int kt, int g) {
+    const int64_t k0 = (int64_t)(lkbeg + kt) * BKE;
+    unsigned char *dst = sA0 + (g & 1) * BM * 128 + wave * 8 * 128;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const T *src = AbaseD + (int64_t)a_row[i] * p.lda + k0;
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(dst + i * RPP * 128), 16, 0, 0);
+    }
+  };
   auto gloadA = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
     const int64_t k0 = (int64_t)(lkbeg + kt) * BKE;
@@ -463,9 +514,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
 
   // One K step from LDS buffer `buf`: the fragments of 16-K group g+1 are read
   // while the MFMAs of group g run (two fragment register sets).
-  auto compute = [&](int buf, auto &&mid) {
+  auto compute = [&](int buf, const unsigned char *sB, auto &&mid) {
     const unsigned char *sA = sA0 + buf * BM * 128;
-    const unsigned char *sB = sB0 + buf * BN * 128;
     u32x4 af[2][TM][CPL], bfg[2][TN][CPL];
     auto frags = [&](auto GC, auto SC) {
       constexpr int g = decltype(GC)::value, f = decltype(SC)::value;
@@ -527,7 +577,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   // of PF (p.xpf), the last steps of a tile already load the first steps of
   // the work-group's next tile, so those loads are in flight while the tile's
   // epilogue stores run; otherwise each tile starts with its own prologue.
+  int gbase = 0;  // BDMA: global step index of the current tile's step 0
   auto prologue = [&](int nk) {
+    if constexpr (BDMA) {
+      dmaA(0, gbase);
+      dmaB(0, gbase);
+      if (1 < nk) dmaB(1, gbase + 1);
+      wait_vm_lgkm0<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      return;
+    }
     gloadA(IC<0>{}, 0);
     gloadB(IC<0>{}, 0);
     if (PF > 1 && 1 < nk) {
@@ -560,6 +621,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       l32 = t_o & 31;
       lrow = t_o >> 3;
       lchunk = t_o & 7;
+      lbc = (t_o & 7) ^ ((t_o >> 3) & 7) ^ ((t_o >> 6) & 1);
     }
     const int lt_next = dyn ? q_next : lt + per;
     const bool has_next = dyn ? lt_next >= 0 : lt_next < lt_end;
@@ -598,14 +660,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     auto step = [&](auto SETC, auto CHECKC, int kt) {
       constexpr int S = decltype(SETC)::value;  // == kt % NSET
       constexpr bool CHECK = decltype(CHECKC)::value != 0;
+      if constexpr (BDMA) {
+        const int g = gbase + kt;
+        bool b_iss = false;
+        {  // A of step kt + 1 (or the next tile's step 0)
+          const int j = kt + 1;
+          if (!CHECK || j < nk) {
+            dmaA(j, g + 1);
+          } else if (xnext) {
+            if (j == nk) {
+#pragma unroll
+              for (int i = 0; i < A_LD; ++i) a_row[i] = n_row[i];
+            }
+            dmaA(j - nk, g + 1);
+          }
+        }
+        {  // B of step kt + 2 (or of the next tile's step kt + 2 - nk)
+          const int j = kt + 2;
+          if (!CHECK || j < nk) {
+            dmaB(j, g + 2);
+            b_iss = true;
+          } else if (xnext) {
+            if (j == nk) set_b(nxt);
+            dmaB(j - nk, g + 2);
+            b_iss = true;
+          }
+        }
+        compute(g & 1, sB0 + (g % NSB) * BN * 128, [] {});
+        if (GROUPED && dyn && kt == 0 && tid == 0) qslot[tile_par] = grabbed;
+        // A and B of step kt + 1 must be in LDS: only this step's B loads (if
+        // any) were issued after them
+        if (b_iss) wait_vm_lgkm0<B_LD>();
+        else wait_vm_lgkm0<0>();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        return;
+      }
       const bool st_next = !CHECK || kt + 1 < nk || xnext;
+      const unsigned char *sBk = sB0 + (kt & 1) * BN * 128;
       if (PF == 1) {
         loads(IC<0>{}, CHECKC, kt + 1);
-        compute(kt & 1, [] {});
+        compute(kt & 1, sBk, [] {});
         if (st_next) lstore(IC<0>{}, (kt + 1) & 1);
       } else {
         loads(IC<S>{}, CHECKC, kt + PF);
-        compute(kt & 1, [&] {
+        compute(kt & 1, sBk, [&] {
           if (st_next) lstore(IC<(S + 1) % NSET>{}, (kt + 1) & 1);
         });
       }
@@ -638,7 +738,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     }
 
     // ---- epilogue
+    if constexpr (BDMA) sE = sB0 + ((gbase + nk - 1) % NSB) * BN * 128 + (threadIdx.x >> 6) * STAGE_BYTES_PER_WAVE;
     store_tile<TO, EPI, BN, WTN, WM, TM, TN>(p, acc, cur.m0, cur.rows, cur.nt, cur.ks, wm, wn, half, l32, sE);
+    if constexpr (BDMA && STAGED) {
+      // the next tile's first step loads B into the stage used for staging
+      __builtin_amdgcn_s_waitcnt((7 << 4) | 0xF | (3 << 14));  // lgkmcnt(0) only
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    gbase += nk;
 
     if (!has_next) break;
     lt = lt_next;
