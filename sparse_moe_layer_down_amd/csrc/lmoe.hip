@@ -51,7 +51,7 @@ using CfgMid = Cfg<128, 128, 2, 2, 1>;     // dense GEMMs whose 256 x 256 tiles 
 using CfgSkinny = Cfg<64, 256, 1, 4, 2>;   // dense GEMMs with M <= 64 (decode), always split-K
 using CfgW12 = Cfg<192, 256, 2, 4, 2, true>;
 using CfgUp = Cfg<192, 256, 2, 4, 2>;      // W_up (N = d): 192-row tiles divide its tile rounds better
-using CfgW3 = Cfg<192, 256, 2, 4, 2>;
+using CfgW3 = Cfg<192, 256, 2, 4, 2, true>;
 // experts with few rows each (decode): 32-row tiles
 using CfgW12Small = Cfg<32, 256, 1, 4, 2>;
 using CfgW3Small = Cfg<32, 256, 1, 4, 2>;
