@@ -331,7 +331,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   static_assert(EPI != EPI_GLU || TN % 2 == 0, "GLU needs W1/W2 subtile pairs");
   static_assert(PF >= 1 && PF <= 4, "prefetch distance");
   static_assert(NG == 2 || NG == 4, "16-K groups per 128-byte K step");
-  static_assert(!BDMA || (GROUPED && PF == 2 && RPP == 64), "B to LDS: grouped, two-step pipeline, 8 waves");
+  static_assert(!BDMA || (PF == 2 && RPP == 64 && EPI != EPI_PARTIAL), "load to LDS: two-step pipeline, 8 waves");
   constexpr int NSB = BDMA ? 3 : 2;  // LDS stages of B
   constexpr bool STAGED = StagedStore<TO, EPI, WTN, TN>::value;
   static_assert(!BDMA || !STAGED || (NT / 64) * STAGE_BYTES_PER_WAVE <= BN * 128, "staging fits one B stage");
@@ -481,7 +481,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const T *src = (b_w2[i] ? lb2 : lb1) + (int64_t)b_row[i] * p.ldb + boff;
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(dst + i * RPP * 128), 16, 0, 2 /* nt */);
+      // expert weights are streamed once (non-temporal); dense B is re-read by other M tiles
+      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(dst + i * RPP * 128), 16, 0, GROUPED ? 2 : 0);
     }
   };
   // BDMA: A of tile step kt into the LDS stage of global step g (rows as for B)

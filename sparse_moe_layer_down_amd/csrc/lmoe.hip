@@ -45,12 +45,12 @@ template <int BM_, int BN_, int WM_, int WN_, int PF_, bool BD_ = false> struct 
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, PF = PF_;
   static constexpr bool BD = BD_;  // B straight into LDS (three stages)
 };
-using CfgDense = Cfg<256, 256, 2, 4, 1>;
+using CfgDense = Cfg<256, 256, 2, 4, 2, true>;
 using CfgRouter = Cfg<128, 256, 2, 4, 2>;  // N = n = 896 gives 4 N tiles, 64 x 4 = 256 tiles at T = 8192
 using CfgMid = Cfg<128, 128, 2, 2, 1>;     // dense GEMMs whose 256 x 256 tiles would not fill the GPU
 using CfgSkinny = Cfg<64, 256, 1, 4, 2>;   // dense GEMMs with M <= 64 (decode), always split-K
 using CfgW12 = Cfg<192, 256, 2, 4, 2, true>;
-using CfgUp = Cfg<192, 256, 2, 4, 2>;      // W_up (N = d): 192-row tiles divide its tile rounds better
+using CfgUp = Cfg<192, 256, 2, 4, 2, true>;      // W_up (N = d): 192-row tiles divide its tile rounds better
 using CfgW3 = Cfg<192, 256, 2, 4, 2, true>;
 // experts with few rows each (decode): 32-row tiles
 using CfgW12Small = Cfg<32, 256, 1, 4, 2>;
@@ -199,7 +199,7 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   constexpr int threads = 64 * C::WM * C::WN;
   constexpr bool staged = StagedStore<TO, EPI, C::BN / C::WN, C::BN / C::WN / 32>::value;
   // grouped GEMMs: two more ints of LDS publish the next tile taken from the counters
-  constexpr bool bd = C::BD && GROUPED;
+  constexpr bool bd = C::BD;
   constexpr int lds = (bd ? 2 * C::BM * 128 + 3 * C::BN * 128  // staging lives in a B stage
                           : 2 * (C::BM + C::BN) * 128 + (staged ? (threads / 64) * STAGE_BYTES_PER_WAVE : 0)) +
                       (GROUPED ? 16 : 0);
