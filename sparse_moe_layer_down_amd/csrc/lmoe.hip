@@ -46,7 +46,7 @@ template <int BM_, int BN_, int WM_, int WN_, int PF_, bool BD_ = false> struct 
   static constexpr bool BD = BD_;  // B straight into LDS (three stages)
 };
 using CfgDense = Cfg<256, 256, 2, 4, 2, true>;
-using CfgRouter = Cfg<128, 256, 2, 4, 2>;  // N = n = 896 gives 4 N tiles, 64 x 4 = 256 tiles at T = 8192
+using CfgRouter = Cfg<128, 256, 2, 4, 2, true>;  // N = n = 896 gives 4 N tiles, 64 x 4 = 256 tiles at T = 8192
 using CfgMid = Cfg<128, 128, 2, 2, 1>;     // dense GEMMs whose 256 x 256 tiles would not fill the GPU
 using CfgSkinny = Cfg<64, 256, 1, 4, 2>;   // dense GEMMs with M <= 64 (decode), always split-K
 using CfgW12 = Cfg<192, 256, 2, 4, 2, true>;
