@@ -188,7 +188,9 @@ def lds(pmc_dir, out, cmd, title=PREFILL, cus=256, xcds=8):
         f.write(f"# LDS traffic per dispatch: {title}\n\n")
         f.write("LDS read / written GB = SQ_INSTS_LDS_LOAD_BANDWIDTH / _STORE_BANDWIDTH x 64 B; B/clk/CU = both over "
                 "GRBM_GUI_ACTIVE / %d XCDs x %d CUs; bank conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; "
-                "LDS issue wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES.\n\n" % (xcds, cus))
+                "LDS issue wait = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES. Operands written by the global-load-to-LDS "
+                "instruction are not LDS instructions: they appear in neither bandwidth counter (the written column "
+                "then holds only LDS stores such as epilogue staging).\n\n" % (xcds, cus))
         f.write(f"Command (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
         f.write("| kernel | stage | dispatches | LDS read (GB) | LDS written (GB) | B/clk/CU | bank conflicts | "
                 "LDS issue wait |\n|---|---|---|---|---|---|---|---|\n")
