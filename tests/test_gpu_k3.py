@@ -87,3 +87,19 @@ def test_c4_skewed_forward_and_qb(k3_weights):
     bo = ref.qb_bins(own_s.astype(np.float32), cfg.nbins)
     bg = ref.qb_bins(s32[rows], cfg.nbins)
     assert np.array_equal(bo[~edge], bg[~edge])
+
+
+def test_odd_k_steps_on_the_load_to_lds_path():
+    """Shapes whose K-step counts are odd (latent 2112: 33 steps of 64 for W_up and
+    the expert W1/W2; D = 192: 3 steps for W3), large enough for the 192 x 256 and
+    256 x 256 load-to-LDS tiles: every tile then loads its own first steps instead
+    of prefetching them during the previous tile.  2048 rows per expert, so each
+    expert spans several M tiles."""
+    cfg = synth.get_config("C1").with_(T=8192, d=4224, L=2112, n=16, k=4, n_shared=2, D=192, x_seed=31, w_seed=31)
+    gpu = run_gpu(cfg)
+    P = synth.HostParams(cfg)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.choice(cfg.T, 10, replace=False), [0, cfg.T - 1]]))
+    sampled_check(cfg, gpu, rows, P)
+    check_dispatch(cfg, gpu)
+    assert np.isfinite(gpu["y"]).all()
