@@ -32,36 +32,37 @@ LMOE_DEV uint32_t ord_f32(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// 64-bit value of another lane of the same 16-lane row, by DPP pattern CTRL
+// Maximum over the wavefront of 32-bit values, returned wave-uniform: DPP within
+// each row of 16 lanes (swap neighbours, swap pairs, mirror halves, mirror the
+// row), then the four row maxima through scalar lane reads.
 template <int CTRL>
-LMOE_DEV uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
+LMOE_DEV uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+LMOE_DEV uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
 }
 
-// Maximum over the wavefront, returned wave-uniform: DPP within each row of 16
-// lanes (swap neighbours, swap pairs, mirror halves, mirror the row), then the
-// four row maxima through scalar lane reads.
-LMOE_DEV uint64_t wave_max_u64(uint64_t v) {
-  uint64_t w;
-  w = dpp_u64<0xB1>(v);  // quad_perm [1,0,3,2]
-  v = w > v ? w : v;
-  w = dpp_u64<0x4E>(v);  // quad_perm [2,3,0,1]
-  v = w > v ? w : v;
-  w = dpp_u64<0x141>(v);  // row_half_mirror
-  v = w > v ? w : v;
-  w = dpp_u64<0x140>(v);  // row_mirror
-  v = w > v ? w : v;
-  uint64_t r = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * q);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * q);
-    const uint64_t x = ((uint64_t)hi << 32) | lo;
-    r = x > r ? x : r;
-  }
-  return r;
+// Maximum over the wavefront of the 64-bit keys (score word << 32 | index
+// word): the maximum of the score words, then the index word of the one lane
+// holding it; only when lanes tie on the score word is the maximum of their
+// index words taken.
+LMOE_DEV uint64_t wave_max_key(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32), lo = (uint32_t)v;
+  const uint32_t mh = wave_max_u32(hi);
+  const uint64_t holders = __ballot(hi == mh);
+  uint32_t ml;
+  if (__popcll(holders) == 1)
+    ml = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((long long)holders) - 1);
+  else
+    ml = wave_max_u32(hi == mh ? lo : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 template <int MAXJ>
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ s, 
     top2_below(~0ull);
     int my_e = 0;
     for (int r = 0; r < k; ++r) {
-      const uint64_t g = wave_max_u64(best);
+      const uint64_t g = wave_max_key(best);
       const int e = (int)(0xFFFFFFFFu - (uint32_t)g);
       if (lane == r) my_e = e;
       if (best == g) {  // the owning lane drops the winner
