@@ -52,7 +52,8 @@ typedef enum {
  * g_ie * (a W3_e^T) of a token are staged in the workspace before their fp32
  * sum: in fp16 when the work dtype is bf16 (an element beyond +-65504 becomes
  * +-inf and so shows in y; the gated hidden a is bounded by beta1 * beta2, so
- * this needs a W3 row whose absolute values sum past 65504 / (beta1 * beta2)),
+ * this needs a W3 row whose absolute values sum past 65504 / (beta1 * beta2);
+ * with either cap at +inf the hidden is unbounded and no such bound holds),
  * in fp32 when it is fp32. */
 typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
 
@@ -86,7 +87,10 @@ typedef struct {
  *   rms_gain [L]         gain of the single RMSNorm ([DD] §2: kept before the
  *                        up-projection only)
  *   w_up [d, L]          up-projection
- *   beta1, beta2         SiTU and softcap caps ([DD] §1: 4 and 25; > 0)
+ *   beta1, beta2         SiTU and softcap caps ([DD] §1: 4 and 25), in
+ *                        (0, +inf]; +inf is the uncapped limit (softcap
+ *                        becomes the identity, SiTU becomes SiLU), so both at
+ *                        +inf give the SwiGLU expert the caps replace
  *   rms_eps              RMSNorm epsilon (>= 0; 1e-6 by default)            */
 typedef struct {
   const void *w_down;

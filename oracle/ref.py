@@ -82,8 +82,15 @@ def sigmoid(x):
 
 
 def softcap(x, beta):
-    """softcap(x; beta) = beta * tanh(x / beta)  ([DD] §1)."""
-    return beta * np.tanh(np.asarray(x, dtype=np.float64) / beta)
+    """softcap(x; beta) = beta * tanh(x / beta)  ([DD] §1).
+
+    READING: beta = +inf is the limit of that expression, the identity (the
+    uncapped gate; with both caps at +inf SiTU-GLU is SwiGLU).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if beta == np.inf:
+        return x.copy()
+    return beta * np.tanh(x / beta)
 
 
 def situ(x, beta):

@@ -94,7 +94,11 @@ LMOE_DEV float tanh_hw(float y) {
   const float r = a < 0.375f ? a * q : big;
   return copysignf(r, y);
 }
-LMOE_DEV float softcapf_(float x, float beta) { return beta * tanh_hw(x * (1.0f / beta)); }  // 1/beta is hoisted
+// beta = +inf takes the limit beta * tanh(x / beta) -> x (no cap): SiTU becomes
+// SiLU and SiTU-GLU becomes SwiGLU, the gate the caps are measured against.
+LMOE_DEV float softcapf_(float x, float beta) {
+  return beta == __builtin_inff() ? x : beta * tanh_hw(x * (1.0f / beta));  // 1/beta is hoisted
+}
 LMOE_DEV float situf_(float x, float beta) { return softcapf_(x, beta) * sigmoid_hw(x); }
 
 LMOE_DEV float wave_sum(float v) {

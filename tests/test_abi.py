@@ -2,6 +2,7 @@
 workspace and rejects invalid arguments before launching anything (no GPU
 needed: every call here fails validation or is a no-op)."""
 import ctypes
+import math
 import os
 import re
 
@@ -87,6 +88,8 @@ def test_other_errors():
     assert call(d, fake_weights(w3=FAKE + 8)) == -4
     assert call(d, fake_weights(), wsb=1000) == -5
     assert call(d, fake_weights(beta1=0.0)) == -7
+    assert call(d, fake_weights(beta2=-math.inf)) == -7
+    assert call(d, fake_weights(beta1=math.nan)) == -7
     assert call(d, fake_weights(rms_eps=-1.0)) == -7
     assert lib().lmoe_forward(None, ctypes.byref(fake_weights()), 1, FAKE, FAKE, None, None, None, FAKE, 1, None) == -1
 

@@ -361,3 +361,50 @@ def test_timed_forward_with_null_events_equals_forward():
     torch.cuda.synchronize()
     assert torch.equal(y, ref_y)
     assert ev[i].elapsed_time(ev[i + 1]) > 0.0
+
+
+def test_swiglu_ablation_full_parity():
+    # both caps at +inf: the uncapped limit, every expert a SwiGLU ([DD] §1 compares
+    # SiTU-GLU against it); same kernels, same parity bar
+    cfg = synth.get_config("C1").with_(beta1=np.inf, beta2=np.inf)
+    gpu = run_gpu(cfg)
+    P = synth.HostParams(cfg, cache=True)
+    x = P.x()
+    check_against_oracle(cfg, gpu, x, P)
+    check_dispatch(cfg, gpu)
+    check_hidden(cfg, gpu, P, x)
+
+
+def test_caps_bound_the_hidden_of_outlier_tokens():
+    """Forward activation maxima on outlier tokens, capped against uncapped.
+
+    One token in a hundred is scaled by 50 ([DD] §1: the caps exist for such
+    tokens, whose SwiGLU gate grows like the square of the input).  With
+    beta1 = 4, beta2 = 25 the gated hidden of those tokens saturates just below
+    beta1 * beta2 = 100; without the caps the oracle puts the shared expert's
+    maximum near 1.7e4 on this input, while the other tokens stay near 10
+    either way.  Both runs are held to the parity bar first, the outlier rows
+    apart from the rest (their elements are some 40 RMS of the whole batch, so
+    half an ulp of bf16 there would exceed a bound relative to the batch RMS)."""
+    base = synth.get_config("C1").with_(T=512, outlier_frac=0.01)
+    rows = synth.outlier_rows(base)
+    assert rows.size == 5
+    rest = np.setdiff1d(np.arange(base.T), rows)
+    peak = {}
+    for b in (4.0, np.inf):
+        cfg = base.with_(beta1=b, beta2=25.0 if b == 4.0 else np.inf)
+        gpu = run_gpu(cfg)
+        P = synth.HostParams(cfg)
+        x = P.x()
+        check_against_oracle(cfg, gpu, x[rows], P, rows=rows)
+        check_against_oracle(cfg, gpu, x[rest], P, rows=rest)
+        check_hidden(cfg, gpu, P, x)
+        T = cfg.T
+        shared = np.abs(gpu["hidden"][T * cfg.k:T * cfg.k + T * cfg.n_shared]).reshape(cfg.n_shared, T, -1)
+        per_tok = shared.max(axis=(0, 2))
+        others = np.delete(per_tok, rows)
+        peak[b] = (per_tok[rows].max(), others.max())
+    capped, free = peak[4.0], peak[np.inf]
+    assert 90.0 < capped[0] <= 100.0
+    assert free[0] > 1e4
+    assert capped[1] < 20.0 and free[1] < 20.0

@@ -177,12 +177,13 @@ def test_token_independence():
         assert np.array_equal(one["y"][0], full["y"][t])
 
 
-def test_swiglu_limit_of_layer_against_torch_experts():
+@pytest.mark.parametrize("beta", [1e30, np.inf])
+def test_swiglu_limit_of_layer_against_torch_experts(beta):
     # beta -> infinity turns every expert into SwiGLU; build that expert from torch's silu
     rng = np.random.default_rng(11)
     p = rand_params(rng, n_s=1)
     x = rng.standard_normal((4, 64))
-    out = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", beta1=1e30, beta2=1e30, eps=0.0)
+    out = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", beta1=beta, beta2=beta, eps=0.0)
     z = torch.from_numpy(out["z"])
     u = torch.zeros_like(z)
     for t in range(4):

@@ -84,8 +84,9 @@ def test_softcap_odd_bounded_and_small_x():
         xs = x[np.abs(x) <= 2.0]
         err = np.abs(ref.softcap(xs, beta) - xs)
         assert np.all(err <= np.abs(xs) ** 3 / (3 * beta ** 2) + 1e-15)
-    # beta -> infinity: identity
+    # beta -> infinity: identity; beta = +inf is that limit exactly
     assert np.allclose(ref.softcap(x, 1e30), x, rtol=1e-15, atol=0)
+    assert np.array_equal(ref.softcap(x, np.inf), x)
 
 
 def test_sigmoid_closed_forms():
@@ -103,6 +104,7 @@ def test_situ_closed_form_and_silu_limit():
     x = np.linspace(-30, 30, 6001)
     silu = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
     assert np.allclose(ref.situ(x, 1e30), silu, rtol=1e-13, atol=1e-300)
+    assert np.allclose(ref.situ(x, np.inf), silu, rtol=1e-14, atol=1e-300)
 
 
 def test_situ_range():
@@ -129,6 +131,9 @@ def test_situ_glu_product_bound_and_swiglu_limit():
     q2 = rng.standard_normal(1000) * 5
     sw = (torch.nn.functional.silu(torch.from_numpy(q1)) * torch.from_numpy(q2)).numpy()
     assert np.allclose(ref.situ_glu_hidden(q1, q2, 1e30, 1e30), sw, rtol=1e-13)
+    assert np.allclose(ref.situ_glu_hidden(q1, q2, np.inf, np.inf), sw, rtol=1e-14)
+    # without the caps the outlier-scale products above are no longer bounded
+    assert np.abs(ref.situ_glu_hidden(p1, p2, np.inf, np.inf)).max() > 1e6
 
 
 def test_situ_glu_branch_assignment():
