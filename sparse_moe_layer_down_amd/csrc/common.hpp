@@ -71,16 +71,21 @@ LMOE_DEV void store8(float *p, const float *v) {
 // ("Kimi K3 Architecture Deep Dive" §1)
 // The router's sigmoid uses the library expf (its scores feed the top-k and
 // the QB histogram); the gate epilogue, evaluated for every hidden unit of
-// every dispatched row, uses the hardware exp2 / reciprocal:
-//   tanh(y) = sign(y) (1 - e^{-2|y|}) / (1 + e^{-2|y|})     for |y| >= 3/8,
-//   tanh(y) = y - y^3/3 + 2y^5/15 - 17y^7/315 + 62y^9/2835 - 1382y^11/155925  below
-// (the odd Taylor series; the truncation error there is under 2e-8 relative), so
-// the first form never cancels by more than a factor of 3.5; both stay within
-// about 3e-7 relative of tanh, NaN and +-inf included.
+// every dispatched row, uses the hardware exp2 / reciprocal.  With y = x / beta:
+//   softcap = beta sign(y) (1 - e^{-2|y|}) / (1 + e^{-2|y|})          for |y| >= 3/8,
+//   softcap = x (1 - y^2/3 + 2y^4/15 - 17y^6/315 + 62y^8/2835 - 1382y^10/155925)  below
+// (tanh's odd Taylor series divided by y; the truncation error there is under
+// 2e-8 relative), so the first form never cancels by more than a factor of
+// 3.5; both stay within about 3e-7 relative of beta tanh(x / beta), NaN and
+// +-inf included (but beta = +inf turns an infinite x into NaN: y = inf * 0).
+// beta = +inf gives y = 0 for finite x and so exactly x, the uncapped
+// limit: SiTU becomes SiLU and SiTU-GLU becomes SwiGLU, the gate the caps are
+// measured against.
 LMOE_DEV float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 LMOE_DEV float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 LMOE_DEV float sigmoid_hw(float x) { return __builtin_amdgcn_rcpf(1.0f + exp_hw(-x)); }
-LMOE_DEV float tanh_hw(float y) {
+LMOE_DEV float softcapf_(float x, float beta) {
+  const float y = x * (1.0f / beta);  // 1/beta is hoisted
   const float a = fabsf(y);
   const float t = exp_hw(-2.0f * a);
   const float big = (1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t);
@@ -91,13 +96,7 @@ LMOE_DEV float tanh_hw(float y) {
   q = 2.0f / 15.0f + y2 * q;
   q = -1.0f / 3.0f + y2 * q;
   q = 1.0f + y2 * q;
-  const float r = a < 0.375f ? a * q : big;
-  return copysignf(r, y);
-}
-// beta = +inf takes the limit beta * tanh(x / beta) -> x (no cap): SiTU becomes
-// SiLU and SiTU-GLU becomes SwiGLU, the gate the caps are measured against.
-LMOE_DEV float softcapf_(float x, float beta) {
-  return beta == __builtin_inff() ? x : beta * tanh_hw(x * (1.0f / beta));  // 1/beta is hoisted
+  return a < 0.375f ? x * q : beta * copysignf(big, y);
 }
 LMOE_DEV float situf_(float x, float beta) { return softcapf_(x, beta) * sigmoid_hw(x); }
 
