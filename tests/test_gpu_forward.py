@@ -381,8 +381,8 @@ def test_caps_bound_the_hidden_of_outlier_tokens():
     One token in a hundred is scaled by 50 ([DD] §1: the caps exist for such
     tokens, whose SwiGLU gate grows like the square of the input).  With
     beta1 = 4, beta2 = 25 the gated hidden of those tokens saturates just below
-    beta1 * beta2 = 100; without the caps the oracle puts the shared expert's
-    maximum near 1.7e4 on this input, while the other tokens stay near 10
+    beta1 * beta2 = 100; without the caps the oracle puts the shared experts'
+    maximum near 2.6e4 on this input, while the other tokens stay near 10
     either way.  Both runs are held to the parity bar first, the outlier rows
     apart from the rest (their elements are some 40 RMS of the whole batch, so
     half an ulp of bf16 there would exceed a bound relative to the batch RMS)."""
