@@ -93,25 +93,44 @@ def softcap(x, beta):
     return beta * np.tanh(x / beta)
 
 
-def situ(x, beta):
+def hard_clip(x, beta):
+    """clamp(x; beta) = min(max(x, -beta), beta): the hard clip that the tanh
+    softcap replaces at the same ceiling ([DD] §1; [IK] section SiTU-GLU).
+
+    READING: the hard-clip ablation puts this in place of softcap in both
+    branches, with the same beta1 and beta2.
+    """
+    return np.clip(np.asarray(x, dtype=np.float64), -beta, beta)
+
+
+def cap(x, beta, gate="tanh"):
+    """The branch cap: softcap for gate "tanh" (the pages' choice), hard_clip for "clip"."""
+    if gate == "tanh":
+        return softcap(x, beta)
+    if gate == "clip":
+        return hard_clip(x, beta)
+    raise ValueError(f"unknown gate {gate!r}")
+
+
+def situ(x, beta, gate="tanh"):
     """SiTU(x; beta) = softcap(x; beta) * sigmoid(x)  ([DD] §1)."""
-    return softcap(x, beta) * sigmoid(x)
+    return cap(x, beta, gate) * sigmoid(x)
 
 
-def situ_glu_hidden(p1, p2, beta1, beta2):
+def situ_glu_hidden(p1, p2, beta1, beta2, gate="tanh"):
     """Gated hidden of SiTU-GLU: SiTU(W1 x; beta1) (.) softcap(W2 x; beta2)  ([DD] §1).
 
     READING: W1 is the gate branch (SiTU), W2 the linear branch (softcap), as
     the pages state; the W3 product is applied by the caller.
     """
-    return situ(p1, beta1) * softcap(p2, beta2)
+    return situ(p1, beta1, gate) * cap(p2, beta2, gate)
 
 
-def expert_hidden(zr, w1, w2, beta1, beta2, dtype):
+def expert_hidden(zr, w1, w2, beta1, beta2, dtype, gate="tanh"):
     """a = rnd(SiTU(zr W1^T; b1) * softcap(zr W2^T; b2)) for the rows routed to one expert."""
     p1 = zr @ w1.T
     p2 = zr @ w2.T
-    return round_to(situ_glu_hidden(p1, p2, beta1, beta2), dtype)
+    return round_to(situ_glu_hidden(p1, p2, beta1, beta2, gate), dtype)
 
 
 # ---------------------------------------------------------------------------
@@ -247,7 +266,7 @@ class ArrayParams:
         return np.ones(L) if self._gamma is None else np.asarray(self._gamma, dtype=np.float64)
 
 
-def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_idx=None):
+def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_idx=None, gate="tanh"):
     """Stable LatentMoE forward for the token rows x [T, d].
 
     Steps ([DD] §2 LatentMoE: d -(down)-> d/2 -(route/gate)-> D -> d/2 -(up)-> d;
@@ -265,7 +284,9 @@ def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_id
     READING: shared experts run in the latent space and are summed into u
     before the norm; the residual add of the surrounding block is not part of
     the layer.  forced_idx replaces step 3 (used to compare expert math on
-    tokens whose k-th/(k+1)-th scores are too close to call).
+    tokens whose k-th/(k+1)-th scores are too close to call).  gate="clip"
+    puts hard_clip in place of softcap in steps 6 and 8 (the hard-clip
+    ablation).
     """
     x = np.asarray(x, dtype=np.float64)
     w_router = P.w_router()
@@ -288,10 +309,10 @@ def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_id
         if lo == hi:
             continue
         toks = row_token[lo:hi]
-        a = expert_hidden(z[toks], P.w1(e), P.w2(e), beta1, beta2, dtype)
+        a = expert_hidden(z[toks], P.w1(e), P.w2(e), beta1, beta2, dtype, gate)
         u[toks] += g[toks, row_slot[lo:hi]][:, None] * (a @ P.w3(e).T)
     for j in range(n_shared):
-        a = expert_hidden(z, P.ws1(j), P.ws2(j), beta1, beta2, dtype)
+        a = expert_hidden(z, P.ws1(j), P.ws2(j), beta1, beta2, dtype, gate)
         u += a @ P.ws3(j).T
     v_pre = rms_norm(u, P.gamma(), eps)
     v = round_to(v_pre, dtype)

@@ -177,13 +177,14 @@ def test_token_independence():
         assert np.array_equal(one["y"][0], full["y"][t])
 
 
-@pytest.mark.parametrize("beta", [1e30, np.inf])
-def test_swiglu_limit_of_layer_against_torch_experts(beta):
-    # beta -> infinity turns every expert into SwiGLU; build that expert from torch's silu
+@pytest.mark.parametrize("beta,gate", [(1e30, "tanh"), (np.inf, "tanh"), (1e30, "clip"), (np.inf, "clip")])
+def test_swiglu_limit_of_layer_against_torch_experts(beta, gate):
+    # beta -> infinity turns every expert into SwiGLU, whichever cap (softcap or
+    # hard clip) is lifted; build that expert from torch's silu
     rng = np.random.default_rng(11)
     p = rand_params(rng, n_s=1)
     x = rng.standard_normal((4, 64))
-    out = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", beta1=beta, beta2=beta, eps=0.0)
+    out = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", beta1=beta, beta2=beta, eps=0.0, gate=gate)
     z = torch.from_numpy(out["z"])
     u = torch.zeros_like(z)
     for t in range(4):
@@ -194,6 +195,32 @@ def test_swiglu_limit_of_layer_against_torch_experts(beta):
         hs = torch.nn.functional.silu(torch.from_numpy(p["ws1"][0]) @ z[t]) * (torch.from_numpy(p["ws2"][0]) @ z[t])
         u[t] += torch.from_numpy(p["ws3"][0]) @ hs
     assert np.allclose(out["u"], u.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_hard_clip_layer_matches_hardtanh_experts():
+    # the hard-clip ablation: every expert's caps are torch's hardtanh at beta1, beta2
+    rng = np.random.default_rng(13)
+    p = rand_params(rng, n_s=1)
+    x = rng.standard_normal((4, 64)) * 30
+    out = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", eps=0.0, gate="clip")
+    tanh = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", eps=0.0)
+    assert np.array_equal(out["idx"], tanh["idx"])   # the gate does not touch routing
+    z = torch.from_numpy(out["z"])
+    ht = torch.nn.functional.hardtanh
+
+    def hidden(w1, w2, zt):
+        q1, q2 = w1 @ zt, w2 @ zt
+        return ht(q1, -4.0, 4.0) * torch.sigmoid(q1) * ht(q2, -25.0, 25.0)
+
+    u = torch.zeros_like(z)
+    for t in range(4):
+        for j in range(2):
+            e = int(out["idx"][t, j])
+            h = hidden(torch.from_numpy(p["w1"][e]), torch.from_numpy(p["w2"][e]), z[t])
+            u[t] += float(out["g"][t, j]) * (torch.from_numpy(p["w3"][e]) @ h)
+        u[t] += torch.from_numpy(p["ws3"][0]) @ hidden(torch.from_numpy(p["ws1"][0]), torch.from_numpy(p["ws2"][0]), z[t])
+    assert np.allclose(out["u"], u.numpy(), rtol=1e-12, atol=1e-12)
+    assert not np.allclose(out["u"], tanh["u"])
 
 
 def test_gated_hidden_bounded_on_outlier_tokens():

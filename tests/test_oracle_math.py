@@ -142,3 +142,29 @@ def test_situ_glu_branch_assignment():
     assert a == pytest.approx(768 / 17, rel=1e-14)
     swapped = ref.situ_glu_hidden(25 * math.log(3), 4 * math.log(2), 4.0, 25.0)
     assert abs(swapped - 768 / 17) > 1.0
+
+
+def test_hard_clip_is_hardtanh_and_its_gate():
+    # the hard clip the softcap replaces ([DD] §1) is torch's hardtanh at the same ceiling
+    x = np.concatenate([np.linspace(-200, 200, 40001), [4.0, -4.0, 25.0, -25.0, np.inf, -np.inf]])
+    for beta in (4.0, 25.0):
+        ht = torch.nn.functional.hardtanh(torch.from_numpy(x), -beta, beta).numpy()
+        assert np.array_equal(ref.hard_clip(x, beta), ht)
+        assert np.array_equal(ref.cap(x, beta, "clip"), ht)
+    # clipped SiTU: SiLU inside the ceiling, beta * sigmoid beyond it
+    silu = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    inside = np.abs(x) <= 4.0
+    assert np.allclose(ref.situ(x[inside], 4.0, "clip"), silu[inside], rtol=1e-14, atol=1e-300)
+    out = x[x > 4.0]
+    assert np.allclose(ref.situ(out, 4.0, "clip"), 4.0 * scipy.special.expit(out), rtol=1e-14)
+    # the gated product keeps the ceiling beta1 * beta2 and reaches it once both saturate
+    rng = np.random.default_rng(3)
+    p1 = rng.standard_normal(100000) * 1e4
+    p2 = rng.standard_normal(100000) * 1e4
+    a = ref.situ_glu_hidden(p1, p2, 4.0, 25.0, "clip")
+    assert np.all(np.abs(a) <= 100.0) and np.abs(a).max() == 100.0
+    # unlike the softcap, the clip maps every value past the ceiling to the same number
+    assert ref.hard_clip(30.0, 25.0) == ref.hard_clip(60.0, 25.0) == 25.0
+    assert ref.softcap(30.0, 25.0) < ref.softcap(60.0, 25.0) < 25.0
+    with pytest.raises(ValueError):
+        ref.cap(x, 4.0, "relu")
