@@ -71,6 +71,15 @@ typedef struct {
   int64_t T, d, L, n, k, n_shared, D;
 } lmoe_dims;
 
+/* Expert caps ("Kimi K3 Architecture Deep Dive" §1 and "Inside K3", section
+ * SiTU-GLU, contrast the tanh softcap with the hard clip it replaces):
+ *   LMOE_GATE_TANH  softcap(x; beta) = beta tanh(x / beta): SiTU-GLU, the layer
+ *                   as the pages define it
+ *   LMOE_GATE_CLIP  clamp(x; beta) = min(max(x, -beta), beta) in both branches,
+ *                   same beta1 and beta2: the hard-clip ablation
+ * Any other value is rejected with LMOE_ERR_VALUE. */
+typedef enum { LMOE_GATE_TANH = 0, LMOE_GATE_CLIP = 1 } lmoe_gate;
+
 /* Weights (device pointers, work dtype unless noted).
  *   w_down [L, d]        down-projection, no bias ([DD] §2: pure linear map)
  *   w_router [n, L]      router; scores s = sigmoid(z w_router^T + o)
@@ -91,7 +100,8 @@ typedef struct {
  *                        (0, +inf]; +inf is the uncapped limit (softcap
  *                        becomes the identity, SiTU becomes SiLU), so both at
  *                        +inf give the SwiGLU expert the caps replace
- *   rms_eps              RMSNorm epsilon (>= 0; 1e-6 by default)            */
+ *   rms_eps              RMSNorm epsilon (>= 0; 1e-6 by default)
+ *   gate                 lmoe_gate: how both expert branches are capped      */
 typedef struct {
   const void *w_down;
   const void *w_router;
@@ -102,6 +112,7 @@ typedef struct {
   const void *rms_gain;
   const void *w_up;
   float beta1, beta2, rms_eps;
+  int32_t gate;
 } lmoe_weights;
 
 /* Bytes of device workspace lmoe_forward needs for these dims and dtype

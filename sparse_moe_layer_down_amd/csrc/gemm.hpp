@@ -13,6 +13,7 @@
 //                 interleaves 32-row blocks of W1 and W2 for the same hidden
 //                 units so both products of one hidden unit land in the same
 //                 lane and register
+//   EPI_GLU_CLIP  the same with both caps a hard clip (the cap ablation)
 //   EPI_ROWSCALE  C[row] = row_scale[row] * acc            (routing weight g)
 //   EPI_PARTIAL   split-K: fp32 partial sums of one K range, C[split][row][col];
 //                 a finalize kernel sums the splits and applies the real
@@ -33,7 +34,24 @@
 
 namespace lmoe {
 
-enum { EPI_STORE = 0, EPI_SIGMOID = 1, EPI_GLU = 2, EPI_ROWSCALE = 3, EPI_PARTIAL = 4 };
+enum { EPI_STORE = 0, EPI_SIGMOID = 1, EPI_GLU = 2, EPI_ROWSCALE = 3, EPI_PARTIAL = 4, EPI_GLU_CLIP = 5 };
+
+// Both gated epilogues: EPI_GLU caps its branches with the tanh softcap,
+// EPI_GLU_CLIP with the hard clip clamp(x; beta) = min(max(x, -beta), beta) that
+// the softcap replaces at the same ceilings (the cap ablation; "Kimi K3
+// Architecture Deep Dive" §1).  The clamp keeps NaN (its comparisons fail).
+template <int EPI>
+constexpr bool is_glu = EPI == EPI_GLU || EPI == EPI_GLU_CLIP;
+
+LMOE_DEV float clampf_(float x, float beta) { return x < -beta ? -beta : (x > beta ? beta : x); }
+
+template <int EPI>
+LMOE_DEV float glu_(float x1, float x2, float beta1, float beta2) {
+  if constexpr (EPI == EPI_GLU_CLIP)
+    return clampf_(x1, beta1) * sigmoid_hw(x1) * clampf_(x2, beta2);
+  else
+    return situf_(x1, beta1) * softcapf_(x2, beta2);
+}
 
 struct GemmArgs {
   const void *A;            // [rows, lda]
@@ -157,7 +175,7 @@ LMOE_DEV TileI decode_tile(const GemmArgs &p, int l, int nk_all) {
 // lines.
 template <typename TO, int EPI, int WTN, int TN>
 struct StagedStore {
-  static constexpr bool value = (EPI == EPI_ROWSCALE || EPI == EPI_STORE || EPI == EPI_GLU) &&
+  static constexpr bool value = (EPI == EPI_ROWSCALE || EPI == EPI_STORE || is_glu<EPI>) &&
                                 sizeof(TO) == 2 && WTN == 64 && TN == 2;
 };
 constexpr int STAGE_BYTES_PER_WAVE = 32 * 128;
@@ -167,7 +185,7 @@ LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, i
                          int wm, int wn, int half, int l32, unsigned char *stage) {
   TO *C = (TO *)p.C;
   if constexpr (StagedStore<TO, EPI, WTN, TN>::value) {
-    constexpr bool GLU = EPI == EPI_GLU;
+    constexpr bool GLU = is_glu<EPI>;
     constexpr int CPR = GLU ? 4 : 8;  // 16-byte chunks per staged row (32 or 64 outputs)
     const int lane = half * 32 + l32;
     const int nout = GLU ? p.N / 2 : p.N;
@@ -187,7 +205,7 @@ LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, i
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             if (GLU)
-              o[c] = situf_(acc[a][0][4 * g + c], p.beta1) * softcapf_(acc[a][1][4 * g + c], p.beta2);
+              o[c] = glu_<EPI>(acc[a][0][4 * g + c], acc[a][1][4 * g + c], p.beta1, p.beta2);
             else
               o[c] = acc[a][b][4 * g + c] * rs;
           }
@@ -220,7 +238,7 @@ LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, i
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           if (c0 + c >= nout) continue;
-          const float v = GLU ? situf_(acc[a][0][4 * g + c], p.beta1) * softcapf_(acc[a][1][4 * g + c], p.beta2)
+          const float v = GLU ? glu_<EPI>(acc[a][0][4 * g + c], acc[a][1][4 * g + c], p.beta1, p.beta2)
                               : acc[a][b][4 * g + c] * rs;
           C[(m0 + rl) * p.ldc + c0 + c] = from_f32<TO>(v);
         }
@@ -237,14 +255,14 @@ LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, i
     const float rs = (EPI == EPI_ROWSCALE) ? p.row_scale[grow] : 1.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if (EPI == EPI_GLU) {
+      if (is_glu<EPI>) {
 #pragma unroll
         for (int b = 0; b < TN; b += 2) {
           const int64_t h0 = (int64_t)nt * (BN / 2) + wn * (WTN / 2) + (b / 2) * 32 + g * 8 + half * 4;
           float o[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            o[c] = situf_(acc[a][b][4 * g + c], p.beta1) * softcapf_(acc[a][b + 1][4 * g + c], p.beta2);
+            o[c] = glu_<EPI>(acc[a][b][4 * g + c], acc[a][b + 1][4 * g + c], p.beta1, p.beta2);
           TO *dst = C + grow * p.ldc + h0;
           if (vec && h0 + 3 < p.N / 2) {
             store4(dst, o);
@@ -328,7 +346,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   constexpr int NSET = PF;  // B register sets: B(j) lives in set j % PF
   static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of the load pass");
   static_assert(BM % (32 * WM) == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(EPI != EPI_GLU || TN % 2 == 0, "GLU needs W1/W2 subtile pairs");
+  static_assert(!is_glu<EPI> || TN % 2 == 0, "GLU needs W1/W2 subtile pairs");
   static_assert(PF >= 1 && PF <= 4, "prefetch distance");
   static_assert(NG == 2 || NG == 4, "16-K groups per 128-byte K step");
   static_assert(!BDMA || (PF == 2 && RPP == 64 && EPI != EPI_PARTIAL), "load to LDS: two-step pipeline, 8 waves");
@@ -425,7 +443,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
       const int br = lrow + i * RPP;
-      if (EPI == EPI_GLU) {
+      if (is_glu<EPI>) {
         const int wcol = br / WTN, within = br % WTN, j = within / 32;
         const int row = t.nt * (BN / 2) + wcol * (WTN / 2) + (j / 2) * 32 + (br & 31);
         b_row[i] = min(row, p.N / 2 - 1);
@@ -441,7 +459,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     }
     const int bc = BDMA ? lbc : lchunk;
     lb1 = (const T *)t.B + bc * EPT;
-    lb2 = ((EPI == EPI_GLU || EPI == EPI_PARTIAL) && t.B2) ? (const T *)t.B2 + bc * EPT : lb1;
+    lb2 = ((is_glu<EPI> || EPI == EPI_PARTIAL) && t.B2) ? (const T *)t.B2 + bc * EPT : lb1;
     lkbeg = t.kbeg;
   };
   const T *const Abase = (const T *)p.A + lchunk * EPT;
@@ -762,13 +780,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
 }
 
 // Split-K finalize: out = epilogue(sum over splits of the fp32 partials).
-// EPI_GLU reads the stacked layout: W1 products in columns [0, H), W2 in [H, 2H).
+// The gated epilogues read the stacked layout: W1 products in columns [0, H), W2 in [H, 2H).
 template <typename TO, int EPI>
 __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__restrict__ part, int splits, int M,
                                                               int Np, TO *__restrict__ out, int64_t ldo,
                                                               const float *__restrict__ col_bias, float beta1,
                                                               float beta2) {
-  const int Nout = (EPI == EPI_GLU) ? Np / 2 : Np;
+  const int Nout = (is_glu<EPI>) ? Np / 2 : Np;
   const int64_t total = (int64_t)M * Nout;
   const int64_t plane = (int64_t)M * Np;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
@@ -776,10 +794,10 @@ __global__ __launch_bounds__(256) void splitk_finalize_kernel(const float *__res
     const float *pp = part + (int64_t)m * Np + c;
     float v = 0.0f;
     for (int sp = 0; sp < splits; ++sp) v += pp[sp * plane];
-    if (EPI == EPI_GLU) {
+    if (is_glu<EPI>) {
       float v2 = 0.0f;
       for (int sp = 0; sp < splits; ++sp) v2 += pp[sp * plane + Nout];
-      v = situf_(v, beta1) * softcapf_(v2, beta2);
+      v = glu_<EPI>(v, v2, beta1, beta2);
     } else if (EPI == EPI_SIGMOID) {
       if (col_bias) v += col_bias[c];
       v = sigmoidf_(v);

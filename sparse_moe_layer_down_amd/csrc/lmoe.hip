@@ -256,12 +256,12 @@ hipError_t launch_dense(GemmArgs a, float *part, hipStream_t st) {
   b.ldc = a.N;
   b.splits = pl.sp.splits;
   b.ksteps = pl.sp.ksteps;
-  b.b_split_row = (EPI == EPI_GLU) ? a.N / 2 : a.N;
-  if (EPI != EPI_GLU) b.B2 = nullptr;
+  b.b_split_row = is_glu<EPI> ? a.N / 2 : a.N;
+  if (!is_glu<EPI>) b.B2 = nullptr;
   hipError_t e = (pl.mode == DM_SKINNY) ? launch_gemm<CfgSkinny, T, float, EPI_PARTIAL, false, false>(b, st)
                                         : launch_gemm<CfgMid, T, float, EPI_PARTIAL, false, false>(b, st);
   if (e != hipSuccess) return e;
-  const int64_t outs = (int64_t)a.M * (EPI == EPI_GLU ? a.N / 2 : a.N);
+  const int64_t outs = (int64_t)a.M * (is_glu<EPI> ? a.N / 2 : a.N);
   const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(outs, 256), 8192);
   hipLaunchKernelGGL((splitk_finalize_kernel<TO, EPI>), dim3(blocks), dim3(256), 0, st, part, pl.sp.splits, a.M,
                      a.N, (TO *)a.C, a.ldc, a.col_bias, a.beta1, a.beta2);
@@ -361,8 +361,13 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, w12_bm(d));
     a.sched = ntiles + 2;
     a.beta1 = w.beta1; a.beta2 = w.beta2;
-    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_GLU, true, true>(a, st)));
-    else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU, true, true>(a, st)));
+    if (w.gate == LMOE_GATE_CLIP) {
+      if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_GLU_CLIP, true, true>(a, st)));
+      else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU_CLIP, true, true>(a, st)));
+    } else {
+      if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_GLU, true, true>(a, st)));
+      else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU, true, true>(a, st)));
+    }
   }
   // 6 W3 of every expert row, scaled by its weight (g, or 1 for shared rows)
   LMOE_MARK(5);
@@ -425,7 +430,8 @@ static int forward_impl(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   if (rc != LMOE_OK) return rc;
   if (!w) return LMOE_ERR_NULL;
   if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
-  if (!(w->beta1 > 0.0f) || !(w->beta2 > 0.0f) || !(w->rms_eps >= 0.0f) || w->rms_eps == INFINITY)
+  if (!(w->beta1 > 0.0f) || !(w->beta2 > 0.0f) || !(w->rms_eps >= 0.0f) || w->rms_eps == INFINITY ||
+      (w->gate != LMOE_GATE_TANH && w->gate != LMOE_GATE_CLIP))
     return LMOE_ERR_VALUE;
   if (dims->T == 0) return LMOE_OK;
   if (!x || !y || !workspace || !w->w_down || !w->w_router || !w->router_bias || !w->w1 || !w->w2 || !w->w3 ||

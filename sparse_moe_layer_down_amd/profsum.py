@@ -25,7 +25,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 COPY_BYTES = 1 << 30
-EPI = {0: "store", 1: "sigmoid", 2: "SiTU-GLU", 3: "rowscale", 4: "split-K partial"}
+EPI = {0: "store", 1: "sigmoid", 2: "SiTU-GLU", 3: "rowscale", 4: "split-K partial", 5: "clip-GLU"}
 
 
 def source_sha256():

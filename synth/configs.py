@@ -32,6 +32,7 @@ class Config:
     nbins: int = 1000
     beta1: float = 4.0
     beta2: float = 25.0
+    gate: str = "tanh"  # expert caps: "tanh" softcap, or "clip" for the hard-clip ablation
     eps: float = 1e-6
 
     def flops_per_token(self):

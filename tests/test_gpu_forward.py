@@ -59,7 +59,7 @@ def run_gpu(cfg, x=None, weights=None, step=None):
     dims = lmoe.dims_of(x, w, cfg.k)
     ws = lmoe.make_workspace(dims, x.dtype, dev)
     y = lmoe.forward(x, w, cfg.k, topk_idx=idx, topk_w=tw, scores=s, workspace=ws,
-                     beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps)
+                     beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, gate=cfg.gate)
     torch.cuda.synchronize()
     out = dict(y=y.double().cpu().numpy(), idx=idx.cpu().numpy().astype(np.int64), g=tw.double().cpu().numpy(),
                s=s.double().cpu().numpy())
@@ -78,12 +78,13 @@ def check_against_oracle(cfg, gpu, x_host, P, rows=None):
     sel = np.arange(x_host.shape[0]) if rows is None else np.asarray(rows)
     g_idx = gpu["idx"][sel]
     # the oracle's own routing decision
-    own = ref.forward(x_host, P, cfg.k, cfg.n_shared, dt, cfg.beta1, cfg.beta2, cfg.eps)
+    own = ref.forward(x_host, P, cfg.k, cfg.n_shared, dt, cfg.beta1, cfg.beta2, cfg.eps, gate=cfg.gate)
     clear = own["gap"] >= GAP
     assert clear.mean() > 0.5
     assert np.array_equal(np.sort(own["idx"][clear], 1), np.sort(g_idx[clear], 1)), "top-k sets differ"
     # expert math on the GPU's routing
-    forced = ref.forward(x_host, P, cfg.k, cfg.n_shared, dt, cfg.beta1, cfg.beta2, cfg.eps, forced_idx=g_idx)
+    forced = ref.forward(x_host, P, cfg.k, cfg.n_shared, dt, cfg.beta1, cfg.beta2, cfg.eps, forced_idx=g_idx,
+                         gate=cfg.gate)
     tl = tol(dt, cfg.d)
     assert rel_err(gpu["z"][sel], forced["z_pre"], f"{cfg.name} z", tl) <= tl, "z"
     assert rel_err(gpu["s"][sel], forced["s"], f"{cfg.name} s", tl) <= tl, "scores"
@@ -135,12 +136,12 @@ def check_hidden(cfg, gpu, P, x_host):
         if lo == hi:
             continue
         toks = gpu["row_token"][lo:hi]
-        a = ref.expert_hidden(z[toks], P.w1(e), P.w2(e), cfg.beta1, cfg.beta2, "f64")
+        a = ref.expert_hidden(z[toks], P.w1(e), P.w2(e), cfg.beta1, cfg.beta2, "f64", cfg.gate)
         r = worst(gpu["hidden"][lo:hi], a)
         assert r <= 1.0, f"expert {e}: error {r:.3g} x the bound"
     T = z.shape[0]
     for j in range(cfg.n_shared):  # shared expert j: rows T*k + j*T .. + T, one per token
-        a = ref.expert_hidden(z, P.ws1(j), P.ws2(j), cfg.beta1, cfg.beta2, "f64")
+        a = ref.expert_hidden(z, P.ws1(j), P.ws2(j), cfg.beta1, cfg.beta2, "f64", cfg.gate)
         r = worst(gpu["hidden"][T * cfg.k + j * T:T * cfg.k + (j + 1) * T], a)
         assert r <= 1.0, f"shared expert {j}: error {r:.3g} x the bound"
     assert np.all(np.abs(gpu["hidden"]) <= cfg.beta1 * cfg.beta2)
@@ -408,3 +409,45 @@ def test_caps_bound_the_hidden_of_outlier_tokens():
     assert 90.0 < capped[0] <= 100.0
     assert free[0] > 1e4
     assert capped[1] < 20.0 and free[1] < 20.0
+
+
+@pytest.mark.parametrize("shape", [
+    dict(name="C1"),
+    dict(name="C0", T=333, d=512, L=256, n=200, k=7, n_shared=3, D=64, dtype="bf16"),   # ragged, small experts
+])
+def test_hard_clip_ablation_full_parity(shape):
+    # both caps a hard clip at beta1 = 4, beta2 = 25: the ablation the tanh softcap
+    # is compared against ([DD] §1), in the same kernels, at the same parity bar
+    shape = dict(shape)
+    cfg = synth.get_config(shape.pop("name")).with_(gate="clip", x_seed=31, **shape)
+    gpu = run_gpu(cfg)
+    P = synth.HostParams(cfg)
+    x = P.x()
+    check_against_oracle(cfg, gpu, x, P)
+    check_dispatch(cfg, gpu)
+    check_hidden(cfg, gpu, P, x)
+
+
+def test_hard_clip_collapses_outlier_hidden_to_the_ceiling():
+    """On 1% x50 outlier tokens both caps hold the gated hidden to the same
+    ceiling beta1 * beta2 = 100, but the hard clip maps every unit past both
+    thresholds onto 100 * sigmoid(x1), i.e. onto the ceiling itself once
+    stored in bf16, while the softcap keeps most of them below it (the pages:
+    a clamp collapses every value past the threshold onto one number).  On
+    this input the oracle puts 1459 of the outlier tokens' 5120 shared-expert
+    units at exactly 100 with the clip and 208 with the softcap."""
+    base = synth.get_config("C1").with_(T=512, outlier_frac=0.01)
+    rows = synth.outlier_rows(base)
+    T = base.T
+    sat = {}
+    for gate in ("tanh", "clip"):
+        cfg = base.with_(gate=gate)
+        gpu = run_gpu(cfg)
+        P = synth.HostParams(cfg)
+        x = P.x()
+        check_against_oracle(cfg, gpu, x[rows], P, rows=rows)
+        check_hidden(cfg, gpu, P, x)
+        h = np.abs(gpu["hidden"][T * cfg.k:T * cfg.k + T * cfg.n_shared]).reshape(cfg.n_shared, T, -1)[:, rows]
+        assert h.max() == 100.0
+        sat[gate] = int((h == 100.0).sum())
+    assert sat["clip"] > 3 * sat["tanh"]
