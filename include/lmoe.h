@@ -152,7 +152,8 @@ int64_t lmoe_workspace_offset(const lmoe_dims *dims, int dtype, int region);
  *   u_i += sum_j W3s_j (SiTU(W1s_j z_i; beta1) * softcap(W2s_j z_i; beta2))
  *   v = rms_gain * u / sqrt(mean(u^2) + rms_eps)  (work dtype)
  *   y = v w_up^T                        (work dtype)
- * where softcap(x; b) = b tanh(x / b) and SiTU(x; b) = softcap(x; b) sigmoid(x).
+ * where softcap(x; b) = b tanh(x / b) and SiTU(x; b) = softcap(x; b) sigmoid(x);
+ * with w->gate == LMOE_GATE_CLIP every softcap above is clamp(x; b) instead.
  * Arguments:
  *   x [T, d]      input tokens, work dtype
  *   y [T, d]      output, work dtype (may not alias x)
