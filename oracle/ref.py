@@ -266,7 +266,8 @@ class ArrayParams:
         return np.ones(L) if self._gamma is None else np.asarray(self._gamma, dtype=np.float64)
 
 
-def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_idx=None, gate="tanh"):
+def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_idx=None, gate="tanh",
+            norm="rms"):
     """Stable LatentMoE forward for the token rows x [T, d].
 
     Steps ([DD] §2 LatentMoE: d -(down)-> d/2 -(route/gate)-> D -> d/2 -(up)-> d;
@@ -286,8 +287,11 @@ def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_id
     the layer.  forced_idx replaces step 3 (used to compare expert math on
     tokens whose k-th/(k+1)-th scores are too close to call).  gate="clip"
     puts hard_clip in place of softcap in steps 6 and 8 (the hard-clip
-    ablation).
+    ablation).  norm="none" drops step 9's norm, v = rnd(u) (the ablation of
+    the one retained norm, [DD] §2).
     """
+    if norm not in ("rms", "none"):
+        raise ValueError(f"unknown norm {norm!r}")
     x = np.asarray(x, dtype=np.float64)
     w_router = P.w_router()
     n = w_router.shape[0]
@@ -314,7 +318,7 @@ def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_id
     for j in range(n_shared):
         a = expert_hidden(z, P.ws1(j), P.ws2(j), beta1, beta2, dtype, gate)
         u += a @ P.ws3(j).T
-    v_pre = rms_norm(u, P.gamma(), eps)
+    v_pre = rms_norm(u, P.gamma(), eps) if norm == "rms" else u
     v = round_to(v_pre, dtype)
     y_pre = v @ P.w_up().T
     y = round_to(y_pre, dtype)

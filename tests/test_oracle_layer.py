@@ -223,6 +223,28 @@ def test_hard_clip_layer_matches_hardtanh_experts():
     assert not np.allclose(out["u"], tanh["u"])
 
 
+def test_no_norm_ablation_against_the_normed_layer():
+    # without the norm, v = u: y is the normed layer's y times each token's RMS(u)
+    # (gain 1, eps 0), and it scales with the expert outputs, which the norm cancels
+    rng = np.random.default_rng(14)
+    p = rand_params(rng, n_s=1)
+    x = rng.standard_normal((5, 64))
+    normed = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", eps=0.0)
+    plain = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", eps=0.0, norm="none")
+    assert np.array_equal(plain["u"], normed["u"]) and np.array_equal(plain["v"], plain["u"])
+    rms = np.sqrt(np.mean(normed["u"] ** 2, axis=1, keepdims=True))
+    assert np.allclose(plain["y"], normed["y"] * rms, rtol=1e-12, atol=1e-14)
+    q = dict(p)
+    q["w3"] = p["w3"] * 3.0
+    q["ws3"] = p["ws3"] * 3.0
+    assert np.allclose(ref.forward(x, P(q), k=2, n_shared=1, dtype="f64", eps=0.0, norm="none")["y"],
+                       3.0 * plain["y"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(ref.forward(x, P(q), k=2, n_shared=1, dtype="f64", eps=0.0)["y"], normed["y"],
+                       rtol=1e-12, atol=1e-14)
+    with pytest.raises(ValueError):
+        ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", norm="layer")
+
+
 def test_gated_hidden_bounded_on_outlier_tokens():
     # the configured C2 outliers (x50) saturate the caps but never exceed beta1*beta2
     rng = np.random.default_rng(12)
