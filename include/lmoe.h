@@ -80,6 +80,14 @@ typedef struct {
  * Any other value is rejected with LMOE_ERR_VALUE. */
 typedef enum { LMOE_GATE_TANH = 0, LMOE_GATE_CLIP = 1 } lmoe_gate;
 
+/* The norm before the up-projection ("Kimi K3 Architecture Deep Dive" §2 keeps
+ * this one RMSNorm and no other):
+ *   LMOE_NORM_RMS   v = rms_gain * u / sqrt(mean(u^2) + rms_eps): the layer as
+ *                   the pages define it
+ *   LMOE_NORM_NONE  v = u (rms_gain and rms_eps unused): the ablation
+ * Any other value is rejected with LMOE_ERR_VALUE. */
+typedef enum { LMOE_NORM_RMS = 0, LMOE_NORM_NONE = 1 } lmoe_norm;
+
 /* Weights (device pointers, work dtype unless noted).
  *   w_down [L, d]        down-projection, no bias ([DD] §2: pure linear map)
  *   w_router [n, L]      router; scores s = sigmoid(z w_router^T + o)
@@ -101,7 +109,8 @@ typedef enum { LMOE_GATE_TANH = 0, LMOE_GATE_CLIP = 1 } lmoe_gate;
  *                        becomes the identity, SiTU becomes SiLU), so both at
  *                        +inf give the SwiGLU expert the caps replace
  *   rms_eps              RMSNorm epsilon (>= 0; 1e-6 by default)
- *   gate                 lmoe_gate: how both expert branches are capped      */
+ *   gate                 lmoe_gate: how both expert branches are capped
+ *   norm                 lmoe_norm: the norm before the up-projection          */
 typedef struct {
   const void *w_down;
   const void *w_router;
@@ -113,6 +122,7 @@ typedef struct {
   const void *w_up;
   float beta1, beta2, rms_eps;
   int32_t gate;
+  int32_t norm;
 } lmoe_weights;
 
 /* Bytes of device workspace lmoe_forward needs for these dims and dtype
@@ -153,7 +163,8 @@ int64_t lmoe_workspace_offset(const lmoe_dims *dims, int dtype, int region);
  *   v = rms_gain * u / sqrt(mean(u^2) + rms_eps)  (work dtype)
  *   y = v w_up^T                        (work dtype)
  * where softcap(x; b) = b tanh(x / b) and SiTU(x; b) = softcap(x; b) sigmoid(x);
- * with w->gate == LMOE_GATE_CLIP every softcap above is clamp(x; b) instead.
+ * with w->gate == LMOE_GATE_CLIP every softcap above is clamp(x; b) instead,
+ * and with w->norm == LMOE_NORM_NONE, v = u (work dtype).
  * Arguments:
  *   x [T, d]      input tokens, work dtype
  *   y [T, d]      output, work dtype (may not alias x)

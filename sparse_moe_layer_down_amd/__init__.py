@@ -9,7 +9,7 @@ import ctypes
 
 import torch
 
-from ._abi import (Dims, Weights, GATES, LMOE_BF16, LMOE_F32, WS_REGIONS, EXPORTS, N_STAGES, STAGES, lib,  # noqa: F401
+from ._abi import (Dims, Weights, GATES, NORMS, LMOE_BF16, LMOE_F32, WS_REGIONS, EXPORTS, N_STAGES, STAGES, lib,  # noqa: F401
                    check, strerror)
 
 __all__ = ["dims_of", "workspace_size", "workspace_view", "forward", "qb_update", "qb_workspace_size",
@@ -63,18 +63,20 @@ def workspace_view(workspace, dims, dtype, region):
     return workspace[off:off + cnt * nbytes].view(dt).view(*shape)
 
 
-def _weights_struct(w, beta1, beta2, eps, gate="tanh"):
+def _weights_struct(w, beta1, beta2, eps, gate="tanh", norm="rms"):
     return Weights(_ptr(w["w_down"]), _ptr(w["w_router"]), _ptr(w["router_bias"]),
                    _ptr(w.get("router_logit_offset")), _ptr(w["w1"]), _ptr(w["w2"]), _ptr(w["w3"]),
                    _ptr(w.get("ws1")), _ptr(w.get("ws2")), _ptr(w.get("ws3")), _ptr(w["rms_gain"]),
-                   _ptr(w["w_up"]), float(beta1), float(beta2), float(eps), GATES[gate])
+                   _ptr(w["w_up"]), float(beta1), float(beta2), float(eps), GATES[gate],
+                   NORMS[norm])
 
 
 def forward(x, weights, k, y=None, topk_idx=None, topk_w=None, scores=None, workspace=None, beta1=4.0,
-            beta2=25.0, eps=1e-6, stream=None, stage_events=None, gate="tanh"):
+            beta2=25.0, eps=1e-6, stream=None, stage_events=None, gate="tanh", norm="rms"):
     """y = LatentMoE(x) via lmoe_forward on the current stream; returns y.
 
-    ``gate`` is "tanh" (SiTU-GLU) or "clip" (both caps a hard clip: the ablation).
+    ``gate`` is "tanh" (SiTU-GLU) or "clip" (both caps a hard clip: the ablation);
+    ``norm`` is "rms" (the layer's one RMSNorm) or "none" (v = u: the ablation).
 
     ``weights`` holds device tensors named as in include/lmoe.h (w_down, w_router,
     router_bias, router_logit_offset, w1, w2, w3, ws1, ws2, ws3, rms_gain, w_up).
@@ -86,7 +88,7 @@ def forward(x, weights, k, y=None, topk_idx=None, topk_w=None, scores=None, work
         workspace = make_workspace(dims, x.dtype, x.device)
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    W = _weights_struct(weights, beta1, beta2, eps, gate)
+    W = _weights_struct(weights, beta1, beta2, eps, gate, norm)
     if stage_events is None:
         rc = lib().lmoe_forward(dims, W, _dtype_code(x.dtype), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w),
                                 _ptr(scores), _ptr(workspace), workspace.numel(), stream)

@@ -30,9 +30,10 @@ class Weights(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in ("w_down", "w_router", "router_bias", "router_logit_offset", "w1",
                                                "w2", "w3", "ws1", "ws2", "ws3", "rms_gain", "w_up")] + \
                [("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("rms_eps", ctypes.c_float),
-                ("gate", ctypes.c_int32)]
+                ("gate", ctypes.c_int32), ("norm", ctypes.c_int32)]
 
 GATES = {"tanh": 0, "clip": 1}  # lmoe_gate
+NORMS = {"rms": 0, "none": 1}   # lmoe_norm
 
 
 _lib = None

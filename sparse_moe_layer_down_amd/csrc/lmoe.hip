@@ -385,13 +385,14 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   {
     const int nch8 = L / 8;
     const T *gain = (const T *)w.rms_gain;
+    const int no_norm = w.norm == LMOE_NORM_NONE;
     const dim3 wg((unsigned)cdiv(d.T, 4));
-    if (nch8 <= 64) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 1>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
-    else if (nch8 <= 128) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 2>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
-    else if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 4>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
-    else if (nch8 <= 448) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 7>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
-    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 8>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
-    else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 4>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps);
+    if (nch8 <= 64) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 1>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+    else if (nch8 <= 128) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 2>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+    else if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 4>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+    else if (nch8 <= 448) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 7>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 8>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+    else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 4>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
     LMOE_TRY(hipGetLastError());
   }
   // 8 y = v W_up^T
@@ -431,7 +432,7 @@ static int forward_impl(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   if (!w) return LMOE_ERR_NULL;
   if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
   if (!(w->beta1 > 0.0f) || !(w->beta2 > 0.0f) || !(w->rms_eps >= 0.0f) || w->rms_eps == INFINITY ||
-      (w->gate != LMOE_GATE_TANH && w->gate != LMOE_GATE_CLIP))
+      (w->gate != LMOE_GATE_TANH && w->gate != LMOE_GATE_CLIP) || (w->norm != LMOE_NORM_RMS && w->norm != LMOE_NORM_NONE))
     return LMOE_ERR_VALUE;
   if (dims->T == 0) return LMOE_OK;
   if (!x || !y || !workspace || !w->w_down || !w->w_router || !w->router_bias || !w->w1 || !w->w2 || !w->w3 ||

@@ -5,7 +5,8 @@
 // retained RMSNorm then gives v = gain * u / sqrt(mean(u^2) + eps)
 // ("Kimi K3 Architecture Deep Dive" §2: one RMS norm before the
 // up-projection; LeiPhone report "Keeping the numbers in range": after
-// aggregation, before projecting back up).  u stays in registers between the
+// aggregation, before projecting back up); with no_norm set (the ablation of
+// that norm) v = u.  u stays in registers between the
 // two passes.  Up to L = 4096 one wave handles one token (CPT 16-byte chunks
 // of the row per lane, no block barrier); wider rows use one work-group per
 // token.
@@ -34,7 +35,8 @@ template <typename T, typename TS, int CPT>
 __global__ __launch_bounds__(256) void combine_rmsnorm_wave_kernel(const TS *__restrict__ ystage,
                                                                    const int32_t *__restrict__ slot_row,
                                                                    const T *__restrict__ gain, T *__restrict__ v,
-                                                                   int T_, int L, int k, int n_shared, float eps) {
+                                                                   int T_, int L, int k, int n_shared, float eps,
+                                                                   int no_norm) {
   constexpr int RIF = 2;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;  // the whole wave: no barrier follows
@@ -86,6 +88,10 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_wave_kernel(const TS *__r
   for (int q = 0; q < CPT; ++q) {
     const int ch = lane + q * 64;
     if (ch < nch) {
+      if (no_norm) {  // the ablation: v = u
+        store8(v + t * L + ch * 8, u[q]);
+        continue;
+      }
       float g[8], o[8];
       load8_f32(gain + ch * 8, g);
 #pragma unroll
@@ -99,7 +105,8 @@ template <typename T, typename TS, int CPT>
 __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS *__restrict__ ystage,
                                                               const int32_t *__restrict__ slot_row,
                                                               const T *__restrict__ gain, T *__restrict__ v,
-                                                              int T_, int L, int k, int n_shared, float eps) {
+                                                              int T_, int L, int k, int n_shared, float eps,
+                                                              int no_norm) {
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const int nch = L / 8;
@@ -152,6 +159,10 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS *__restri
   for (int q = 0; q < CPT; ++q) {
     const int ch = threadIdx.x + q * 256;
     if (ch < nch) {
+      if (no_norm) {  // the ablation: v = u
+        store8(v + t * L + ch * 8, u[q]);
+        continue;
+      }
       float g[8], o[8];
       load8_f32(gain + ch * 8, g);
 #pragma unroll

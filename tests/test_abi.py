@@ -62,7 +62,7 @@ def fake_weights(n_shared=2, **over):
     vals = dict(w_down=FAKE, w_router=FAKE, router_bias=FAKE, router_logit_offset=None, w1=FAKE, w2=FAKE,
                 w3=FAKE, ws1=FAKE if n_shared else None, ws2=FAKE if n_shared else None,
                 ws3=FAKE if n_shared else None, rms_gain=FAKE, w_up=FAKE, beta1=4.0, beta2=25.0, rms_eps=1e-6,
-                gate=0)
+                gate=0, norm=0)
     vals.update(over)
     return Weights(*[vals[f] for f, _ in Weights._fields_])
 
@@ -93,6 +93,7 @@ def test_other_errors():
     assert call(d, fake_weights(beta1=math.nan)) == -7
     assert call(d, fake_weights(gate=2)) == -7
     assert call(d, fake_weights(gate=-1)) == -7
+    assert call(d, fake_weights(norm=2)) == -7
     assert call(d, fake_weights(rms_eps=-1.0)) == -7
     assert lib().lmoe_forward(None, ctypes.byref(fake_weights()), 1, FAKE, FAKE, None, None, None, FAKE, 1, None) == -1
 
