@@ -288,14 +288,19 @@ def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_id
     tokens whose k-th/(k+1)-th scores are too close to call).  gate="clip"
     puts hard_clip in place of softcap in steps 6 and 8 (the hard-clip
     ablation).  norm="none" drops step 9's norm, v = rnd(u) (the ablation of
-    the one retained norm, [DD] §2).
+    the one retained norm, [DD] §2); norm="both" keeps it and adds the norm
+    the pages leave out after the down-projection: step 1 becomes
+    z = rnd(RMSNorm(rnd(x W_down^T))), unit gain, the same eps (READING: the
+    stored z is normed in place, so the router and the experts both see it).
     """
-    if norm not in ("rms", "none"):
+    if norm not in ("rms", "none", "both"):
         raise ValueError(f"unknown norm {norm!r}")
     x = np.asarray(x, dtype=np.float64)
     w_router = P.w_router()
     n = w_router.shape[0]
     z_pre = x @ P.w_down().T
+    if norm == "both":
+        z_pre = rms_norm(round_to(z_pre, dtype), np.ones(z_pre.shape[1]), eps)
     z = round_to(z_pre, dtype)
     s = router_scores(z, w_router, P.logit_offset())
     if forced_idx is None:
@@ -318,7 +323,7 @@ def forward(x, P, k, n_shared, dtype, beta1=4.0, beta2=25.0, eps=1e-6, forced_id
     for j in range(n_shared):
         a = expert_hidden(z, P.ws1(j), P.ws2(j), beta1, beta2, dtype, gate)
         u += a @ P.ws3(j).T
-    v_pre = rms_norm(u, P.gamma(), eps) if norm == "rms" else u
+    v_pre = u if norm == "none" else rms_norm(u, P.gamma(), eps)
     v = round_to(v_pre, dtype)
     y_pre = v @ P.w_up().T
     y = round_to(y_pre, dtype)

@@ -245,6 +245,29 @@ def test_no_norm_ablation_against_the_normed_layer():
         ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", norm="layer")
 
 
+def test_extra_down_norm_ablation_is_a_per_token_input_rescale():
+    # z is linear in x, so norming z after the down-projection (eps 0) is the
+    # normed layer run on x_t / RMS(z_t); and the layer forgets each token's scale
+    rng = np.random.default_rng(15)
+    p = rand_params(rng, n_s=1)
+    x = rng.standard_normal((5, 64))
+    both = ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", eps=0.0, norm="both")
+    z = x @ p["w_down"].T
+    xs = x / np.sqrt(np.mean(z ** 2, axis=1, keepdims=True))
+    rms = ref.forward(xs, P(p), k=2, n_shared=1, dtype="f64", eps=0.0)
+    assert np.array_equal(both["idx"], rms["idx"])
+    assert np.allclose(both["z"], rms["z"], rtol=1e-12, atol=1e-14)
+    assert np.allclose(both["y"], rms["y"], rtol=1e-10, atol=1e-12)
+    assert np.allclose(np.mean(both["z"] ** 2, axis=1), 1.0, rtol=1e-12)
+    c = np.array([0.01, 0.5, 3.0, 40.0, 1e3])[:, None]
+    scaled = ref.forward(x * c, P(p), k=2, n_shared=1, dtype="f64", eps=0.0, norm="both")
+    assert np.array_equal(scaled["idx"], both["idx"])
+    assert np.allclose(scaled["y"], both["y"], rtol=1e-10, atol=1e-12)
+    # without it a token's scale reaches the router (the sigmoid is not scale free)
+    plain = ref.forward(x * c, P(p), k=2, n_shared=1, dtype="f64", eps=0.0)
+    assert not np.allclose(plain["s"], ref.forward(x, P(p), k=2, n_shared=1, dtype="f64", eps=0.0)["s"])
+
+
 def test_gated_hidden_bounded_on_outlier_tokens():
     # the configured C2 outliers (x50) saturate the caps but never exceed beta1*beta2
     rng = np.random.default_rng(12)
