@@ -85,8 +85,12 @@ typedef enum { LMOE_GATE_TANH = 0, LMOE_GATE_CLIP = 1 } lmoe_gate;
  *   LMOE_NORM_RMS   v = rms_gain * u / sqrt(mean(u^2) + rms_eps): the layer as
  *                   the pages define it
  *   LMOE_NORM_NONE  v = u (rms_gain and rms_eps unused): the ablation
+ *   LMOE_NORM_BOTH  LMOE_NORM_RMS plus the norm the pages leave out after the
+ *                   down-projection: the stored z becomes
+ *                   z / sqrt(mean(z^2) + rms_eps) (unit gain) before routing,
+ *                   so the router and the experts both see it: the ablation
  * Any other value is rejected with LMOE_ERR_VALUE. */
-typedef enum { LMOE_NORM_RMS = 0, LMOE_NORM_NONE = 1 } lmoe_norm;
+typedef enum { LMOE_NORM_RMS = 0, LMOE_NORM_NONE = 1, LMOE_NORM_BOTH = 2 } lmoe_norm;
 
 /* Weights (device pointers, work dtype unless noted).
  *   w_down [L, d]        down-projection, no bias ([DD] §2: pure linear map)
@@ -164,7 +168,8 @@ int64_t lmoe_workspace_offset(const lmoe_dims *dims, int dtype, int region);
  *   y = v w_up^T                        (work dtype)
  * where softcap(x; b) = b tanh(x / b) and SiTU(x; b) = softcap(x; b) sigmoid(x);
  * with w->gate == LMOE_GATE_CLIP every softcap above is clamp(x; b) instead,
- * and with w->norm == LMOE_NORM_NONE, v = u (work dtype).
+ * with w->norm == LMOE_NORM_NONE, v = u (work dtype), and with LMOE_NORM_BOTH
+ * z is normed in place first (see lmoe_norm).
  * Arguments:
  *   x [T, d]      input tokens, work dtype
  *   y [T, d]      output, work dtype (may not alias x)

@@ -76,7 +76,8 @@ def forward(x, weights, k, y=None, topk_idx=None, topk_w=None, scores=None, work
     """y = LatentMoE(x) via lmoe_forward on the current stream; returns y.
 
     ``gate`` is "tanh" (SiTU-GLU) or "clip" (both caps a hard clip: the ablation);
-    ``norm`` is "rms" (the layer's one RMSNorm) or "none" (v = u: the ablation).
+    ``norm`` is "rms" (the layer's one RMSNorm), "none" (v = u) or "both" (an
+    extra RMSNorm on z after the down-projection); the last two are ablations.
 
     ``weights`` holds device tensors named as in include/lmoe.h (w_down, w_router,
     router_bias, router_logit_offset, w1, w2, w3, ws1, ws2, ws3, rms_gain, w_up).

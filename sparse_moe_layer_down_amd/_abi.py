@@ -33,7 +33,7 @@ class Weights(ctypes.Structure):
                 ("gate", ctypes.c_int32), ("norm", ctypes.c_int32)]
 
 GATES = {"tanh": 0, "clip": 1}  # lmoe_gate
-NORMS = {"rms": 0, "none": 1}   # lmoe_norm
+NORMS = {"rms": 0, "none": 1, "both": 2}   # lmoe_norm
 
 
 _lib = None

@@ -316,6 +316,11 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     a.M = T_; a.N = L; a.K = (int)d.d;
     LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
   }
+  if (w.norm == LMOE_NORM_BOTH) {  // the ablation: z normed in place before routing
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(d.T, 4), 65536);
+    hipLaunchKernelGGL(rmsnorm_rows_kernel<T>, dim3(blocks), dim3(256), 0, st, z, T_, L, w.rms_eps);
+    LMOE_TRY(hipGetLastError());
+  }
   // 2 s = sigmoid(z W_r^T + o)
   LMOE_MARK(1);
   {
@@ -432,7 +437,7 @@ static int forward_impl(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   if (!w) return LMOE_ERR_NULL;
   if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
   if (!(w->beta1 > 0.0f) || !(w->beta2 > 0.0f) || !(w->rms_eps >= 0.0f) || w->rms_eps == INFINITY ||
-      (w->gate != LMOE_GATE_TANH && w->gate != LMOE_GATE_CLIP) || (w->norm != LMOE_NORM_RMS && w->norm != LMOE_NORM_NONE))
+      (w->gate != LMOE_GATE_TANH && w->gate != LMOE_GATE_CLIP) || (w->norm != LMOE_NORM_RMS && w->norm != LMOE_NORM_NONE && w->norm != LMOE_NORM_BOTH))
     return LMOE_ERR_VALUE;
   if (dims->T == 0) return LMOE_OK;
   if (!x || !y || !workspace || !w->w_down || !w->w_router || !w->router_bias || !w->w1 || !w->w2 || !w->w3 ||

@@ -172,4 +172,35 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS *__restri
   }
 }
 
+// In-place row RMSNorm with unit gain, z[t] <- z[t] / sqrt(mean(z[t]^2) + eps):
+// the extra norm after the down-projection that the layer leaves out ("Kimi K3
+// Architecture Deep Dive" §2 keeps only the norm before the up-projection), for
+// its ablation.  One wave per row, four rows per work-group, rows strided over
+// the grid; each lane reads its 8-element chunks twice (the second read hits
+// the caches), since this runs only in the ablation.  L is a multiple of 8.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(T *__restrict__ z, int T_, int L, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int nch = L / 8;
+  for (int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); t < T_; t += (int64_t)gridDim.x * 4) {
+    T *row = z + t * L;
+    float ss = 0.0f;
+    for (int ch = lane; ch < nch; ch += 64) {
+      float a[8];
+      load8_f32(row + ch * 8, a);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += a[i] * a[i];
+    }
+    ss = wave_sum(ss);
+    const float rstd = 1.0f / sqrtf(ss / (float)L + eps);
+    for (int ch = lane; ch < nch; ch += 64) {
+      float a[8];
+      load8_f32(row + ch * 8, a);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] *= rstd;
+      store8(row + ch * 8, a);
+    }
+  }
+}
+
 }  // namespace lmoe

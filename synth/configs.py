@@ -33,7 +33,7 @@ class Config:
     beta1: float = 4.0
     beta2: float = 25.0
     gate: str = "tanh"  # expert caps: "tanh" softcap, or "clip" for the hard-clip ablation
-    norm: str = "rms"   # the norm before the up-projection: "rms", or "none" for its ablation
+    norm: str = "rms"   # "rms" (the layer's norm); "none" or "both" (an extra norm on z) for ablations
     eps: float = 1e-6
 
     def flops_per_token(self):

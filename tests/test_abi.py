@@ -93,7 +93,7 @@ def test_other_errors():
     assert call(d, fake_weights(beta1=math.nan)) == -7
     assert call(d, fake_weights(gate=2)) == -7
     assert call(d, fake_weights(gate=-1)) == -7
-    assert call(d, fake_weights(norm=2)) == -7
+    assert call(d, fake_weights(norm=3)) == -7
     assert call(d, fake_weights(rms_eps=-1.0)) == -7
     assert lib().lmoe_forward(None, ctypes.byref(fake_weights()), 1, FAKE, FAKE, None, None, None, FAKE, 1, None) == -1
 
