@@ -91,3 +91,21 @@ def test_dispatch_brute_force():
         seg = row_token[offs[e]:offs[e + 1]]
         assert np.all(np.diff(seg) > 0)
         assert np.all(idx[seg, row_slot[offs[e]:offs[e + 1]]] == e)
+
+
+def test_logit_offset_enters_before_the_sigmoid():
+    """router_scores with a per-expert logit offset o: s = sigmoid(z W_r^T + o).
+
+    With W_r = 0 the scores are exactly sigmoid(o); with logits (ln 3, 0) and
+    o = (-ln 3, ln 3) they are (1/2, 3/4).  An offset added after the sigmoid
+    would give 3/4 - ln 3 and 1/2 + ln 3 instead, and a dropped offset (3/4, 1/2)."""
+    import math
+    o = np.array([-2.0, -0.5, 0.0, 0.75, 3.0])
+    s = ref.router_scores(np.ones((3, 4)), np.zeros((5, 4)), o)
+    want = 1.0 / (1.0 + np.exp(-o))
+    assert np.array_equal(s, np.broadcast_to(want, (3, 5)))
+    z = np.array([[math.log(3), 0.0]])
+    w_r = np.array([[1.0, 0.0], [0.0, 1.0]])
+    s = ref.router_scores(z, w_r, np.array([-math.log(3), math.log(3)]))
+    assert s == pytest.approx(np.array([[0.5, 0.75]]), rel=1e-15)
+    assert ref.router_scores(z, w_r) == pytest.approx(np.array([[0.75, 0.5]]), rel=1e-15)
