@@ -5,7 +5,7 @@ One step = one lmoe_forward over one batch of the K3-shaped prefill workload
 expert hidden 512, bf16, every weight resident in HBM), seeded synthetic
 inputs already in device memory.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config C2] [--no-cpu-baseline] [--no-qb-protocol] [--no-decode]
+  python bench.py [--steps K] [--warmup W] [--config C2] [--no-cpu-baseline] [--only all|prefill|decode|qb|calib]
 """
 import argparse
 import json
@@ -28,25 +28,25 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-qb-protocol", action="store_true",
-                    help="skip the 20-step Quantile Balancing run on the skewed-routing workload")
-    ap.add_argument("--no-decode", action="store_true",
-                    help="skip the decode-shaped (T=64) forwards on the same weights")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after the timed steps, copy 1 GiB device-to-device once (a plain copy kernel of known "
-                         "size whose memory counters calibrate the byte counters of a profiler run)")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "qb", "calib"), default="all",
+                    help="run one part alone (for profiler runs of one workload): the timed prefill forwards, "
+                         "the decode forwards, the Quantile Balancing protocol, or 'calib': a single 1 GiB "
+                         "device-to-device copy (a plain copy of known size, whose memory counters calibrate "
+                         "the byte counters of the other profiler runs), nothing else")
     return ap.parse_args()
 
 
 def experts_w12_bytes(cfg, counts):
     """Algorithmic HBM bytes of the W1/W2 + SiTU-GLU grouped GEMM (routed and shared experts)
-    for one launch: each touched routed expert's and each shared expert's W1 and W2 once, each
-    expert row's latent input once, each gated hidden row written once."""
+    for one launch: each touched routed expert's and each shared expert's W1 and W2 once, the
+    latent z of every token once, the gated hidden of every expert row written once.  (Re-reads
+    of a token's latent by its other experts are not algorithmic: they are what the kernel
+    should serve from the caches.)"""
     es = 2 if cfg.dtype == "bf16" else 4
     touched = int((counts > 0).sum())
     rows = int(counts.sum()) + cfg.n_shared * cfg.T
-    return (touched + cfg.n_shared) * 2 * cfg.D * cfg.L * es + rows * (cfg.L + cfg.D) * es, touched
+    return (touched + cfg.n_shared) * 2 * cfg.D * cfg.L * es + cfg.T * cfg.L * es + rows * cfg.D * es, touched
 
 
 def qb_protocol(w, dev, lmoe, synth):
@@ -148,24 +148,157 @@ def decode_protocol(w, dev, lmoe, synth, steps):
             "cache_state": "512 MB written between forwards (MALL and L2 hold no weights at the start)"}
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, n_tok):
-    """Time the oracle (as it stands) on the first n_tok tokens of the same workload."""
+    """Time the oracle (as it stands) on bounded samples of each workload, on the host cores.
+
+    Headline: the first n_tok tokens of the prefill workload.  Beside it: the tiny fp32
+    workload in full, the first 512 tokens of the small bf16 one, the decode workload in full,
+    and for the skewed workload the router + Quantile Balancing path (down-projection, scores,
+    histogram, bias solve) on the first 256 tokens of each of its 21 batches plus one forward
+    of 64 tokens.  Weight synthesis is done before each timed call (the oracle regenerates
+    expert weights on demand; the cache holds them)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     import synth
     from oracle import ref
-    P = synth.HostParams(cfg, cache=True)
-    x = P.x_rows(np.arange(n_tok))
-    # input synthesis (not timed): generate the weights the sample touches
-    pre = ref.forward(x, P, cfg.k, cfg.n_shared, cfg.dtype, cfg.beta1, cfg.beta2, cfg.eps)
+    cache = {}
+    per = {}
+
+    def fwd(c, rows, step=None, P=None, synthesise=True):
+        P = P or synth.HostParams(c, cache=cache)
+        x = P.x_rows(rows, step=step)
+        if synthesise:  # untimed: generate the weights the sample touches into the cache
+            ref.forward(x, P, c.k, c.n_shared, c.dtype, c.beta1, c.beta2, c.eps)
+        t0 = time.perf_counter()
+        ref.forward(x, P, c.k, c.n_shared, c.dtype, c.beta1, c.beta2, c.eps)
+        dt = time.perf_counter() - t0
+        return {"tokens_per_s": len(rows) / dt, "gflops": len(rows) * c.flops_per_token() / dt / 1e9,
+                "seconds": dt}
+
+    main_cfg = cfg
+    head = fwd(main_cfg, np.arange(n_tok))
+    for name, ntok in (("C0", None), ("C1", 512), ("C3", None)):
+        c = synth.get_config(name)
+        # the decode workload shares the prefill weights, already synthesised above
+        r = fwd(c, np.arange(c.T if ntok is None else ntok), synthesise=name != "C3")
+        r["sample"] = f"{'all' if ntok is None else 'first ' + str(ntok)} of {c.T} tokens, full forward"
+        per[name] = r
+    c4 = synth.get_config("C4")
+    P4 = synth.HostParams(c4, cache=cache)
+    w_down, w_r, off = P4.w_down(), P4.w_router(), P4.logit_offset()
+    rows = np.arange(256)
+    xs = [P4.x_rows(rows, step=t) for t in range(c4.qb_steps + 1)]
     t0 = time.perf_counter()
-    ref.forward(x, P, cfg.k, cfg.n_shared, cfg.dtype, cfg.beta1, cfg.beta2, cfg.eps)
+    bias = np.zeros(c4.n, np.float32)
+    for x in xs:
+        z = ref.round_to(x @ w_down.T, c4.dtype)
+        s = ref.router_scores(z, w_r, off)
+        _, bias = ref.qb_update(s.astype(np.float32), c4.nbins, c4.k, bias=bias)
     dt = time.perf_counter() - t0
+    r4 = fwd(c4, np.arange(64), step=0, P=P4, synthesise=False)
+    per["C4"] = {"router_qb_tokens_per_s": len(xs) * rows.size / dt, "router_qb_seconds": dt,
+                 "forward": r4,
+                 "sample": f"router + QB on the first {rows.size} tokens of each of the {len(xs)} batches; "
+                           "full forward of the first 64 tokens of batch 0"}
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n_tok} tokens of the {cfg.name} workload (T={cfg.T}), NumPy fp64 oracle, "
-                      f"{int((pre['counts'] > 0).sum())} experts touched; weight synthesis excluded; "
-                      f"{dt:.2f} s"}
+    return {"value": head["tokens_per_s"], "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_tok} tokens of the {main_cfg.name} workload (T={main_cfg.T}), NumPy fp64 oracle, "
+                      f"weight synthesis excluded; {head['seconds']:.2f} s",
+            "cpu_model": _cpu_model(), "gflops": head["gflops"], "per_config": per}
+
+
+def other_configs(lmoe, synth, dev, steps=50):
+    """GPU time of the tiny fp32 and the small bf16 workloads (whole forward, events on the
+    library's stream, median of `steps` forwards after warm-up)."""
+    import numpy as np
+    import torch
+    out = {}
+    for name in ("C0", "C1"):
+        c = synth.get_config(name)
+        w = synth.device_params(c, device=dev)
+        x = w.pop("x")
+        ws = lmoe.make_workspace(lmoe.dims_of(x, w, c.k), x.dtype, dev)
+        y = torch.empty_like(x)
+        for _ in range(5):
+            lmoe.forward(x, w, c.k, y=y, workspace=ws)
+        times = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lmoe.forward(x, w, c.k, y=y, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        out[name] = {"T": c.T, "dtype": c.dtype, "ms_per_forward_median": ms, "tokens_per_s": c.T / (ms * 1e-3),
+                     "tflops": c.flops_per_token() * c.T / (ms * 1e-3) / 1e12}
+        del w, x, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def measured_ceilings(dev):
+    """Ceilings measured on this GPU beside the datasheet peaks: a 1 GiB device-to-device copy
+    (torch's copy kernel; read + write bytes over its time) and the vendor library's bf16 GEMM
+    (torch.matmul, 8192 x 7168 x 3584, B stored [N, K] as the layer's weights)."""
+    import numpy as np
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    copy_gbs = 2 * (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9
+    del src, dst
+    a = torch.randn(8192, 3584, device=dev).to(torch.bfloat16)
+    b = torch.randn(7168, 3584, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        a @ b.t()
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        a @ b.t()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    gemm_tf = 2 * 8192 * 7168 * 3584 / (float(np.median(ts)) * 1e-3) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_1GiB_GBps": copy_gbs, "vendor_bf16_gemm_8192x7168x3584_TFLOPs": gemm_tf}
+
+
+def profile_avg_ms(cfg_name):
+    """Average duration (ms) of the expert W1/W2 kernel in the committed kernel-trace summary
+    of this workload, if that summary was taken on the sources being run; else None."""
+    from sparse_moe_layer_down_amd import profsum
+    path = os.path.join(ROOT, "profiles", f"{cfg_name.lower()}_prefill_kernel_trace.md")
+    if not os.path.exists(path):
+        return None
+    sha, avg = None, None
+    for line in open(path):
+        if line.startswith("Kernel-source SHA-256:"):
+            sha = line.split("`")[1]
+        elif "expert W1/W2 + SiTU-GLU" in line and avg is None:
+            avg = float(line.split("|")[4]) / 1e3
+    return avg if sha == profsum.source_sha256() else None
 
 
 def main():
@@ -179,15 +312,44 @@ def main():
     import sparse_moe_layer_down_amd as lmoe
     import synth
 
-    cfg = synth.get_config(args.config)
     dev = torch.device("cuda:0")
+    if args.only == "calib":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": 1 << 30}))
+        return
+
+    cfg = synth.get_config(args.config)
     w = synth.device_params(cfg, device=dev)
     x = w.pop("x")
     dims = lmoe.dims_of(x, w, cfg.k)
     ws = lmoe.make_workspace(dims, x.dtype, dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream(dev)
+    out = {}
+    if args.only in ("all", "prefill"):
+        out = prefill(args, cfg, w, x, y, ws, dims, stream, lmoe, np, torch)
+    if args.only in ("all", "decode") and cfg.name == "C2":
+        out["decode"] = decode_protocol(w, dev, lmoe, synth, steps=20)
+    if args.only in ("all", "qb") and cfg.name == "C2":
+        del ws
+        torch.cuda.empty_cache()
+        out["qb_protocol"] = qb_protocol(w, dev, lmoe, synth)
+    if args.only == "all":
+        del w, x, y
+        torch.cuda.empty_cache()
+        out["other_configs"] = other_configs(lmoe, synth, dev)
+        out["measured_ceilings"] = measured_ceilings(dev)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
+    print(json.dumps(out))
 
+
+def prefill(args, cfg, w, x, y, ws, dims, stream, lmoe, np, torch):
+    """The timed forwards of the headline workload and the roofline of its dominant kernel."""
     def step(ev=None):
         lmoe.forward(x, w, cfg.k, y=y, workspace=ws, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps,
                      stage_events=ev)
@@ -228,16 +390,8 @@ def main():
         stage_ms += np.array([ev[j].elapsed_time(ev[j + 1]) for j in range(lmoe.N_STAGES)])
     stage_ms /= args.steps
 
-    if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     counts = lmoe.workspace_view(ws, dims, x.dtype, "counts").cpu().numpy()
-    # HBM traffic of the routed W1/W2 launch from the committed rocprofv3 counter summary, if it was
+    # HBM traffic of the W1/W2 launch from the committed rocprofv3 counter summary, if it was
     # taken on these exact kernel sources and this workload
     from sparse_moe_layer_down_amd import profsum
     tb, sha = profsum.read_counters(os.path.join(ROOT, "profiles", f"experts_w12_{cfg.name.lower()}_hbm_counters.md"))
@@ -246,8 +400,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     w12_bytes, touched = experts_w12_bytes(cfg, counts)
     achieved = w12_bytes / (w12_ms * 1e-3) / 1e9
-
-    out = {
+    return {
         "metric": "LatentMoE fwd tokens/s + % bf16 MFMA peak (d=7168, 896c16) on 1 MI355X",
         "value": cfg.T / (ms * 1e-3),
         "unit": "tokens/s",
@@ -268,18 +421,11 @@ def main():
         "stage_ms": {name: float(v) for name, v in zip(lmoe.STAGES, stage_ms)},
         "roofline": {"kernel": "expert W1/W2 + SiTU-GLU grouped GEMM (routed + shared)", "bound": "hbm",
                      "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic, "algorithmic_bytes": w12_bytes, "experts_touched": touched,
-                     "avg_ms": w12_ms},
+                     "traffic": traffic,
+                     "traffic_over_algorithmic": None if traffic is None else traffic / w12_bytes,
+                     "algorithmic_bytes": w12_bytes, "experts_touched": touched, "avg_ms": w12_ms,
+                     "profile_avg_ms": profile_avg_ms(cfg.name)},
     }
-    if not args.no_decode and cfg.name == "C2":
-        out["decode"] = decode_protocol(w, dev, lmoe, synth, steps=20)
-    if not args.no_qb_protocol and cfg.name == "C2":
-        del ws
-        torch.cuda.empty_cache()
-        out["qb_protocol"] = qb_protocol(w, dev, lmoe, synth)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
-    print(json.dumps(out))
 
 
 if __name__ == "__main__":

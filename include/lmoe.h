@@ -50,11 +50,11 @@ typedef enum {
  * z, a, v, y.  Accumulation, router scores, routing weights, the aggregated
  * latent and the norm statistics are always fp32.  The k routed contributions
  * g_ie * (a W3_e^T) of a token are staged in the workspace before their fp32
- * sum: in fp16 when the work dtype is bf16 (an element beyond +-65504 becomes
- * +-inf and so shows in y; the gated hidden a is bounded by beta1 * beta2, so
- * this needs a W3 row whose absolute values sum past 65504 / (beta1 * beta2);
- * with either cap at +inf the hidden is unbounded and no such bound holds),
- * in fp32 when it is fp32. */
+ * sum: in fp16 when the work dtype is bf16 and both caps are finite (an
+ * element beyond +-65504 becomes +-inf and so shows in y; the gated hidden a is
+ * bounded by beta1 * beta2, so this needs a W3 row whose absolute values sum
+ * past 65504 / (beta1 * beta2)), in fp32 when either cap is +inf (the hidden is
+ * then unbounded) and when the work dtype is fp32. */
 typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
 
 /* Layer dimensions ([DD] §2: d -> d/2 -> D -> d/2 -> d, k of n routed experts;
@@ -146,8 +146,9 @@ typedef enum {
   LMOE_WS_ROW_SLOT = 4,  /* [T*k] int32: dispatched row of (token t, slot r) at t*k+r      */
   LMOE_WS_HIDDEN = 5,    /* [T*(k+n_shared), D] work dtype: gated hidden a of each row     */
   LMOE_WS_ROWS = 6,      /* [T*(k+n_shared), L] staged expert outputs: routed rows scaled
-                                   by g, shared rows by 1; fp16 for bf16 work dtype, fp32
-                                   for fp32                                               */
+                                   by g, shared rows by 1; fp16 for bf16 work dtype with
+                                   both caps finite, else fp32 (the region is sized for
+                                   fp32 either way)                                       */
   LMOE_WS_V = 7          /* [T, L] work dtype: v = RMSNorm(u)                             */
 } lmoe_ws_region;
 

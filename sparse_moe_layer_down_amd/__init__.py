@@ -43,15 +43,18 @@ def make_workspace(dims, dtype, device="cuda"):
     return torch.empty(max(workspace_size(dims, dtype), 256), dtype=torch.uint8, device=device)
 
 
-def workspace_view(workspace, dims, dtype, region):
-    """A typed view of one inspectable workspace region (see lmoe_ws_region)."""
+def workspace_view(workspace, dims, dtype, region, capped=True):
+    """A typed view of one inspectable workspace region (see lmoe_ws_region).
+
+    ``capped``: both expert caps finite (the staged rows are fp16 for bf16 work
+    dtype only then, fp32 otherwise)."""
     code = _dtype_code(dtype)
     off = int(lib().lmoe_workspace_offset(dims, code, WS_REGIONS[region]))
     if off < 0:
         raise ValueError(region)
     T, L, n, k, D, ns = dims.T, dims.L, dims.n, dims.k, dims.D, dims.n_shared
     R = T * (k + ns)  # expert rows: dispatched, then each shared expert's T
-    stage_dt = torch.float16 if dtype == torch.bfloat16 else torch.float32
+    stage_dt = torch.float16 if (dtype == torch.bfloat16 and capped) else torch.float32
     shapes = {"z": ((T, L), dtype), "counts": ((n,), torch.int32), "offs": ((n + 1,), torch.int32),
               "row_token": ((R,), torch.int32), "row_slot": ((T * k,), torch.int32),
               "hidden": ((R, D), dtype), "rows": ((R, L), stage_dt), "v": ((T, L), dtype)}

@@ -11,13 +11,14 @@
 //   1 gemm   z = x W_down^T
 //   2 gemm   s = sigmoid(z W_r^T + o)                 (fp32 scores)
 //   3 topk   biased top-k, routing weights g
-//   4 perm   chunk masks -> scan (offsets, tile table) -> scatter
-//   5 gemm   shared experts' gated hidden (dense, SiTU-GLU epilogue)
-//   6 gemm   routed experts' gated hidden (grouped, gathered rows, SiTU-GLU)
-//   7 gemm   shared W3 -> u_shared (fp32)
-//   8 gemm   routed W3, scaled by g -> one fp32 row per (token, slot)
-//   9 norm   u = u_shared + sum of the token's k rows; v = RMSNorm(u)
-//  10 gemm   y = v W_up^T
+//   4 perm   chunk masks -> scan (offsets, tile tables) -> scatter
+//   5 gemm   gated hidden of every expert row, one grouped launch: routed
+//            experts on their gathered rows, shared experts on all tokens
+//            (SiTU-GLU epilogue)
+//   6 gemm   W3 of every expert row scaled by g (1 for shared rows) -> one
+//            staged row per expert row (fp16, or fp32 when uncapped / fp32)
+//   7 norm   u = sum of the token's staged rows; v = RMSNorm(u)
+//   8 gemm   y = v W_up^T
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -131,7 +132,7 @@ WsLayout layout(const lmoe_dims &d, int dtype) {
   sz[R_SLOT_ROW] = d.T * d.k * 4;
   sz[R_HIDDEN] = expert_rows(d) * d.D * es;
   // staged expert outputs, one row per expert row: fp16 (bf16 inputs) or fp32
-  sz[R_ROWS] = expert_rows(d) * d.L * (es == 2 ? 2 : 4);
+  sz[R_ROWS] = expert_rows(d) * d.L * 4;  // fp32 rows at most (fp16 when bf16 and both caps finite)
   sz[R_V] = d.T * d.L * es;
   sz[R_SCORES] = d.T * d.n * 4;
   sz[R_IDX] = d.T * d.k * 4;
@@ -268,6 +269,8 @@ hipError_t launch_dense(GemmArgs a, float *part, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <typename X> struct TypeTag { using type = X; };
+
 GemmArgs gargs() {
   GemmArgs a;
   memset(&a, 0, sizeof(a));
@@ -299,9 +302,12 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   int32_t *ntiles = (int32_t *)(ws + Lw.off[R_NTILES]);
   float *row_w = (float *)(ws + Lw.off[R_ROW_W]);
   // staged expert outputs, one row per expert row: fp16 for bf16 inputs
-  // (11-bit mantissa, summed in fp32 by the combine), fp32 for fp32 inputs
-  using TS = typename std::conditional<sizeof(T) == 2, f16, float>::type;
-  TS *ystage = (TS *)(ws + Lw.off[R_ROWS]);
+  // (11-bit mantissa, summed in fp32 by the combine) while both caps are
+  // finite, since the gated hidden is then bounded by beta1 * beta2; fp32 for
+  // fp32 inputs and for the uncapped ablation (either cap +inf), whose hidden
+  // has no bound.  The region is sized for fp32 rows either way.
+  unsigned char *ystage = ws + Lw.off[R_ROWS];
+  const bool wide_stage = std::isinf(w.beta1) || std::isinf(w.beta2);
   float *part = (float *)(ws + Lw.off[R_PART]);
   const int T_ = (int)d.T, n = (int)d.n, k = (int)d.k, L = (int)d.L, D = (int)d.D, ns = (int)d.n_shared;
   hipError_t e;
@@ -374,31 +380,43 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
       else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU, true, true>(a, st)));
     }
   }
-  // 6 W3 of every expert row, scaled by its weight (g, or 1 for shared rows)
-  LMOE_MARK(5);
-  {
-    GemmArgs a = gargs();
-    a.A = hid; a.lda = D; a.B = w.w3; a.Bsh = w.ws3; a.n_routed = n; a.ldb = D; a.b_group_stride = (int64_t)L * D;
-    a.C = ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles2; a.ntiles = ntiles + 1;
-    a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w;
-    a.sched = ntiles + 2 + SCHED_COUNTERS;
-    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, TS, EPI_ROWSCALE, false, true>(a, st)));
-    else LMOE_TRY((launch_gemm<CfgW3, T, TS, EPI_ROWSCALE, false, true>(a, st)));
-  }
-  // 7 combine + RMSNorm
-  LMOE_MARK(6);
-  {
-    const int nch8 = L / 8;
-    const T *gain = (const T *)w.rms_gain;
-    const int no_norm = w.norm == LMOE_NORM_NONE;
-    const dim3 wg((unsigned)cdiv(d.T, 4));
-    if (nch8 <= 64) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 1>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
-    else if (nch8 <= 128) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 2>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
-    else if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 4>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
-    else if (nch8 <= 448) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 7>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
-    else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 8>), wg, dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
-    else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 4>), dim3(T_), dim3(256), 0, st, ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
-    LMOE_TRY(hipGetLastError());
+  // 6 + 7: W3 into the staged rows, then the combine reading them, for one
+  // staging type
+  auto w3_combine = [&](auto tag) -> hipError_t {
+    using TS = typename decltype(tag)::type;
+    // 6 W3 of every expert row, scaled by its weight (g, or 1 for shared rows)
+    LMOE_MARK(5);
+    {
+      GemmArgs a = gargs();
+      a.A = hid; a.lda = D; a.B = w.w3; a.Bsh = w.ws3; a.n_routed = n; a.ldb = D; a.b_group_stride = (int64_t)L * D;
+      a.C = (TS *)ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles2; a.ntiles = ntiles + 1;
+      a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w;
+      a.sched = ntiles + 2 + SCHED_COUNTERS;
+      if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, TS, EPI_ROWSCALE, false, true>(a, st)));
+      else LMOE_TRY((launch_gemm<CfgW3, T, TS, EPI_ROWSCALE, false, true>(a, st)));
+    }
+    // 7 combine + RMSNorm
+    LMOE_MARK(6);
+    {
+      const int nch8 = L / 8;
+      const T *gain = (const T *)w.rms_gain;
+      const int no_norm = w.norm == LMOE_NORM_NONE;
+      const dim3 wg((unsigned)cdiv(d.T, 4));
+      if (nch8 <= 64) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 1>), wg, dim3(256), 0, st, (const TS *)ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+      else if (nch8 <= 128) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 2>), wg, dim3(256), 0, st, (const TS *)ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+      else if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 4>), wg, dim3(256), 0, st, (const TS *)ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+      else if (nch8 <= 448) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 7>), wg, dim3(256), 0, st, (const TS *)ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+      else if (nch8 <= 512) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, TS, 8>), wg, dim3(256), 0, st, (const TS *)ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+      else hipLaunchKernelGGL((combine_rmsnorm_kernel<T, TS, 4>), dim3(T_), dim3(256), 0, st, (const TS *)ystage, slot_row, gain, v, T_, L, k, ns, w.rms_eps, no_norm);
+      LMOE_TRY(hipGetLastError());
+    }
+    return hipSuccess;
+  };
+  if constexpr (sizeof(T) == 2) {
+    if (wide_stage) LMOE_TRY(w3_combine(TypeTag<float>{}));
+    else LMOE_TRY(w3_combine(TypeTag<f16>{}));
+  } else {
+    LMOE_TRY(w3_combine(TypeTag<float>{}));
   }
   // 8 y = v W_up^T
   LMOE_MARK(7);

@@ -2,7 +2,7 @@
 under profiles/.
 
   python -m sparse_moe_layer_down_amd.profsum trace  <kernel_stats.csv> <out.md> "<command>" ["<title>"]
-  python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <out.md> "<commands>" ["<title>"] [<kernel_stats.csv>]
+  python -m sparse_moe_layer_down_amd.profsum counters <fetch_dir> <write_dir> <calib_fetch_dir> <calib_write_dir> <out.md> "<commands>" ["<title>"] [<kernel_stats.csv>]
   python -m sparse_moe_layer_down_amd.profsum mfma <pmc_dir> <out.md> "<command>" ["<title>"]
   python -m sparse_moe_layer_down_amd.profsum lds <pmc_dir> <out.md> "<command>" ["<title>"]
 
@@ -10,8 +10,8 @@ The counters summary records, for every kernel of the forward, the mean
 FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as the counters read), with a
 kernel trace of the same workload also the achieved GB/s (scaled bytes over the
 kernel's average duration in that trace), the same
-counters for the 1 GiB device copy that `bench.py --copy-calibration` runs, the
-calibration factors they give, and a SHA-256 of the library's kernel sources.
+counters for the 1 GiB device copy that `bench.py --only calib` runs in a
+process of its own, the calibration factors they give, and a SHA-256 of the library's kernel sources.
 `bench.py` reports the expert W1/W2 kernel's traffic from this file only while
 that hash matches the sources it runs.
 """
@@ -91,12 +91,14 @@ def trace(stats_csv, out, cmd, title=PREFILL):
                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |\n")
 
 
-def _means(d, counter):
+def _means(d, counter, by_grid=False):
+    """Mean value of `counter` per kernel (per (kernel, grid size) with by_grid) and dispatch counts."""
     vals = {}
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] == counter:
-                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                key = (r["Kernel_Name"], int(r.get("Grid_Size") or 0)) if by_grid else r["Kernel_Name"]
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
 
 
@@ -107,16 +109,28 @@ def _durations(stats_csv):
     return {label(r["Name"]): float(r["AverageNs"]) * 1e-9 for r in csv.DictReader(open(stats_csv))}
 
 
-def counters(fetch_dir, write_dir, out, cmd, title=PREFILL, stats_csv=None):
+def calibration(calib_fetch, calib_write):
+    """KiB the counters read for the 1 GiB device copy of `bench.py --only calib`
+    (run alone in its own profiled process, so every copy dispatch there is that
+    copy): (fetch KiB, write KiB), summed over its dispatches."""
+    fetch, nf = _means(calib_fetch, "FETCH_SIZE")
+    write, nw = _means(calib_write, "WRITE_SIZE")
+    cf = sum(v * nf[k] for k, v in fetch.items() if "copyBuffer" in k)
+    cw = sum(v * nw[k] for k, v in write.items() if "copyBuffer" in k)
+    if cf <= 0 or cw <= 0:
+        raise SystemExit("no device copy in the calibration runs")
+    return cf, cw
+
+
+def counters(fetch_dir, write_dir, out, cmd, title=PREFILL, stats_csv=None, calib_fetch=None, calib_write=None):
+    """Counter summary of one workload.  The calibration copy comes from its own
+    profiled runs (calib_fetch / calib_write directories).  Rows are per
+    (kernel, grid size), so launches of one kernel with different grids (e.g.
+    the QB histogram at 1000 and at 10000 bins) stay apart."""
     dur = _durations(stats_csv)
-    fetch, nf = _means(fetch_dir, "FETCH_SIZE")
-    write, _ = _means(write_dir, "WRITE_SIZE")
-    copy = [k for k in fetch if "copyBuffer" in k]
-    if not copy:
-        raise SystemExit("no calibration copy in the fetch pass (run bench.py with --copy-calibration)")
-    # the 1 GiB copy may run as several dispatches: sum them
-    cf = fetch[copy[0]] * nf[copy[0]]
-    cw = write[copy[0]] * nf[copy[0]]
+    fetch, nf = _means(fetch_dir, "FETCH_SIZE", by_grid=True)
+    write, _ = _means(write_dir, "WRITE_SIZE", by_grid=True)
+    cf, cw = calibration(calib_fetch, calib_write)
     ff = COPY_BYTES / (cf * 1024.0)
     wf = COPY_BYTES / (cw * 1024.0)
     with open(out, "w") as f:
@@ -124,28 +138,29 @@ def counters(fetch_dir, write_dir, out, cmd, title=PREFILL, stats_csv=None):
         f.write(f"source_sha256: {source_sha256()}\n")
         f.write(f"fetch_factor: {ff:.4f}\nwrite_factor: {wf:.4f}\n\n")
         f.write("FETCH_SIZE and WRITE_SIZE are in KiB per dispatch as rocprofv3 reports them. The factors scale them to "
-                f"bytes moved: a 1 GiB device-to-device copy read {cf:.0f} KiB (FETCH_SIZE) and wrote {cw:.0f} KiB "
-                "(WRITE_SIZE), summed over its dispatches.\n\n")
+                f"bytes moved: a 1 GiB device-to-device copy, profiled alone in its own process, read {cf:.0f} KiB "
+                f"(FETCH_SIZE) and wrote {cw:.0f} KiB (WRITE_SIZE), summed over its dispatches.\n\n")
         f.write(f"Commands (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
         if dur:
             f.write("GB/s = scaled traffic over the kernel's average duration in the kernel trace of the same "
                     "workload (a separate run of the same command without counters).\n\n")
-        f.write("| kernel | stage | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled traffic (GB) | GB/s |\n"
-                "|---|---|---|---|---|---|---|\n")
-        for k in sorted(fetch, key=lambda k: -fetch[k]):
+        f.write("| kernel | stage | grid | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled traffic (GB) | GB/s |\n"
+                "|---|---|---|---|---|---|---|---|\n")
+        for key in sorted(fetch, key=lambda k: -fetch[k]):
+            k, grid = key
             lab = label(k)
-            st = "1 GiB calibration copy" if k in copy else stage(lab, k)
+            st = "device copy" if "copyBuffer" in k else stage(lab, k)
             if st.startswith("input synthesis"):
                 continue
-            w = write.get(k, 0.0)
-            gb = (fetch[k] * ff + w * wf) * 1024 / 1e9
-            key = "experts_w12: " if st == "expert W1/W2 + SiTU-GLU" else ""
-            rate = f"{gb / dur[lab]:.0f}" if dur.get(lab) and k not in copy else ""
-            f.write(f"| `{lab}` | {key}{st} | {nf[k]} | {fetch[k]:.0f} | {w:.0f} | {gb:.3f} | {rate} |\n")
-        rw = [k for k in fetch if stage(label(k), k) == "expert W1/W2 + SiTU-GLU"]
-        if rw:
-            k = rw[0]
-            tb = (fetch[k] * ff + write.get(k, 0.0) * wf) * 1024
+            w = write.get(key, 0.0)
+            gb = (fetch[key] * ff + w * wf) * 1024 / 1e9
+            tag = "experts_w12: " if st == "expert W1/W2 + SiTU-GLU" else ""
+            rate = f"{gb / dur[lab]:.0f}" if dur.get(lab) and "copyBuffer" not in k else ""
+            f.write(f"| `{lab}` | {tag}{st} | {grid} | {nf[key]} | {fetch[key]:.0f} | {w:.0f} | {gb:.3f} | {rate} |\n")
+        rw = [key for key in fetch if stage(label(key[0]), key[0]) == "expert W1/W2 + SiTU-GLU"]
+        if len(rw) == 1:
+            key = rw[0]
+            tb = (fetch[key] * ff + write.get(key, 0.0) * wf) * 1024
             f.write(f"\nexperts_w12_traffic_bytes: {tb:.0f}\n")
 
 
@@ -226,7 +241,9 @@ if __name__ == "__main__":
     if len(sys.argv) >= 5 and sys.argv[1] == "trace":
         trace(*sys.argv[2:6])
     elif len(sys.argv) >= 6 and sys.argv[1] == "counters":
-        counters(*sys.argv[2:8])
+        # counters <fetch_dir> <write_dir> <calib_fetch_dir> <calib_write_dir> <out.md> "<cmd>" ["<title>"] [<stats.csv>]
+        a = sys.argv[2:]
+        counters(a[0], a[1], a[4], a[5], *(a[6:8]), calib_fetch=a[2], calib_write=a[3])
     elif len(sys.argv) >= 5 and sys.argv[1] == "mfma":
         mfma(*sys.argv[2:6])
     elif len(sys.argv) >= 5 and sys.argv[1] == "lds":

@@ -41,12 +41,14 @@ class HostParams:
 
     Expert weights are generated on demand; ``cache=True`` keeps the compact
     (bf16 bit / fp32) form of what was generated so later calls only convert.
+    ``cache`` may also be a dict, shared by workloads with the same weights
+    (same w_seed, shapes and dtype).
     """
 
     def __init__(self, cfg, cache=False):
         self.cfg = cfg
         self.bf16 = cfg.dtype == "bf16"
-        self._cache = {} if cache else None
+        self._cache = cache if isinstance(cache, dict) else ({} if cache else None)
 
     def _gen(self, name, tid, count, start, std):
         key = (name, start, count)

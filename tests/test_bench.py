@@ -22,15 +22,16 @@ def test_more_than_one_gpu_is_refused():
 
 def test_w12_algorithmic_bytes():
     """Each touched routed expert's and each shared expert's W1 and W2 once
-    (2 * D * L bf16 values), each expert row's latent input and gated hidden once."""
+    (2 * D * L bf16 values), each token's latent once, each expert row's gated
+    hidden once."""
     cfg = synth.get_config("C2")
     counts = np.full(cfg.n, cfg.T * cfg.k // cfg.n)
     counts[:5] = 0                                   # five experts receive no token
     b, touched = bench.experts_w12_bytes(cfg, counts)
     rows = int(counts.sum()) + cfg.n_shared * cfg.T
     assert touched == cfg.n - 5
-    assert b == (touched + cfg.n_shared) * 2 * cfg.D * cfg.L * 2 + rows * (cfg.L + cfg.D) * 2
+    assert b == (touched + cfg.n_shared) * 2 * cfg.D * cfg.L * 2 + cfg.T * cfg.L * 2 + rows * cfg.D * 2
     full = np.full(cfg.n, cfg.T * cfg.k // cfg.n)
     full[: (cfg.T * cfg.k) % cfg.n] += 1             # exactly T * k dispatched rows, every expert touched
     b2, t2 = bench.experts_w12_bytes(cfg, full)
-    assert t2 == cfg.n and b2 == 7_799_308_288       # the prefill figure the benchmark reports
+    assert t2 == cfg.n and b2 == 6_801_063_936       # the prefill figure the benchmark reports

@@ -82,11 +82,51 @@ def run_gpu(cfg, x=None, weights=None, step=None):
                s=s.double().cpu().numpy())
     for r in ("z", "counts", "offs", "row_token", "row_slot", "hidden", "v"):
         out[r] = lmoe.workspace_view(ws, dims, x.dtype, r).cpu()
+    # the staged rows stay on the device (up to ~1 GB); tests gather what they check
+    out["rows_dev"] = lmoe.workspace_view(ws, dims, x.dtype, "rows",
+                                          capped=bool(np.isfinite(cfg.beta1) and np.isfinite(cfg.beta2)))
     for r in ("z", "hidden", "v"):
         out[r] = out[r].double().numpy()
     for r in ("counts", "offs", "row_token", "row_slot"):
         out[r] = out[r].numpy().astype(np.int64)
     return out
+
+
+def check_topk_valid(s, bias, idx):
+    """Every token's list is a valid biased top-k of the GPU's own fp32 scores.
+
+    The selection key is fp32(s) + fp32(b), one IEEE fp32 add as in the kernel.
+    For every token: k distinct experts; min(chosen keys) >= max(unchosen keys);
+    where the two meet, every chosen expert at that key has a lower index than
+    every unchosen one (ties go to the lower index); the list is ordered by
+    decreasing key, equal keys by increasing index.  Returns the number of
+    tokens that had an exact tie at the threshold."""
+    s32 = np.asarray(s, dtype=np.float32)
+    b32 = np.asarray(bias, dtype=np.float32)
+    sel = s32 + b32[None, :]
+    idx = np.asarray(idx, dtype=np.int64)
+    T, n = sel.shape
+    k = idx.shape[1]
+    assert idx.min() >= 0 and idx.max() < n, "expert index out of range"
+    assert np.all(np.diff(np.sort(idx, axis=1), axis=1) > 0), "repeated expert in a token's list"
+    chosen = np.zeros((T, n), dtype=bool)
+    np.put_along_axis(chosen, idx, True, axis=1)
+    cs = np.take_along_axis(sel, idx, axis=1)
+    lo = cs.min(axis=1)
+    if k == n:
+        hi = np.full(T, -np.inf, dtype=np.float32)
+    else:
+        hi = np.where(chosen, np.float32(-np.inf), sel).max(axis=1)
+    bad = np.nonzero(lo < hi)[0]
+    assert bad.size == 0, f"{bad.size} tokens chose a lower key than one left out (first: token {bad[:1]})"
+    ties = np.nonzero(lo == hi)[0]
+    for t in ties:
+        c_at = idx[t][cs[t] == lo[t]].max()
+        u_at = np.nonzero(~chosen[t] & (sel[t] == lo[t]))[0].min()
+        assert c_at < u_at, f"token {t}: tie at the threshold not broken by the lower index"
+    d, di = np.diff(cs, axis=1), np.diff(idx, axis=1)
+    assert np.all((d < 0) | ((d == 0) & (di > 0))), "list not ordered by (-key, index)"
+    return int(ties.size)
 
 
 def check_against_oracle(cfg, gpu, x_host, P, rows=None):
@@ -109,10 +149,8 @@ def check_against_oracle(cfg, gpu, x_host, P, rows=None):
     # routing weights from the GPU's own fp32 scores, order matching the GPU's list
     g_ref = ref.routing_weights(gpu["s"][sel], g_idx)
     assert np.abs(gpu["g"][sel] - g_ref).max() <= 1e-6
-    # biased ordering of the GPU's list is non-increasing in the GPU's scores
-    sb = gpu["s"][sel] + P.bias()[None, :]
-    srt = np.take_along_axis(sb, g_idx, 1)
-    assert np.all(np.diff(srt.astype(np.float32), axis=1) <= 0)
+    # every token (near-ties included) chose a valid biased top-k of its own fp32 scores
+    check_topk_valid(gpu["s"][sel], P.bias(), g_idx)
     err = rel_err_rows if cfg.norm == "none" else rel_err
     assert err(gpu["v"][sel], forced["v_pre"], f"{cfg.name} v", tl) <= tl, "v"
     assert err(gpu["y"][sel], forced["y_pre"], f"{cfg.name} y", tl) <= tl, "y"
@@ -204,6 +242,7 @@ def test_c1_small_bf16_full_parity():
     dict(T=257, d=256, L=128, n=64, k=64, n_shared=1, D=64, dtype="f32"),       # k = n = 64: every expert
     dict(T=1, d=128, L=64, n=1, k=1, n_shared=1, D=64, dtype="f32"),            # one token, one expert
     dict(T=130, d=384, L=192, n=1024, k=3, n_shared=2, D=192, dtype="bf16"),    # largest expert count
+    dict(T=777, d=256, L=128, n=700, k=16, n_shared=2, D=64, dtype="bf16"),     # 512 < n <= 896: the K3 top-k kernel
     # latent widths that take each combine + RMSNorm layout: 4 and 8 chunks of
     # 8 elements per lane (one wavefront per token), then one work-group per token
     dict(T=70, d=4096, L=2048, n=16, k=2, n_shared=1, D=64, dtype="bf16"),
@@ -218,6 +257,52 @@ def test_ragged_and_edge_shapes(shape):
     check_against_oracle(cfg, gpu, x, P)
     check_dispatch(cfg, gpu)
     check_hidden(cfg, gpu, P, x)
+
+
+@pytest.mark.parametrize("n,k", [(896, 16), (1024, 64), (200, 7), (40, 5)])
+def test_topk_exact_ties_go_to_the_lower_index(n, k):
+    """Exact ties in the top-k kernel that serves each expert count (896 is the
+    K3 pool of "Kimi K3 Architecture Deep Dive" §3).  With W_r = 0 every logit
+    is exactly 0 and every score exactly sigmoid(0) = 1/2, so (1) with zero bias
+    every key ties and each token's list must be experts 0 .. k-1 in that order,
+    with weights 1/k; (2) with the bias on a few exactly representable levels
+    the list must be the stable order of (-b, e): the oracle's top-k of the
+    same keys, order included; (3) with the router rows repeated (expert e uses
+    row e mod 37) and a bias equal within each class, tokens differ but every
+    list must still be a valid top-k that breaks ties by the lower index."""
+    cfg = synth.get_config("C0").with_(T=300, d=256, L=128, n=n, k=k, n_shared=1, D=64, dtype="bf16",
+                                       x_seed=61, w_seed=61)
+    dev = torch.device("cuda:0")
+    w = synth.device_params(cfg, device=dev)
+    x = w.pop("x")
+    wr = w["w_router"].clone()
+
+    def route(bias):
+        w["router_bias"] = torch.as_tensor(np.asarray(bias, dtype=np.float32)).to(dev)
+        idx = torch.full((cfg.T, k), -1, dtype=torch.int32, device=dev)
+        g = torch.empty((cfg.T, k), dtype=torch.float32, device=dev)
+        s = torch.empty((cfg.T, n), dtype=torch.float32, device=dev)
+        lmoe.forward(x, w, k, topk_idx=idx, topk_w=g, scores=s)
+        torch.cuda.synchronize()
+        return idx.cpu().numpy().astype(np.int64), g.cpu().numpy(), s.cpu().numpy()
+
+    w["w_router"].zero_()
+    idx, g, s = route(np.zeros(n))
+    assert np.all(s == 0.5)
+    assert np.array_equal(idx, np.broadcast_to(np.arange(k), (cfg.T, k)))
+    assert np.allclose(g, 1.0 / k, rtol=1e-7, atol=0)
+    assert check_topk_valid(s, np.zeros(n), idx) == (cfg.T if k < n else 0)
+
+    b = np.random.default_rng(n).integers(0, 4, n) * 0.125
+    idx, g, s = route(b)
+    want, _ = ref.biased_topk(np.full((1, n), 0.5), b, k)
+    assert np.array_equal(idx, np.broadcast_to(want[0], (cfg.T, k)))
+    check_topk_valid(s, b, idx)
+
+    w["w_router"].copy_(wr[torch.arange(n, device=dev) % 37])
+    b = (np.arange(n) % 37 % 3) * 0.0625
+    idx, g, s = route(b)
+    check_topk_valid(s, b, idx)
 
 
 def test_bias_shift_invariance_on_gpu():

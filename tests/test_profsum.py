@@ -21,26 +21,47 @@ def test_labels_and_stages():
 
 
 def _write_pass(d, counter, values):
+    """values: {kernel: [value, ...]} or {kernel: [(value, grid), ...]}."""
     d.mkdir()
     with open(d / "p_counter_collection.csv", "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"])
         w.writeheader()
         for name, vals in values.items():
             for v in vals:
-                w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+                val, grid = v if isinstance(v, tuple) else (v, 256)
+                w.writerow({"Kernel_Name": name, "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": val})
+
+
+def _calib(tmp_path):
+    # a 1 GiB copy split over two dispatches reads half its bytes in FETCH_SIZE and writes all of them
+    _write_pass(tmp_path / "cf", "FETCH_SIZE", {COPY: [262144, 262144]})
+    _write_pass(tmp_path / "cw", "WRITE_SIZE", {COPY: [524288, 524288]})
+    return dict(calib_fetch=str(tmp_path / "cf"), calib_write=str(tmp_path / "cw"))
 
 
 def test_counter_scaling_and_round_trip(tmp_path):
-    # a 1 GiB copy split over two dispatches reads half its bytes in FETCH_SIZE and writes all of them
-    _write_pass(tmp_path / "f", "FETCH_SIZE", {COPY: [262144, 262144], W12: [1000, 3000]})
-    _write_pass(tmp_path / "w", "WRITE_SIZE", {COPY: [524288, 524288], W12: [100, 300]})
+    # the workload's own device copies (of other sizes) do not enter the calibration
+    _write_pass(tmp_path / "f", "FETCH_SIZE", {COPY: [1000, 5000], W12: [1000, 3000]})
+    _write_pass(tmp_path / "w", "WRITE_SIZE", {COPY: [2000, 9000], W12: [100, 300]})
     out = tmp_path / "summary.md"
-    profsum.counters(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "cmd")
+    profsum.counters(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "cmd", **_calib(tmp_path))
     text = out.read_text()
     assert "fetch_factor: 2.0000" in text and "write_factor: 1.0000" in text
     tb, sha = profsum.read_counters(str(out))
     assert tb == (2000 * 2.0 + 200 * 1.0) * 1024  # per-dispatch means, scaled, in bytes
     assert sha == profsum.source_sha256()
+
+
+def test_rows_are_split_by_grid(tmp_path):
+    # one kernel launched with two grids (e.g. the QB histogram at 1000 and 10000 bins): two rows
+    hist = "_ZN4lmoe14qb_hist_kernelEPKflii"
+    _write_pass(tmp_path / "f", "FETCH_SIZE", {hist: [(100, 1024), (100, 1024), (900, 8192)]})
+    _write_pass(tmp_path / "w", "WRITE_SIZE", {hist: [(10, 1024), (10, 1024), (90, 8192)]})
+    out = tmp_path / "summary.md"
+    profsum.counters(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "cmd", **_calib(tmp_path))
+    rows = [ln.split("|") for ln in out.read_text().splitlines() if "QB histogram" in ln]
+    got = sorted((int(r[3]), int(r[4]), r[5].strip()) for r in rows)
+    assert got == [(1024, 2, "100"), (8192, 1, "900")]
 
 
 def test_missing_summary_and_stable_hash(tmp_path):
@@ -50,15 +71,16 @@ def test_missing_summary_and_stable_hash(tmp_path):
 
 
 def test_achieved_rate_from_kernel_trace(tmp_path):
-    _write_pass(tmp_path / "f", "FETCH_SIZE", {COPY: [524288], W12: [1000]})
-    _write_pass(tmp_path / "w", "WRITE_SIZE", {COPY: [1048576], W12: [0]})
+    _write_pass(tmp_path / "f", "FETCH_SIZE", {W12: [1000]})
+    _write_pass(tmp_path / "w", "WRITE_SIZE", {W12: [0]})
     stats = tmp_path / "k_kernel_stats.csv"
     with open(stats, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"])
         w.writeheader()
         w.writerow({"Name": W12, "Calls": 1, "AverageNs": 1000.0, "MinNs": 1000.0, "MaxNs": 1000.0, "Percentage": 100})
     out = tmp_path / "summary.md"
-    profsum.counters(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "cmd", "title", str(stats))
+    profsum.counters(str(tmp_path / "f"), str(tmp_path / "w"), str(out), "cmd", "title", str(stats),
+                     **_calib(tmp_path))
     row = [ln for ln in out.read_text().splitlines() if "SiTU-GLU" in ln][0]
     gb = 1000 * 2.0 * 1024 / 1e9  # scaled bytes in GB
     assert row.rstrip(" |").split("|")[-1].strip() == f"{gb / 1e-6:.0f}"  # over 1 us
