@@ -433,3 +433,112 @@ def expert_loads(idx, n):
     """Tokens routed to each expert."""
     return np.bincount(np.asarray(idx).reshape(-1), minlength=n)
 
+
+
+# ---------------------------------------------------------------------------
+# Bias-update baselines and variants compared with Quantile Balancing
+# ([DD] §3: K2's loss-free balancing used a SignSGD-style bias update that
+# becomes unstable at 896 experts; [RB] "Keeping the numbers in range": K2
+# nudged each expert's selection up or down by a fixed step; QB instead reads
+# the router scores against the top-k threshold and solves where each expert's
+# threshold should move to get its target share; [IK] Quantile Balancing.)
+
+
+def signsgd_update(loads, T, k, bias, step):
+    """K2-style bias step: b_e <- fp32(b_e + step * sign(T k / n - load_e)).
+
+    READING: the pages give the rule's form (a fixed step up for under-loaded,
+    down for over-loaded experts) but no step size; `step` is the caller's.
+    The comparison with the target share is exact in integers
+    (load_e * n against T * k); an expert exactly at its share keeps its bias.
+    """
+    loads = np.asarray(loads, dtype=np.int64)
+    n = loads.size
+    target = int(T) * int(k)
+    sgn = np.sign(target - loads * n).astype(np.float32)
+    return (np.asarray(bias, dtype=np.float32) + np.float32(step) * sgn).astype(np.float32)
+
+
+def selection_keys(s32, bias):
+    """The keys the top-k compares: fp32(s + b), one fp32 add per element."""
+    return (np.asarray(s32, dtype=np.float32) + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+
+
+def margin_thresholds(sel, k):
+    """Per token, the k-th and (k+1)-th largest selection keys (tau_k, tau_k1);
+    tau_k1 = -inf when k equals the expert count."""
+    srt = -np.sort(-np.asarray(sel, dtype=np.float32), axis=1)
+    tk = srt[:, k - 1]
+    tk1 = srt[:, k] if k < srt.shape[1] else np.full(srt.shape[0], -np.inf, dtype=np.float32)
+    return tk.astype(np.float32), tk1.astype(np.float32)
+
+
+def margins(s32, bias, k):
+    """Margin of every (token, expert) against the threshold that expert must cross.
+
+    READING of "reads the distribution of router scores against the top-k
+    threshold" ([RB]): an expert whose key is at or above the token's k-th key
+    is in the token's top-k and leaves it when its key falls below the (k+1)-th
+    key; any other expert enters when its key passes the k-th.  So
+      m_ie = fp32(sel_ie - tau_k1(i))   if sel_ie >= tau_k(i)
+      m_ie = fp32(sel_ie - tau_k(i))    otherwise,
+    and, away from ties, shifting expert e's bias alone by delta keeps it in
+    (or brings it into) token i's top-k exactly when m_ie + delta > 0.
+    """
+    sel = selection_keys(s32, bias)
+    tk, tk1 = margin_thresholds(sel, k)
+    with np.errstate(invalid="ignore"):
+        above = sel >= tk[:, None]
+    thr = np.where(above, tk1[:, None], tk[:, None]).astype(np.float32)
+    return (sel - thr).astype(np.float32)
+
+
+def margin_bins(m32, nbins):
+    """Bin of each fp32 margin: the margin mapped to [0, 1] as u = fp32(m + 1) * 0.5
+    (margins of sigmoid scores under small biases lie in (-1, 1); the halving is
+    exact), then the score binning rule of qb_bins (clamped to the end bins)."""
+    m32 = np.asarray(m32, dtype=np.float32)
+    u = ((m32 + np.float32(1.0)).astype(np.float32) * np.float32(0.5)).astype(np.float32)
+    return qb_bins(u, nbins)
+
+
+def margin_histogram(s32, bias, k, nbins):
+    """H[e][j]: tokens whose margin for expert e falls in bin j (int64 [n, B])."""
+    b = margin_bins(margins(s32, bias, k), nbins)
+    T, n = b.shape
+    H = np.zeros((n, nbins), dtype=np.int64)
+    for e in range(n):
+        H[e] = np.bincount(b[:, e], minlength=nbins)
+    return H
+
+
+def margin_solve(H, k, n, bias_in):
+    """Move each expert's bias so that its target share k/n of tokens clears its threshold.
+
+    q_e = upper-(k/n) quantile of expert e's margin histogram (in [0, 1]
+    units), i.e. the margin 2 q_e - 1 that N_e k / n of its tokens reach;
+    b_e <- fp32(b_e - (2 q_e - 1)), computed in fp64.  No step size: the shift
+    is read off the distribution.  Experts with an empty histogram keep their
+    bias.  READING: iterated batch after batch, since every expert moves at once
+    and the tokens' thresholds move with them.
+    """
+    H = np.asarray(H, dtype=np.int64)
+    out = np.array(bias_in, dtype=np.float32, copy=True)
+    for e in range(H.shape[0]):
+        Ne = int(H[e].sum())
+        if Ne == 0:
+            continue
+        q = qb_read(H[e], Ne * k / n)
+        out[e] = np.float32(float(out[e]) - (2.0 * q - 1.0))
+    return out
+
+
+def margin_update(s32, nbins, k, bias, hist=None, accumulate=False, solve=True):
+    """One margin-QB call: histogram this batch's margins (optionally added to
+    `hist`), then optionally solve the new bias."""
+    s32 = np.asarray(s32, dtype=np.float32)
+    n = s32.shape[1]
+    Hb = margin_histogram(s32, bias, k, nbins)
+    H = Hb + np.asarray(hist, dtype=np.int64) if (accumulate and hist is not None) else Hb
+    b = margin_solve(H, k, n, bias) if solve else None
+    return H, b
