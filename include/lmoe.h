@@ -43,7 +43,9 @@ typedef enum {
   LMOE_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                 */
   LMOE_ERR_WORKSPACE = -5, /* workspace smaller than lmoe_workspace_size()     */
   LMOE_ERR_HIP = -6,       /* a HIP launch or runtime call failed              */
-  LMOE_ERR_VALUE = -7      /* a scalar argument is out of range                */
+  LMOE_ERR_VALUE = -7,     /* a scalar argument is out of range                */
+  LMOE_ERR_SCRATCH = -8    /* lmoe_forward_static: the call needs more scratch
+                              than LMOE_STATIC_SCRATCH_BYTES                     */
 } lmoe_status;
 
 /* Work dtype: the storage type of x, the weights, and the stored activations
@@ -185,6 +187,26 @@ int64_t lmoe_workspace_offset(const lmoe_dims *dims, int dtype, int region);
 int lmoe_forward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
                  int32_t *topk_idx, float *topk_w, float *scores, void *workspace,
                  size_t workspace_bytes, void *stream);
+
+/* Bytes of the library's own device scratch used by lmoe_forward_static, one
+ * copy per device (64 MiB: the workspace of decode-sized calls, e.g. up to
+ * about 100 tokens at d = 7168 with 896 experts choose 16). */
+#define LMOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* lmoe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, with the workspace taken from a static device
+ * array the library holds (LMOE_STATIC_SCRATCH_BYTES per device, looked up on
+ * the first call on each device).  The caller still passes x, y and the
+ * optional outputs.  Calls whose lmoe_workspace_size() exceeds
+ * LMOE_STATIC_SCRATCH_BYTES return LMOE_ERR_SCRATCH before anything is
+ * launched; the other errors are lmoe_forward's.  No memory is allocated or
+ * freed.  The scratch keeps the last call's contents; the forward needs none of
+ * it initialised.  Every call on one device shares that device's scratch:
+ * calls that may overlap on one device (different streams, host threads) race
+ * and must be serialised by the caller. */
+int lmoe_forward_static(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
+                        int32_t *topk_idx, float *topk_w, float *scores, void *stream);
 
 /* Stages of lmoe_forward, in launch order (for lmoe_forward_timed). */
 #define LMOE_N_STAGES 8

@@ -10,9 +10,10 @@ import ctypes
 import torch
 
 from ._abi import (Dims, Weights, GATES, NORMS, LMOE_BF16, LMOE_F32, WS_REGIONS, EXPORTS, N_STAGES, STAGES, lib,  # noqa: F401
+                   STATIC_SCRATCH_BYTES,
                    check, strerror)
 
-__all__ = ["dims_of", "workspace_size", "workspace_view", "forward", "qb_update", "qb_workspace_size",
+__all__ = ["dims_of", "workspace_size", "workspace_view", "forward", "forward_static", "qb_update", "qb_workspace_size",
            "strerror", "make_workspace"]
 
 
@@ -109,6 +110,23 @@ def forward(x, weights, k, y=None, topk_idx=None, topk_w=None, scores=None, work
                                       _ptr(topk_w), _ptr(scores), _ptr(workspace), workspace.numel(), handles,
                                       len(stage_events), stream)
         check(rc, "lmoe_forward_timed")
+    return y
+
+
+def forward_static(x, weights, k, y=None, topk_idx=None, topk_w=None, scores=None, beta1=4.0, beta2=25.0,
+                   eps=1e-6, stream=None, gate="tanh", norm="rms"):
+    """y = LatentMoE(x) via lmoe_forward_static: no workspace argument, nothing allocated by
+    the library (it uses its own static device scratch); y must be given to allocate nothing here
+    either.  Calls on one device share that scratch and must not overlap."""
+    dims = dims_of(x, weights, k)
+    if y is None:
+        y = torch.empty_like(x)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    W = _weights_struct(weights, beta1, beta2, eps, gate, norm)
+    rc = lib().lmoe_forward_static(dims, W, _dtype_code(x.dtype), _ptr(x), _ptr(y), _ptr(topk_idx), _ptr(topk_w),
+                                   _ptr(scores), stream)
+    check(rc, "lmoe_forward_static")
     return y
 
 

@@ -10,12 +10,14 @@ LMOE_F32 = 0
 LMOE_BF16 = 1
 
 STATUS = {0: "LMOE_OK", -1: "LMOE_ERR_NULL", -2: "LMOE_ERR_SHAPE", -3: "LMOE_ERR_DTYPE", -4: "LMOE_ERR_ALIGN",
-          -5: "LMOE_ERR_WORKSPACE", -6: "LMOE_ERR_HIP", -7: "LMOE_ERR_VALUE"}
+          -5: "LMOE_ERR_WORKSPACE", -6: "LMOE_ERR_HIP", -7: "LMOE_ERR_VALUE", -8: "LMOE_ERR_SCRATCH"}
+
+STATIC_SCRATCH_BYTES = 64 << 20  # LMOE_STATIC_SCRATCH_BYTES
 
 WS_REGIONS = {"z": 0, "counts": 1, "offs": 2, "row_token": 3, "row_slot": 4, "hidden": 5, "rows": 6, "v": 7}
 
 # every function the header declares
-EXPORTS = ("lmoe_workspace_size", "lmoe_workspace_offset", "lmoe_forward", "lmoe_forward_timed",
+EXPORTS = ("lmoe_workspace_size", "lmoe_workspace_offset", "lmoe_forward", "lmoe_forward_timed", "lmoe_forward_static",
            "lmoe_qb_update", "lmoe_qb_workspace_size", "lmoe_strerror")
 
 N_STAGES = 8
@@ -60,6 +62,9 @@ def lib():
         L.lmoe_forward_timed.argtypes = [P(Dims), P(Weights), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        L.lmoe_forward_static.restype = ctypes.c_int
+        L.lmoe_forward_static.argtypes = [P(Dims), P(Weights), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         L.lmoe_qb_update.restype = ctypes.c_int
         L.lmoe_qb_update.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,

@@ -495,6 +495,56 @@ int lmoe_forward_timed(const lmoe_dims *dims, const lmoe_weights *w, int dtype, 
   return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, workspace, workspace_bytes, stream, events);
 }
 
+}  // extern "C"
+
+// Scratch of lmoe_forward_static: device memory the library itself holds, one
+// copy per device (the array is allocated when the code object is loaded on a
+// device and kept until the process ends).  On the host the array's name is
+// only a stand-in: its device address is looked up once per device and only
+// that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[LMOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+struct ScratchAddr {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void *ptr = nullptr;
+};
+
+// Device address of the current device's scratch (looked up on the first call
+// on that device, with it current), or nullptr with *err set.
+void *static_scratch(hipError_t *err) {
+  static ScratchAddr addr[MAX_DEVICES];
+  const int dev = current_device();
+  if (dev < 0) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  ScratchAddr &a = addr[dev];
+  std::call_once(a.once, [&] { a.err = hipGetSymbolAddress(&a.ptr, HIP_SYMBOL(scratch)); });
+  *err = a.err;
+  return a.err == hipSuccess ? a.ptr : nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lmoe_forward_static(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, void *y,
+                        int32_t *topk_idx, float *topk_w, float *scores, void *stream) {
+  int rc = check_dims(dims);
+  if (rc != LMOE_OK) return rc;
+  if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
+  const int64_t need = layout(*dims, dtype).total;
+  if (need > (int64_t)LMOE_STATIC_SCRATCH_BYTES) return LMOE_ERR_SCRATCH;
+  if (dims->T == 0) return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, nullptr, 0, stream, nullptr);
+  hipError_t e;
+  void *ws = static_scratch(&e);
+  if (!ws) return LMOE_ERR_HIP;
+  return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, ws, LMOE_STATIC_SCRATCH_BYTES, stream, nullptr);
+}
+
 size_t lmoe_qb_workspace_size(int32_t nbins) {
   if (nbins < 1 || nbins > 16384) return 0;
   return (size_t)align256((int64_t)nbins * 8);
@@ -563,6 +613,7 @@ const char *lmoe_strerror(int status) {
     case LMOE_ERR_WORKSPACE: return "workspace smaller than required";
     case LMOE_ERR_HIP: return "a HIP launch or runtime call failed";
     case LMOE_ERR_VALUE: return "a scalar argument is out of range";
+    case LMOE_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }

@@ -134,3 +134,20 @@ def test_qb_validation():
 def test_strerror():
     assert lmoe.strerror(-5).startswith("workspace")
     assert lmoe.strerror(123) == "unknown status"
+
+
+def test_static_forward_validation():
+    """lmoe_forward_static checks its scratch bound on the host before anything
+    else touches the GPU: the prefill shape needs more than the static scratch."""
+    f = lib().lmoe_forward_static
+    w = fake_weights()
+
+    def call_s(d, **kw):
+        return f(ctypes.byref(d), ctypes.byref(w), kw.get("dtype", 1), FAKE, FAKE, None, None, None, None)
+
+    assert lmoe.workspace_size(c2dims(), 1) > lmoe.STATIC_SCRATCH_BYTES
+    assert call_s(c2dims()) == -8
+    assert call_s(c2dims(L=3000)) == -2
+    assert call_s(c2dims(), dtype=9) == -3
+    assert f(ctypes.byref(c2dims(T=0)), ctypes.byref(w), 1, None, None, None, None, None, None) == 0
+    assert lmoe.strerror(-8).startswith("the call needs more scratch")
