@@ -51,10 +51,14 @@ def experts_w12_bytes(cfg, counts):
 
 def qb_protocol(w, dev, lmoe, synth):
     """Skewed-routing workload (K3 shapes, T=32768, Zipf(1.1) logit skew, same weights as the
-    prefill workload): forward -> expert loads -> lmoe_qb_update (1000-bin histograms, bias solve
-    for share k/n) -> next step's bias, for 20 steps; loads at step 0 (bias 0) and step 20
-    (bias from step 19, fresh batch).  Also times the histogram + solve launch.  The same 20 steps
-    with 10000-bin histograms are reported beside it (the pages find 1000 bins as good as 10000)."""
+    prefill workload): forward -> expert loads -> bias update -> next step's bias, for 20 steps;
+    loads at step 0 (bias 0) and step 20 (bias from step 19, fresh batch), and the max/mean load
+    of every step.  Bias updates compared on the same batches: Quantile Balancing
+    (lmoe_qb_update: 1000-bin histograms, bias solve for share k/n; and with 10000 bins, which
+    the pages find no better than 1000), its margin form (lmoe_qb_margin_update: the scores read
+    against each token's top-k threshold) and the K2-style fixed step it replaces
+    (lmoe_bias_signsgd, steps 1e-3, 1e-2 and 1e-1: the pages give no step size).  Each update
+    launch is timed with events."""
     import torch
     cfg = synth.get_config("C4")
     w = dict(w)
@@ -66,37 +70,47 @@ def qb_protocol(w, dev, lmoe, synth):
     idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
     s = torch.empty((cfg.T, cfg.n), dtype=torch.float32, device=dev)
 
-    def run(nbins):
+    def run(method, nbins=cfg.nbins, step=0.0):
         bias = torch.zeros(cfg.n, dtype=torch.float32, device=dev)
         w["router_bias"] = bias
         hist = torch.empty((cfg.n, nbins), dtype=torch.int32, device=dev)
         qws = torch.empty(lmoe.qb_workspace_size(nbins), dtype=torch.uint8, device=dev)
-        stats, qb_ms = {}, []
+        mws = torch.empty(lmoe.qb_margin_workspace_size(cfg.T), dtype=torch.uint8, device=dev)
+        traj, mins, upd_ms = [], [], []
         for t in range(cfg.qb_steps + 1):
             x.copy_(synth.params.device_x(cfg, dev, step=t))
             lmoe.forward(x, w, cfg.k, y=y, topk_idx=idx, scores=s, workspace=ws, beta1=cfg.beta1,
                          beta2=cfg.beta2, eps=cfg.eps)
-            if t in (0, cfg.qb_steps):
-                load = torch.bincount(idx.flatten().long(), minlength=cfg.n).double()
-                m = load.mean()
-                stats[t] = (float(load.max() / m), float(load.min() / m))
+            load = torch.bincount(idx.flatten().long(), minlength=cfg.n).double()
+            m = load.mean()
+            traj.append(float(load.max() / m))
+            mins.append(float(load.min() / m))
             if t < cfg.qb_steps:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                lmoe.qb_update(s, cfg.k, hist, bias, accumulate=False, solve=True, workspace=qws)
+                if method == "qb":
+                    lmoe.qb_update(s, cfg.k, hist, bias, accumulate=False, solve=True, workspace=qws)
+                elif method == "margin":
+                    lmoe.qb_margin_update(s, cfg.k, hist, bias, workspace=mws)
+                else:
+                    lmoe.bias_signsgd(idx, cfg.n, step, bias)
                 e1.record()
                 torch.cuda.synchronize()
-                qb_ms.append(e0.elapsed_time(e1))
-        ms = float(sorted(qb_ms)[len(qb_ms) // 2])
-        return {"load_max_over_mean": {"step0_bias0": stats[0][0], f"step{cfg.qb_steps}": stats[cfg.qb_steps][0]},
-                "load_min_over_mean": {"step0_bias0": stats[0][1], f"step{cfg.qb_steps}": stats[cfg.qb_steps][1]},
-                "qb_update_ms_median": ms}
+                upd_ms.append(e0.elapsed_time(e1))
+        last = cfg.qb_steps
+        return {"load_max_over_mean": {"step0_bias0": traj[0], f"step{last}": traj[last]},
+                "load_min_over_mean": {"step0_bias0": mins[0], f"step{last}": mins[last]},
+                "max_over_mean_by_step": [round(v, 4) for v in traj],
+                "update_ms_median": float(sorted(upd_ms)[len(upd_ms) // 2])}
 
     out = {"workload": f"C4: T={cfg.T}, K3 shapes, Zipf({cfg.zipf_s}) logit skew alpha={cfg.zipf_alpha}",
            "steps": cfg.qb_steps, "nbins": cfg.nbins}
-    out.update(run(cfg.nbins))
+    out.update(run("qb"))
+    out["qb_update_ms_median"] = out["update_ms_median"]
     out["qb_scores_read_GBps"] = cfg.T * cfg.n * 4 / (out["qb_update_ms_median"] * 1e-3) / 1e9
-    out["bins_10000"] = run(10000)
+    out["bins_10000"] = run("qb", nbins=10000)
+    out["margin"] = run("margin")
+    out["signsgd"] = {f"step_{st:g}": run("signsgd", step=st) for st in (1e-3, 1e-2, 1e-1)}
     return out
 
 

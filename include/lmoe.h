@@ -261,6 +261,49 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
  * histogram, int64 [nbins]); 0 for an invalid nbins. */
 size_t lmoe_qb_workspace_size(int32_t nbins);
 
+/* Margin form of the Quantile Balancing update ("Kimi K3 Architecture Deep
+ * Dive" §3; LeiPhone report "Keeping the numbers in range": the router scores
+ * are read against each token's top-k threshold to estimate where each
+ * expert's threshold must move to receive its target share).
+ *   scores [T, n] fp32    unbiased router scores; 0 <= T < 2^31, 1 <= n <= 1024,
+ *                         1 <= k <= n
+ *   bias [n] fp32         in: the bias the margins are taken against (the one
+ *                         the scores were routed with); out (solve != 0): the
+ *                         updated bias
+ *   hist [n, nbins] int32 in/out, overwritten (accumulate == 0) or added to
+ * Per token i, with keys sel_ie = fp32(s_ie + b_e): tk_i / tk1_i = its k-th /
+ * (k+1)-th largest key (tk1 = -inf when k == n).  The margin of (i, e) is
+ *   m_ie = fp32(sel_ie - tk1_i) if sel_ie >= tk_i, else fp32(sel_ie - tk_i),
+ * the bias shift at which e leaves or enters token i's top-k; it is binned as
+ * the score rule of lmoe_qb_update applied to u = fp32(m + 1) * 0.5.  The
+ * solve reads q_e = read(hist[e], N_e * k / n) (as lmoe_qb_update) and sets
+ *   bias[e] = fp32(bias[e] - (2 q_e - 1))    (computed in fp64);
+ * experts with an empty histogram keep their bias.  All operations are in a
+ * fixed order, so the result is reproducible bit for bit.
+ *   workspace             device buffer of lmoe_qb_margin_workspace_size(T)
+ *                         bytes (the per-token thresholds); may be NULL when
+ *                         T == 0
+ * T == 0 with accumulate == 0 clears the histogram. */
+int lmoe_qb_margin_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
+                          int accumulate, float *bias, int solve, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Bytes of device workspace lmoe_qb_margin_update needs for T tokens (0 for an
+ * invalid T). */
+size_t lmoe_qb_margin_workspace_size(int64_t T);
+
+/* The fixed-step bias update of K2's loss-free balancing that Quantile
+ * Balancing replaces ("Kimi K3 Architecture Deep Dive" §3: SignSGD-style,
+ * unstable at 896 experts; LeiPhone report "Keeping the numbers in range":
+ * selection nudged up or down by a fixed step):
+ *   load_e  = number of entries equal to e in topk_idx [T, k] (int32)
+ *   bias[e] = fp32(bias[e] + step * sign(T k - load_e n))
+ * i.e. a step up below the share T k / n, down above it, none at it.  The
+ * pages give no step size: `step` is the caller's (finite).  Entries outside
+ * [0, n) are not counted.  T == 0 is a no-op (topk_idx may then be NULL). */
+int lmoe_bias_signsgd(const int32_t *topk_idx, int64_t T, int64_t n, int64_t k, float step, float *bias,
+                      void *stream);
+
 /* Static description of a status code. */
 const char *lmoe_strerror(int status);
 

@@ -14,6 +14,7 @@ from ._abi import (Dims, Weights, GATES, NORMS, LMOE_BF16, LMOE_F32, WS_REGIONS,
                    check, strerror)
 
 __all__ = ["dims_of", "workspace_size", "workspace_view", "forward", "forward_static", "qb_update", "qb_workspace_size",
+           "qb_margin_update", "qb_margin_workspace_size", "bias_signsgd",
            "strerror", "make_workspace"]
 
 
@@ -147,3 +148,34 @@ def qb_update(scores, k, hist, bias=None, accumulate=False, solve=True, workspac
                               0 if workspace is None else workspace.numel(), stream)
     check(rc, "lmoe_qb_update")
     return hist, bias
+
+
+def qb_margin_workspace_size(T):
+    return int(lib().lmoe_qb_margin_workspace_size(int(T)))
+
+
+def qb_margin_update(scores, k, hist, bias, accumulate=False, solve=True, workspace=None, stream=None):
+    """Margin form of Quantile Balancing: histogram each (token, expert) margin against the
+    token's top-k threshold under `bias`, then (optionally) move `bias` in place."""
+    T, n = scores.shape
+    nbins = hist.shape[1]
+    if workspace is None and T > 0:
+        workspace = torch.empty(qb_margin_workspace_size(T), dtype=torch.uint8, device=hist.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(hist.device).cuda_stream
+    rc = lib().lmoe_qb_margin_update(_ptr(scores), T, n, int(k), int(nbins), _ptr(hist), int(bool(accumulate)),
+                                     _ptr(bias), int(bool(solve)), _ptr(workspace),
+                                     0 if workspace is None else workspace.numel(), stream)
+    check(rc, "lmoe_qb_margin_update")
+    return hist, bias
+
+
+def bias_signsgd(topk_idx, n, step, bias, stream=None):
+    """K2-style fixed-step bias update from the top-k lists [T, k] (in place on `bias`)."""
+    T, k = topk_idx.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(bias.device).cuda_stream
+    rc = lib().lmoe_bias_signsgd(_ptr(topk_idx) if T > 0 else None, T, int(n), int(k), float(step), _ptr(bias),
+                                 stream)
+    check(rc, "lmoe_bias_signsgd")
+    return bias

@@ -18,7 +18,8 @@ WS_REGIONS = {"z": 0, "counts": 1, "offs": 2, "row_token": 3, "row_slot": 4, "hi
 
 # every function the header declares
 EXPORTS = ("lmoe_workspace_size", "lmoe_workspace_offset", "lmoe_forward", "lmoe_forward_timed", "lmoe_forward_static",
-           "lmoe_qb_update", "lmoe_qb_workspace_size", "lmoe_strerror")
+           "lmoe_qb_update", "lmoe_qb_workspace_size", "lmoe_qb_margin_update", "lmoe_qb_margin_workspace_size",
+           "lmoe_bias_signsgd", "lmoe_strerror")
 
 N_STAGES = 8
 STAGES = ("down_proj", "router", "topk", "permute", "experts_w12", "experts_w3", "combine_norm", "up_proj")
@@ -71,6 +72,15 @@ def lib():
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.lmoe_qb_workspace_size.restype = ctypes.c_size_t
         L.lmoe_qb_workspace_size.argtypes = [ctypes.c_int32]
+        L.lmoe_qb_margin_update.restype = ctypes.c_int
+        L.lmoe_qb_margin_update.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.lmoe_qb_margin_workspace_size.restype = ctypes.c_size_t
+        L.lmoe_qb_margin_workspace_size.argtypes = [ctypes.c_int64]
+        L.lmoe_bias_signsgd.restype = ctypes.c_int
+        L.lmoe_bias_signsgd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
         L.lmoe_strerror.restype = ctypes.c_char_p
         L.lmoe_strerror.argtypes = [ctypes.c_int]
         _lib = L

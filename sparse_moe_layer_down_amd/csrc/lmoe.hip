@@ -432,6 +432,34 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   return hipSuccess;
 }
 
+// The histogram launch of both QB forms: B-bin histograms of every expert over
+// the T tokens, added to hist.  MARGIN: the binned value is the margin of the
+// score against the token's threshold (bias [n], thr [T]).
+template <bool MARGIN>
+hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_t *hist, const float *bias,
+                          const float2 *thr, hipStream_t st) {
+  const int64_t n = ni;
+  const int nbins = kb;
+  // experts per work-group: as many B-bin LDS histograms as fit in 64 KB (max 16)
+  int eg = (int)std::min<int64_t>(16, std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4)));
+  const int64_t groups = cdiv(n, eg);
+  // token runs: every work-group merges its eg * nbins LDS bins into the global
+  // histogram with device atomics, so fewer runs mean fewer merges.  Groups of
+  // at least four experts (16-byte loads of four experts per token) are bound
+  // by those merges: about one work-group per CU.  Narrower groups (wide
+  // histograms, e.g. 10000 bins: one expert per group) walk their tokens with
+  // scalar loads and want more runs: about four work-groups per CU.  (Measured
+  // at 32768 tokens x 896 experts: 1000 bins 0.110 -> 0.096 ms, 10000 bins
+  // 0.49 -> 0.42 ms against two work-groups per CU.)
+  const int64_t target = (eg >= 4 ? 1 : 4) * (int64_t)device_cus();
+  int64_t runs = std::max<int64_t>(1, std::min<int64_t>(cdiv(target, groups), cdiv(T, 256)));
+  const int64_t tpb = cdiv(T, runs);
+  runs = cdiv(T, tpb);  // <= 4 * CUs: within the grid's y limit
+  hipLaunchKernelGGL(qb_hist_kernel<MARGIN>, dim3((unsigned)groups, (unsigned)runs), dim3(256),
+                     (size_t)eg * nbins * 4, st, scores, T, ni, kb, eg, tpb, hist, bias, thr);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -570,24 +598,7 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
   }
   if (T > 0) {
-    // experts per work-group: as many B-bin LDS histograms as fit in 64 KB (max 16)
-    int eg = (int)std::min<int64_t>(16, std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4)));
-    const int64_t groups = cdiv(n, eg);
-    // token runs: every work-group merges its eg * nbins LDS bins into the global
-    // histogram with device atomics, so fewer runs mean fewer merges.  Groups of
-    // at least four experts (16-byte loads of four experts per token) are bound
-    // by those merges: about one work-group per CU.  Narrower groups (wide
-    // histograms, e.g. 10000 bins: one expert per group) walk their tokens with
-    // scalar loads and want more runs: about four work-groups per CU.  (Measured
-    // at 32768 tokens x 896 experts: 1000 bins 0.110 -> 0.096 ms, 10000 bins
-    // 0.49 -> 0.42 ms against two work-groups per CU.)
-    const int64_t target = (eg >= 4 ? 1 : 4) * (int64_t)device_cus();
-    int64_t runs = std::max<int64_t>(1, std::min<int64_t>(cdiv(target, groups), cdiv(T, 256)));
-    const int64_t tpb = cdiv(T, runs);
-    runs = cdiv(T, tpb);  // <= 4 * CUs: within the grid's y limit
-    hipLaunchKernelGGL(qb_hist_kernel, dim3((unsigned)groups, (unsigned)runs), dim3(256),
-                       (size_t)eg * nbins * 4, st, scores, T, ni, kb, eg, tpb, hist);
-    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+    if (launch_qb_hist<false>(scores, T, ni, kb, hist, nullptr, nullptr, st) != hipSuccess) return LMOE_ERR_HIP;
   }
   if (solve) {
     unsigned long long *pooled = (unsigned long long *)workspace;
@@ -601,6 +612,60 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
   }
   return LMOE_OK;
+}
+
+size_t lmoe_qb_margin_workspace_size(int64_t T) {
+  if (T < 0 || T >= ((int64_t)1 << 31)) return 0;
+  return (size_t)align256(std::max<int64_t>(T, 1) * 8);
+}
+
+int lmoe_qb_margin_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
+                          int accumulate, float *bias, int solve, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  if (T < 0 || T >= ((int64_t)1 << 31) || n < 1 || n > 1024 || k < 1 || k > n) return LMOE_ERR_SHAPE;
+  if (nbins < 1 || nbins > 16384) return LMOE_ERR_VALUE;
+  if (!hist || !bias || (T > 0 && (!scores || !workspace))) return LMOE_ERR_NULL;
+  if (!aligned16(hist) || !aligned16(bias) || (scores && !aligned16(scores)) || (workspace && !aligned16(workspace)))
+    return LMOE_ERR_ALIGN;
+  if (T > 0 && workspace_bytes < lmoe_qb_margin_workspace_size(T)) return LMOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int ni = (int)n, kb = nbins, Ti = (int)T;
+  if (!accumulate) {
+    const int64_t cnt = n * nbins;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(cnt, 256), 4096)), dim3(256), 0, st,
+                       hist, cnt, 0);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+  }
+  if (T > 0) {
+    float2 *thr = (float2 *)workspace;
+    const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(T, 4), 65536);
+    if (ni <= 64) hipLaunchKernelGGL(qb_thresholds_kernel<1>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
+    else if (ni <= 128) hipLaunchKernelGGL(qb_thresholds_kernel<2>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
+    else if (ni <= 256) hipLaunchKernelGGL(qb_thresholds_kernel<4>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
+    else if (ni <= 512) hipLaunchKernelGGL(qb_thresholds_kernel<8>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
+    else if (ni <= 896) hipLaunchKernelGGL(qb_thresholds_kernel<14>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
+    else hipLaunchKernelGGL(qb_thresholds_kernel<16>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+    if (launch_qb_hist<true>(scores, T, ni, kb, hist, bias, thr, st) != hipSuccess) return LMOE_ERR_HIP;
+  }
+  if (solve) {
+    hipLaunchKernelGGL(qb_margin_solve_kernel, dim3((unsigned)cdiv(n, 4)), dim3(256), 0, st, hist, ni, kb, (int)k,
+                       bias);
+    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+  }
+  return LMOE_OK;
+}
+
+int lmoe_bias_signsgd(const int32_t *topk_idx, int64_t T, int64_t n, int64_t k, float step, float *bias,
+                      void *stream) {
+  if (T < 0 || n < 1 || n > ((int64_t)1 << 20) || k < 1 || k > n || T * k >= ((int64_t)1 << 40)) return LMOE_ERR_SHAPE;
+  if (!(std::fabs(step) < INFINITY)) return LMOE_ERR_VALUE;
+  if (!bias || (T > 0 && !topk_idx)) return LMOE_ERR_NULL;
+  if (!aligned16(bias) || (topk_idx && !aligned16(topk_idx))) return LMOE_ERR_ALIGN;
+  if (T == 0) return LMOE_OK;  // no loads and a share of zero: every expert is at its share
+  hipLaunchKernelGGL(signsgd_kernel, dim3((unsigned)cdiv(n, 256)), dim3(1024), 0, (hipStream_t)stream, topk_idx,
+                     T * k, (int)n, step, bias);
+  return hipGetLastError() == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
 const char *lmoe_strerror(int status) {

@@ -14,8 +14,22 @@
 //                    from the pooled histogram.  All counts are integers and
 //                    the interpolation is the same sequence of IEEE fp64
 //                    operations as the definition, so the result is exact.
+//
+// The margin form of the estimator ("Keeping the numbers in range": read the
+// scores against the top-k threshold and solve where each expert's threshold
+// must move):
+//   qb_thresholds_kernel  one wavefront per token: the k-th and (k+1)-th
+//                         largest selection keys s + b (k + 1 rounds of a wave
+//                         maximum, as in the top-k kernel)
+//   qb_hist_kernel<true>  histogram of each (token, expert) margin against the
+//                         threshold that expert must cross, mapped to [0,1]
+//   qb_margin_solve_kernel  b_e -= (2 q_e - 1), q_e read as above
+// and the K2-style fixed-step baseline the pages compare QB with:
+//   signsgd_kernel        per-expert loads from the top-k lists, then
+//                         b_e += step * sign(T k / n - load_e)
 #pragma once
 #include "common.hpp"
+#include "route.hpp"
 
 namespace lmoe {
 
@@ -31,13 +45,29 @@ __global__ void fill_i32_kernel(int32_t *p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
+// The value the margin form bins for score s of an expert with bias b in a
+// token whose k-th / (k+1)-th largest keys are tk / tk1: the key sel = s + b,
+// its margin against the threshold it must cross (tk1 if it is at or above tk,
+// else tk), mapped to [0,1] as (m + 1) / 2.  Every step is one fp32 operation
+// (no contraction), so the host can reproduce it exactly.
+LMOE_DEV float qb_margin_u(float s, float b, float tk, float tk1) {
+#pragma clang fp contract(off)
+  const float sel = s + b;
+  const float m = sel - (sel >= tk ? tk1 : tk);
+  return (m + 1.0f) * 0.5f;
+}
+
 // grid: (expert groups, token runs); dynamic LDS = eg * nbins * 4 bytes.
-// When n and the group width are multiples of 4, each thread reads four
+// When n, the group width and its first expert are multiples of 4, each thread reads four
 // adjacent experts of a token as one 16-B load and four tokens per iteration;
 // otherwise one thread walks the group's experts of one token at a time.
+// MARGIN: bin qb_margin_u of the score (bias [n], thr [T] = {tk, tk1}) instead
+// of the score itself.
+template <bool MARGIN>
 __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ scores, int64_t T, int n,
                                                       int nbins, int eg, int64_t tokens_per_block,
-                                                      int32_t *__restrict__ hist) {
+                                                      int32_t *__restrict__ hist, const float *__restrict__ bias,
+                                                      const float2 *__restrict__ thr) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int32_t *h = (int32_t *)smem_raw;
   const int e0 = blockIdx.x * eg;
@@ -46,33 +76,52 @@ __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ 
   __syncthreads();
   const int64_t t0 = (int64_t)blockIdx.y * tokens_per_block;
   const int64_t t1 = min(T, t0 + tokens_per_block);
-  if ((n & 3) == 0 && (ne & 3) == 0) {
+  if ((n & 3) == 0 && (ne & 3) == 0 && (e0 & 3) == 0) {  // 16-byte aligned quads
     const int nq = ne >> 2;            // 16-B quads per token
     const int rows = 256 / nq;          // tokens per pass
     const int tr = threadIdx.x / nq, q = threadIdx.x - tr * nq;
     if (tr < rows) {
       const float *base = scores + e0 + q * 4;
       int32_t *hq = h + q * 4 * nbins;
+      f32x4 bq = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (MARGIN) bq = *(const f32x4 *)(bias + e0 + q * 4);
       int64_t t = t0 + tr;
       for (; t + 3 * rows < t1; t += 4 * rows) {
         f32x4 v[4];
+        float2 th[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *(const f32x4 *)(base + (t + u * rows) * n);
+        for (int u = 0; u < 4; ++u) {
+          v[u] = *(const f32x4 *)(base + (t + u * rows) * n);
+          if (MARGIN) th[u] = thr[t + u * rows];
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) atomicAdd(&hq[c * nbins + qb_bin(v[u][c], nbins)], 1);
+          for (int c = 0; c < 4; ++c) {
+            const float x = MARGIN ? qb_margin_u(v[u][c], bq[c], th[u].x, th[u].y) : v[u][c];
+            atomicAdd(&hq[c * nbins + qb_bin(x, nbins)], 1);
+          }
       }
       for (; t < t1; t += rows) {
         const f32x4 v = *(const f32x4 *)(base + t * n);
+        float2 th = {0.0f, 0.0f};
+        if (MARGIN) th = thr[t];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) atomicAdd(&hq[c * nbins + qb_bin(v[c], nbins)], 1);
+        for (int c = 0; c < 4; ++c) {
+          const float x = MARGIN ? qb_margin_u(v[c], bq[c], th.x, th.y) : v[c];
+          atomicAdd(&hq[c * nbins + qb_bin(x, nbins)], 1);
+        }
       }
     }
   } else {
     for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
       const float *row = scores + t * n + e0;
-      for (int e = 0; e < ne; ++e) atomicAdd(&h[e * nbins + qb_bin(row[e], nbins)], 1);
+      float2 th = {0.0f, 0.0f};
+      if (MARGIN) th = thr[t];
+      for (int e = 0; e < ne; ++e) {
+        const float x = MARGIN ? qb_margin_u(row[e], bias[e0 + e], th.x, th.y) : row[e];
+        atomicAdd(&h[e * nbins + qb_bin(x, nbins)], 1);
+      }
     }
   }
   __syncthreads();
@@ -177,6 +226,87 @@ __global__ __launch_bounds__(256) void qb_solve_kernel(const int32_t *__restrict
   const double q = qb_read_wave(hist + (int64_t)e * nbins, nbins, (long long)k, (long long)n);
   if (tau != tau || q != q) return;
   if ((threadIdx.x & 63) == 0) bias[e] = (float)(tau - q);
+}
+
+// Inverse of ord_f32 (for keys that came from a float): the float whose
+// order-preserving bits are u.
+LMOE_DEV float unord_f32(uint32_t u) {
+  return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// One wavefront per token: tk = the k-th and tk1 = the (k+1)-th largest of the
+// n keys s + b (tk1 = -inf when k == n).  Lane l holds experts l, l + 64, ...
+// as 64-bit keys (order-preserving bits of s + b, complemented index), so each
+// round's wave maximum is unique and its owner drops exactly that key.
+template <int MAXJ>
+__global__ __launch_bounds__(256) void qb_thresholds_kernel(const float *__restrict__ s,
+                                                            const float *__restrict__ bias, int T, int n, int k,
+                                                            float2 *__restrict__ thr) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  const int rounds = min(k + 1, n);
+  for (int t = wave; t < T; t += nwaves) {
+    const float *row = s + (int64_t)t * n;
+    uint64_t key[MAXJ];
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int e = lane + 64 * j;
+      const int ec = min(e, n - 1);
+      const float sel = row[ec] + bias[ec];
+      key[j] = e < n ? ((uint64_t)ord_f32(sel) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
+    }
+    float tk = 0.0f, tk1 = -INFINITY;
+    for (int r = 0; r < rounds; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) best = key[j] > best ? key[j] : best;
+      const uint64_t g = wave_max_key(best);
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j)
+        if (key[j] == g) key[j] = 0ull;
+      const float v = unord_f32((uint32_t)(g >> 32));
+      if (r == k - 1) tk = v;
+      if (r == k) tk1 = v;
+    }
+    if (lane == 0) thr[t] = make_float2(tk, tk1);
+  }
+}
+
+// Margin solve: one wavefront per expert; b_e <- fp32(b_e - (2 q_e - 1)) in
+// fp64, where q_e is the upper-(k/n) read of the expert's margin histogram.
+// Experts with an empty histogram keep their bias.
+__global__ __launch_bounds__(256) void qb_margin_solve_kernel(const int32_t *__restrict__ hist, int n, int nbins,
+                                                              int k, float *__restrict__ bias) {
+#pragma clang fp contract(off)
+  const int e = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (e >= n) return;  // wave-uniform
+  const double q = qb_read_wave(hist + (int64_t)e * nbins, nbins, (long long)k, (long long)n);
+  if (q != q) return;
+  if ((threadIdx.x & 63) == 0) bias[e] = (float)((double)bias[e] - (2.0 * q - 1.0));
+}
+
+// SignSGD-style step: work-group g counts the loads of experts 256 g .. + 255
+// over all T k top-k entries (LDS counters), then
+//   bias[e] += step * sign(T k - load_e * n)
+// (the comparison with the share T k / n is exact in integers; one fp32 add).
+__global__ __launch_bounds__(1024) void signsgd_kernel(const int32_t *__restrict__ idx, int64_t entries, int n,
+                                                       float step, float *__restrict__ bias) {
+  __shared__ int32_t cnt[256];
+  const int e0 = blockIdx.x * 256;
+  if (threadIdx.x < 256) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  for (int64_t i = threadIdx.x; i < entries; i += blockDim.x) {
+    const unsigned r = (unsigned)(idx[i] - e0);
+    if (r < 256u) atomicAdd(&cnt[r], 1);
+  }
+  __syncthreads();
+  const int e = e0 + (int)threadIdx.x;
+  if (threadIdx.x < 256 && e < n) {
+    const long long load = (long long)cnt[threadIdx.x] * n;
+    const float sg = entries > load ? step : (entries < load ? -step : 0.0f);
+    bias[e] = bias[e] + sg;
+  }
 }
 
 }  // namespace lmoe

@@ -52,7 +52,12 @@ def label(name):
                 f"epi={EPI[int(m.group(6))]} out=fp32 gather={int(m.group(7) == 'true')} "
                 f"grouped={int(m.group(8) == 'true')}")
     m = re.search(r"(\w+_kernel)", name)
-    return m.group(1) if m else name[:60]
+    if not m:
+        return name[:60]
+    lab = re.sub(r"^_ZN4lmoe\d+", "", m.group(1))  # drop the mangled namespace prefix
+    if lab == "qb_hist_kernel" and ("ILb1E" in name or "<true>" in name):
+        return "qb_hist_kernel (margin)"
+    return lab
 
 
 def stage(lab, name):
@@ -65,6 +70,10 @@ def stage(lab, name):
              ("combine", "combine + RMSNorm"),
              ("topk", "top-k + routing weights"),
              ("perm_", "permutation"),
+             ("(margin)", "QB margin form: histogram"),
+             ("qb_thresholds", "QB margin form: token thresholds"),
+             ("qb_margin_solve", "QB margin form: bias solve"),
+             ("signsgd", "fixed-step (SignSGD) bias update"),
              ("qb_hist", "QB histogram"),
              ("qb_pool", "QB pooled histogram"),
              ("qb_solve", "QB bias solve"),

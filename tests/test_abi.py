@@ -151,3 +151,24 @@ def test_static_forward_validation():
     assert call_s(c2dims(), dtype=9) == -3
     assert f(ctypes.byref(c2dims(T=0)), ctypes.byref(w), 1, None, None, None, None, None, None) == 0
     assert lmoe.strerror(-8).startswith("the call needs more scratch")
+
+
+def test_balancing_entry_points_validation():
+    """lmoe_qb_margin_update and lmoe_bias_signsgd validate before launching."""
+    q = lib().lmoe_qb_margin_update
+    assert q(FAKE, 10, 1025, 16, 1000, FAKE, 0, FAKE, 1, FAKE, 1 << 20, None) == -2   # n beyond the top-k kernels
+    assert q(FAKE, 10, 896, 897, 1000, FAKE, 0, FAKE, 1, FAKE, 1 << 20, None) == -2   # k > n
+    assert q(FAKE, 10, 896, 16, 0, FAKE, 0, FAKE, 1, FAKE, 1 << 20, None) == -7       # no bins
+    assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, None, 1, FAKE, 1 << 20, None) == -1    # bias is an input too
+    assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, FAKE, 1, None, 0, None) == -1          # thresholds need a workspace
+    assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, FAKE, 1, FAKE, 16, None) == -5
+    assert q(FAKE, 10, 896, 16, 1000, FAKE + 4, 0, FAKE, 1, FAKE, 1 << 20, None) == -4
+    assert lmoe.qb_margin_workspace_size(32768) == 32768 * 8 and lmoe.qb_margin_workspace_size(-1) == 0
+    g = lib().lmoe_bias_signsgd
+    assert g(FAKE, 10, 896, 16, float("inf"), FAKE, None) == -7
+    assert g(FAKE, 10, 896, 16, float("nan"), FAKE, None) == -7
+    assert g(FAKE, 10, 896, 0, 0.01, FAKE, None) == -2
+    assert g(FAKE, 10, 896, 16, 0.01, None, None) == -1
+    assert g(None, 10, 896, 16, 0.01, FAKE, None) == -1
+    assert g(FAKE, 10, 896, 16, 0.01, FAKE + 4, None) == -4
+    assert g(None, 0, 896, 16, 0.01, FAKE, None) == 0                                 # empty batch: no-op

@@ -12,8 +12,9 @@ What is checked at these sizes:
     oracle on the GPU's z and hidden;
   - z, s, v, y of sampled tokens against the oracle's forward on the GPU's
     routing (the outlier tokens, tokens owning sampled subtile rows);
-  - Quantile Balancing over 20 steps of the skewed workload: histogram and
-    bias bit-exact at every step against the oracle fed the GPU's scores.
+  - 20 bias-update steps of the skewed workload for Quantile Balancing, its
+    margin form and the K2-style fixed step: histogram and bias bit-exact at
+    every step against the oracle fed the GPU's scores (or top-k lists).
 """
 import numpy as np
 import pytest
@@ -206,18 +207,23 @@ def test_c4_skewed_forward_and_qb(k3_weights, host_cache):
     assert np.array_equal(bo[~edge], bg[~edge])
 
 
-def test_c4_qb_twenty_steps_per_step_parity(k3_weights, host_cache):
-    """The skewed workload's 20 Quantile Balancing steps ("Kimi K3 Architecture
-    Deep Dive" §3: histogram the scores, read each expert's quantile, set its
-    bias): forward with the current bias -> lmoe_qb_update -> next bias.  At
-    every step the histogram and the bias are bit-exact against the oracle fed
-    the GPU's fp32 scores, every token's list is a valid biased top-k of its own
-    scores, and on 64 sampled tokens the oracle router (on the GPU's z, with the
-    same bias) picks the same sets away from near-ties.  QB takes the max/mean
-    expert load from its skewed start to near balance."""
+@pytest.mark.parametrize("method", ["qb", "margin", "signsgd"])
+def test_c4_bias_updates_twenty_steps_per_step_parity(k3_weights, host_cache, method):
+    """The skewed workload's 20 bias-update steps: forward with the current bias
+    -> update -> next bias, for Quantile Balancing ("Kimi K3 Architecture Deep
+    Dive" §3: histogram the scores, read each expert's quantile, set its bias),
+    its margin form (LeiPhone report "Keeping the numbers in range": scores read
+    against each token's top-k threshold) and the K2-style fixed step it
+    replaces (step 1e-3; the pages give none).  At every step the histogram and
+    the bias are bit-exact against the oracle fed the GPU's fp32 scores (or, for
+    the fixed step, its top-k lists), every token's list is a valid biased top-k
+    of its own scores, and on 64 sampled tokens the oracle router (on the GPU's
+    z, with the same bias) picks the same sets away from near-ties.  Both QB
+    forms take the max/mean expert load from its skewed start to near balance."""
     cfg = synth.get_config("C4")
     dev = torch.device("cuda:0")
     T, n, k, nbins = cfg.T, cfg.n, cfg.k, cfg.nbins
+    step_size = 1e-3
     P = synth.HostParams(cfg, cache=host_cache)
     w_r, offset = P.w_router(), P.logit_offset()
     w = dict(k3_weights)
@@ -232,12 +238,11 @@ def test_c4_qb_twenty_steps_per_step_parity(k3_weights, host_cache):
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     s = torch.empty((T, n), dtype=torch.float32, device=dev)
     hist = torch.empty((n, nbins), dtype=torch.int32, device=dev)
-    qws = torch.empty(lmoe.qb_workspace_size(nbins), dtype=torch.uint8, device=dev)
     rng = np.random.default_rng(2024)
     t_s = tol(cfg.dtype)
     loads = []
     for t in range(cfg.qb_steps + 1):
-        print(f"C4 QB step {t}", flush=True)
+        print(f"C4 {method} step {t}", flush=True)
         x.copy_(synth.params.device_x(cfg, dev, step=t))
         lmoe.forward(x, w, k, y=y, topk_idx=idx, scores=s, workspace=ws)
         torch.cuda.synchronize()
@@ -248,22 +253,33 @@ def test_c4_qb_twenty_steps_per_step_parity(k3_weights, host_cache):
         rows = np.sort(rng.choice(T, 64, replace=False))
         z = z_view[torch.as_tensor(rows, device=dev)].double().cpu().numpy()
         so = ref.router_scores(z, w_r, offset)
-        label = f"C4 QB step {t} sampled s" if t in (0, cfg.qb_steps) else None
+        label = f"C4 {method} step {t} sampled s" if t in (0, cfg.qb_steps) else None
         assert rel_err(s_h[rows], so, label, t_s) <= t_s
         io, gap = ref.biased_topk(so, b_h.astype(np.float64), k)
         clear = gap >= GAP
         assert np.array_equal(np.sort(io[clear], 1), np.sort(i_h[rows][clear], 1)), f"step {t}: top-k sets differ"
         loads.append(np.bincount(i_h.ravel(), minlength=n))
-        if t < cfg.qb_steps:
-            lmoe.qb_update(s, k, hist, bias, workspace=qws)
-            torch.cuda.synchronize()
+        if t == cfg.qb_steps:
+            break
+        if method == "qb":
+            lmoe.qb_update(s, k, hist, bias)
             H, b_ref = ref.qb_update(s_h, nbins, k, bias=b_h)
+        elif method == "margin":
+            lmoe.qb_margin_update(s, k, hist, bias)
+            H, b_ref = ref.margin_update(s_h, nbins, k, b_h)
+        else:
+            lmoe.bias_signsgd(idx, n, step_size, bias)
+            H, b_ref = None, ref.signsgd_update(loads[-1], T, k, b_h, step_size)
+        torch.cuda.synchronize()
+        if H is not None:
             assert np.array_equal(hist.cpu().numpy(), H), f"step {t}: histogram differs"
-            assert np.array_equal(bias.cpu().numpy().view(np.uint32), b_ref.view(np.uint32)), f"step {t}: bias differs"
+        assert np.array_equal(bias.cpu().numpy().view(np.uint32), b_ref.view(np.uint32)), f"step {t}: bias differs"
     m0 = loads[0].max() / loads[0].mean()
     m20 = loads[-1].max() / loads[-1].mean()
-    print(f"C4 max/mean expert load: step 0 {m0:.3f}, step {cfg.qb_steps} {m20:.3f}")
-    assert m0 > 10.0 and m20 < 2.0
+    print(f"C4 {method}: max/mean expert load step 0 {m0:.3f}, step {cfg.qb_steps} {m20:.3f}")
+    assert m0 > 10.0
+    if method != "signsgd":
+        assert m20 < 2.0
 
 
 def test_odd_k_steps_on_the_load_to_lds_path():
