@@ -530,6 +530,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   };
 
   f32x16 acc[TM][TN];
+  bool skip_last = false;  // grouped: this wave's last M subtile is all padding in the current tile
 
   // One K step from LDS buffer `buf`: the fragments of 16-K group g+1 are read
   // while the MFMAs of group g run (two fragment register sets).
@@ -546,6 +547,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       }
 #pragma unroll
       for (int a = 0; a < TM; ++a) {
+        if (a == TM - 1 && skip_last) continue;
         const int r = (a * WM + wm) * 32 + l32;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) af[f][a][c] = *(const u32x4 *)(sA + swz(r, g * 2 * CPL + half * CPL + c));
@@ -554,9 +556,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     auto mma = [&](auto SC) {
       constexpr int f = decltype(SC)::value;
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
+      for (int a = 0; a < TM; ++a) {
+        if (a == TM - 1 && skip_last) continue;
 #pragma unroll
         for (int b = 0; b < TN; ++b) Mma<T>::run(bfg[f][b], af[f][a], acc[a][b]);
+      }
     };
     // interleave: one MFMA, then one LDS read of the next group's fragments
     auto interleave = [&]() {
@@ -652,6 +656,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     if (has_next) nxt = decode(lt_next);
     if (xnext) rows_of(nxt, n_row);
     const int nk = cur.nk;
+    // Grouped tiles are cut to their expert's rows, so the last M tile of an
+    // expert is often short: when this wave's last 32-row subtile holds only
+    // padding rows (never stored), its fragment reads and MFMAs are skipped
+    // (a wave-uniform branch; with ~146 rows per 192-row tile this removes a
+    // sixth of the routed MFMAs)
+    skip_last = GROUPED && TM > 1 && __builtin_amdgcn_readfirstlane(((TM - 1) * WM + wm) * 32 >= cur.rows ? 1 : 0) != 0;
 
 #pragma unroll
     for (int a = 0; a < TM; ++a)
