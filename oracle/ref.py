@@ -542,3 +542,135 @@ def margin_update(s32, nbins, k, bias, hist=None, accumulate=False, solve=True):
     H = Hb + np.asarray(hist, dtype=np.int64) if (accumulate and hist is not None) else Hb
     b = margin_solve(H, k, n, bias) if solve else None
     return H, b
+
+
+# ---------------------------------------------------------------------------
+# Backward pass  ([DD] §2, effect 6: with the norm before the up-projection the
+# up-projection's weight gradient takes the normalised form g (h / |h|_RMS)^T;
+# [DD] §1: the softcap's gradient, unlike a clip's, never vanishes abruptly)
+
+
+def softcap_grad(x, beta, gate="tanh"):
+    """d/dx of the branch cap: 1 - tanh^2(x / beta) for the softcap (1 at beta = +inf);
+    for the hard clip 1 inside (-beta, beta) and 0 outside."""
+    x = np.asarray(x, dtype=np.float64)
+    if gate == "clip":
+        return (np.abs(x) < beta).astype(np.float64)
+    if beta == np.inf:
+        return np.ones_like(x)
+    t = np.tanh(x / beta)
+    return 1.0 - t * t
+
+
+def situ_grad(x, beta, gate="tanh"):
+    """d/dx SiTU(x; beta) = cap'(x) sigmoid(x) + cap(x) sigmoid(x) (1 - sigmoid(x))."""
+    sg = sigmoid(x)
+    return softcap_grad(x, beta, gate) * sg + cap(x, beta, gate) * sg * (1.0 - sg)
+
+
+def backward(x, P, k, n_shared, dtype, dy, beta1=4.0, beta2=25.0, eps=1e-6, forced_idx=None, gate="tanh",
+             norm="rms"):
+    """Gradients of the layer for the upstream gradient dy [T, d] of y.
+
+    The forward is recomputed as `forward` computes it (z, a, v rounded where it
+    stores them).  The backward stores, in the work dtype, the tensors that feed
+    a matrix product: the latent gradient du (and g du, the routed rows'
+    output gradient), the gated hidden's gradient da, the gate inputs'
+    gradients dp1, dp2, the router logits' gradient dl and the latent's
+    gradient dz; every product is then taken in fp64 of those rounded values.
+    dv, the norm's backward and the routing weights' gradient stay unrounded.
+    Steps (chain rule, the forward's notation):
+      dv = dy W_up;  dW_up = dy^T v
+      norm "rms": u_hat = u / r, r = sqrt(mean(u^2) + eps); dgamma = sum_i dv (.) u_hat;
+                  du = (gamma (.) dv - u_hat mean(gamma (.) dv (.) u_hat)) / r
+      norm "none": du = dv
+      routed row (token i, slot j, expert e): o = a W3_e^T; dg_ij = du_i . o;
+                  da = rnd(g_ij du_i) W3_e;  dW3_e += rnd(g du_i)^T a
+      shared expert s: da = rnd(du_i) W3s_s;  dW3s_s += rnd(du_i)^T a
+      gate: dp1 = rnd(da) C(p2) SiTU'(p1);  dp2 = rnd(da) SiTU(p1) C'(p2)
+            with p1 = z W1^T, p2 = z W2^T recomputed from the stored z
+      dz_i += rnd(dp1) W1_e + rnd(dp2) W2_e;  dW1_e += rnd(dp1)^T z;  dW2_e += rnd(dp2)^T z
+      router, chosen experts only (selection is not differentiable; the bias b
+      gets no gradient): g_j = s_j / S, S = sum_j s_j:
+            ds_j = (dg_j - sum_j' dg_j' g_j') / S;  dl_j = ds_j s_j (1 - s_j)
+            dz += rnd(dl) W_r;  dW_r = rnd(dl)^T z
+      dx = rnd(dz) W_down;  dW_down = rnd(dz)^T x
+    Returns a dict with the weight gradients (dw_down [L, d], dw_router [n, L],
+    dw1, dw2 [n, D, L], dw3 [n, L, D], dws1, dws2 [n_s, D, L], dws3 [n_s, L, D],
+    dgamma [L], dw_up [d, L]), dx [T, d] and the intermediates (dv, du, dz, dl
+    [T, n] dense with zeros off the chosen experts), each also before its own
+    store rounding where it has one (*_pre).
+    READING: norm "both" (the extra norm on z) has no backward here.
+    """
+    if norm not in ("rms", "none"):
+        raise ValueError(f"backward has no norm {norm!r}")
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    fw = forward(x, P, k, n_shared, dtype, beta1, beta2, eps, forced_idx=forced_idx, gate=gate, norm=norm)
+    z, s, idx, g, u, v = fw["z"], fw["s"], fw["idx"], fw["g"], fw["u"], fw["v"]
+    T, L = z.shape
+    n = s.shape[1]
+    w_up = P.w_up()
+    dv = dy @ w_up
+    dw_up = dy.T @ v
+    if norm == "rms":
+        gamma = P.gamma()
+        r = np.sqrt(np.mean(u * u, axis=1, keepdims=True) + eps)
+        uh = u / r
+        dgamma = np.sum(dv * uh, axis=0)
+        dh = gamma[None, :] * dv
+        du = (dh - uh * np.mean(dh * uh, axis=1, keepdims=True)) / r
+    else:
+        dgamma = np.zeros(L)
+        du = dv
+    du_r = round_to(du, dtype)
+    counts, offs, row_token, row_slot = dispatch(idx, n)
+    dz = np.zeros((T, L))
+    dg = np.zeros_like(g)
+    D = P.w1(0).shape[0]
+    dw1 = np.zeros((n, D, L))
+    dw2 = np.zeros((n, D, L))
+    dw3 = np.zeros((n, L, D))
+
+    def expert_back(zr, w1, w2, w3, dout):
+        p1 = zr @ w1.T
+        p2 = zr @ w2.T
+        a = round_to(situ_glu_hidden(p1, p2, beta1, beta2, gate), dtype)
+        da = round_to(dout @ w3, dtype)
+        dp1 = round_to(da * cap(p2, beta2, gate) * situ_grad(p1, beta1, gate), dtype)
+        dp2 = round_to(da * situ(p1, beta1, gate) * softcap_grad(p2, beta2, gate), dtype)
+        return a, dp1 @ w1 + dp2 @ w2, dp1.T @ zr, dp2.T @ zr, dout.T @ a
+
+    for e in range(n):
+        lo, hi = offs[e], offs[e + 1]
+        if lo == hi:
+            continue
+        toks, slots = row_token[lo:hi], row_slot[lo:hi]
+        w1, w2, w3 = P.w1(e), P.w2(e), P.w3(e)
+        gr = g[toks, slots]
+        dout = round_to(gr[:, None] * du[toks], dtype)
+        a, dzr, dw1[e], dw2[e], dw3[e] = expert_back(z[toks], w1, w2, w3, dout)
+        dg[toks, slots] = np.sum(du[toks] * (a @ w3.T), axis=1)
+        np.add.at(dz, toks, dzr)
+    dws1 = np.zeros((n_shared, D, L))
+    dws2 = np.zeros((n_shared, D, L))
+    dws3 = np.zeros((n_shared, L, D))
+    for j in range(n_shared):
+        _, dzr, dws1[j], dws2[j], dws3[j] = expert_back(z, P.ws1(j), P.ws2(j), P.ws3(j), du_r)
+        dz += dzr
+    # router: g = s_K / S over the chosen experts
+    sk = np.take_along_axis(s, idx, axis=1)
+    S = sk.sum(axis=1, keepdims=True)
+    dsk = (dg - np.sum(dg * g, axis=1, keepdims=True)) / S
+    dl_pre = np.zeros((T, n))
+    np.put_along_axis(dl_pre, idx, dsk * sk * (1.0 - sk), axis=1)
+    dl = round_to(dl_pre, dtype)
+    w_r = P.w_router()
+    dz += dl @ w_r
+    dw_router = dl.T @ z
+    dz_r = round_to(dz, dtype)
+    dx = dz_r @ P.w_down()
+    dw_down = dz_r.T @ x
+    return dict(dx=dx, dw_down=dw_down, dw_router=dw_router, dw1=dw1, dw2=dw2, dw3=dw3, dws1=dws1, dws2=dws2,
+                dws3=dws3, dgamma=dgamma, dw_up=dw_up, dv=dv, du=du_r, du_pre=du, dz=dz_r, dz_pre=dz, dl=dl,
+                dl_pre=dl_pre, dg=dg, fw=fw)
