@@ -584,9 +584,10 @@ def backward(x, P, k, n_shared, dtype, dy, beta1=4.0, beta2=25.0, eps=1e-6, forc
       norm "rms": u_hat = u / r, r = sqrt(mean(u^2) + eps); dgamma = sum_i dv (.) u_hat;
                   du = (gamma (.) dv - u_hat mean(gamma (.) dv (.) u_hat)) / r
       norm "none": du = dv
-      routed row (token i, slot j, expert e): o = a W3_e^T; dg_ij = du_i . o;
-                  da = rnd(g_ij du_i) W3_e;  dW3_e += rnd(g du_i)^T a
-      shared expert s: da = rnd(du_i) W3s_s;  dW3s_s += rnd(du_i)^T a
+      routed row (token i, slot j, expert e), with du stored as rnd(du):
+                  o = a W3_e^T; dg_ij = du_i . o (unrounded du);
+                  da = rnd(g_ij (rnd(du_i) W3_e));  dW3_e += rnd(g rnd(du_i))^T a
+      shared expert s: da = rnd(rnd(du_i) W3s_s);  dW3s_s += rnd(du_i)^T a
       gate: dp1 = rnd(da) C(p2) SiTU'(p1);  dp2 = rnd(da) SiTU(p1) C'(p2)
             with p1 = z W1^T, p2 = z W2^T recomputed from the stored z
       dz_i += rnd(dp1) W1_e + rnd(dp2) W2_e;  dW1_e += rnd(dp1)^T z;  dW2_e += rnd(dp2)^T z
@@ -632,11 +633,12 @@ def backward(x, P, k, n_shared, dtype, dy, beta1=4.0, beta2=25.0, eps=1e-6, forc
     dw2 = np.zeros((n, D, L))
     dw3 = np.zeros((n, L, D))
 
-    def expert_back(zr, w1, w2, w3, dout):
+    def expert_back(zr, w1, w2, w3, du_rows, gr):
         p1 = zr @ w1.T
         p2 = zr @ w2.T
         a = round_to(situ_glu_hidden(p1, p2, beta1, beta2, gate), dtype)
-        da = round_to(dout @ w3, dtype)
+        da = round_to(gr[:, None] * (du_rows @ w3), dtype)
+        dout = round_to(gr[:, None] * du_rows, dtype)
         dp1 = round_to(da * cap(p2, beta2, gate) * situ_grad(p1, beta1, gate), dtype)
         dp2 = round_to(da * situ(p1, beta1, gate) * softcap_grad(p2, beta2, gate), dtype)
         return a, dp1 @ w1 + dp2 @ w2, dp1.T @ zr, dp2.T @ zr, dout.T @ a
@@ -648,15 +650,14 @@ def backward(x, P, k, n_shared, dtype, dy, beta1=4.0, beta2=25.0, eps=1e-6, forc
         toks, slots = row_token[lo:hi], row_slot[lo:hi]
         w1, w2, w3 = P.w1(e), P.w2(e), P.w3(e)
         gr = g[toks, slots]
-        dout = round_to(gr[:, None] * du[toks], dtype)
-        a, dzr, dw1[e], dw2[e], dw3[e] = expert_back(z[toks], w1, w2, w3, dout)
+        a, dzr, dw1[e], dw2[e], dw3[e] = expert_back(z[toks], w1, w2, w3, du_r[toks], gr)
         dg[toks, slots] = np.sum(du[toks] * (a @ w3.T), axis=1)
         np.add.at(dz, toks, dzr)
     dws1 = np.zeros((n_shared, D, L))
     dws2 = np.zeros((n_shared, D, L))
     dws3 = np.zeros((n_shared, L, D))
     for j in range(n_shared):
-        _, dzr, dws1[j], dws2[j], dws3[j] = expert_back(z, P.ws1(j), P.ws2(j), P.ws3(j), du_r)
+        _, dzr, dws1[j], dws2[j], dws3[j] = expert_back(z, P.ws1(j), P.ws2(j), P.ws3(j), du_r, np.ones(T))
         dz += dzr
     # router: g = s_K / S over the chosen experts
     sk = np.take_along_axis(s, idx, axis=1)
