@@ -261,6 +261,55 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
  * histogram, int64 [nbins]); 0 for an invalid nbins. */
 size_t lmoe_qb_workspace_size(int32_t nbins);
 
+/* Gradients of the layer (device pointers, work dtype, overwritten).  Shapes as
+ * the weights they belong to; dws* NULL iff n_shared == 0. */
+typedef struct {
+  void *dx;          /* [T, d]        gradient of the input x                    */
+  void *dw_down;     /* [L, d]                                                   */
+  void *dw_router;   /* [n, L]                                                   */
+  void *dw1, *dw2;   /* [n, D, L]                                                */
+  void *dw3;         /* [n, L, D]                                                */
+  void *dws1, *dws2; /* [n_shared, D, L]                                         */
+  void *dws3;        /* [n_shared, L, D]                                         */
+  void *dgamma;      /* [L]           gradient of rms_gain                       */
+  void *dw_up;       /* [d, L]                                                   */
+} lmoe_grads;
+
+/* Bytes of device workspace lmoe_backward needs (0 for invalid dims or dtype,
+ * or a latent width above 4096). */
+size_t lmoe_backward_workspace_size(const lmoe_dims *dims, int dtype);
+
+/* Backward pass of the layer ("Kimi K3 Architecture Deep Dive" §1: the capped
+ * gate SiTU(x1) softcap(x2); §2: the norm before the up-projection, whose
+ * weight gradient takes the normalised form g (h / |h|_RMS)^T): the gradients
+ * of x and of every weight for the upstream gradient dy [T, d] of y.
+ * Call after lmoe_forward on the same stream, with the same dims, weights,
+ * dtype and x, passing that forward's topk_idx, topk_w and scores outputs (all
+ * required) and its workspace, untouched since (it holds z, the routing, the
+ * gated hidden, the staged expert rows and v).  Steps, with the forward's
+ * notation, r the token's RMS and u_hat = u / r:
+ *   dv = dy w_up;  dw_up = dy^T v;  dgamma = sum_i dv (.) u_hat
+ *   du = (gamma (.) dv - u_hat mean(gamma (.) dv (.) u_hat)) / r   (LMOE_NORM_RMS;
+ *        du = dv with LMOE_NORM_NONE)
+ *   per expert row (token i, weight g; shared rows g = 1):
+ *     da  = g (du_i W3_e);  dw3_e += (g du_i)^T a
+ *     dp1 = da C(p2) SiTU'(p1),  dp2 = da SiTU(p1) C'(p2)  (p1, p2 recomputed
+ *           from z; C the branch cap, C'(x) = 1 - tanh^2(x / beta), or 1 inside
+ *           the clip's range and 0 outside)
+ *     dz_i += dp1 W1_e + dp2 W2_e;  dw1_e += dp1^T z_i;  dw2_e += dp2^T z_i
+ *   router, chosen experts only (the selection and the bias have no gradient):
+ *     dg_j = du_i . o_j;  ds_j = (dg_j - sum_j' dg_j' g_j') / S;
+ *     dl_j = ds_j s_j (1 - s_j);  dz += dl w_router;  dw_router = dl^T z
+ *   dx = dz w_down;  dw_down = dz^T x
+ * du, g du, da, dp1, dp2, dl and dz are stored in the work dtype between steps;
+ * sums run in fp32.  Restrictions: LMOE_NORM_BOTH is not supported
+ * (LMOE_ERR_VALUE); L <= 4096 (LMOE_ERR_SHAPE).  T == 0 writes zero weight
+ * gradients.  workspace: lmoe_backward_workspace_size() bytes. */
+int lmoe_backward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, const void *dy,
+                  const int32_t *topk_idx, const float *topk_w, const float *scores, const void *fwd_workspace,
+                  size_t fwd_workspace_bytes, const lmoe_grads *grads, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
 /* Margin form of the Quantile Balancing update ("Kimi K3 Architecture Deep
  * Dive" §3; LeiPhone report "Keeping the numbers in range": the router scores
  * are read against each token's top-k threshold to estimate where each

@@ -9,11 +9,11 @@ import ctypes
 
 import torch
 
-from ._abi import (Dims, Weights, GATES, NORMS, LMOE_BF16, LMOE_F32, WS_REGIONS, EXPORTS, N_STAGES, STAGES, lib,  # noqa: F401
+from ._abi import (Dims, Weights, Grads, GRAD_FIELDS, GATES, NORMS, LMOE_BF16, LMOE_F32, WS_REGIONS, EXPORTS, N_STAGES, STAGES, lib,  # noqa: F401
                    STATIC_SCRATCH_BYTES,
                    check, strerror)
 
-__all__ = ["dims_of", "workspace_size", "workspace_view", "forward", "forward_static", "qb_update", "qb_workspace_size",
+__all__ = ["dims_of", "workspace_size", "workspace_view", "forward", "forward_static", "backward", "backward_workspace_size", "qb_update", "qb_workspace_size",
            "qb_margin_update", "qb_margin_workspace_size", "bias_signsgd",
            "strerror", "make_workspace"]
 
@@ -129,6 +129,36 @@ def forward_static(x, weights, k, y=None, topk_idx=None, topk_w=None, scores=Non
                                    _ptr(scores), stream)
     check(rc, "lmoe_forward_static")
     return y
+
+
+def backward_workspace_size(dims, dtype):
+    return int(lib().lmoe_backward_workspace_size(dims, _dtype_code(dtype) if isinstance(dtype, torch.dtype) else dtype))
+
+
+def backward(x, dy, weights, k, topk_idx, topk_w, scores, fwd_workspace, grads=None, workspace=None, beta1=4.0,
+             beta2=25.0, eps=1e-6, stream=None, gate="tanh", norm="rms"):
+    """Gradients of the layer for dy via lmoe_backward, after a forward on the same stream that
+    returned topk_idx, topk_w and scores and used fwd_workspace (untouched since).  Returns a dict
+    of gradient tensors (allocated here unless given): dx and one per weight (dw_down,
+    dw_router, dw1, dw2, dw3, dws1, dws2, dws3 when there are shared experts, dgamma, dw_up)."""
+    dims = dims_of(x, weights, k)
+    if grads is None:
+        like = {"dx": x, "dw_down": weights["w_down"], "dw_router": weights["w_router"], "dw1": weights["w1"],
+                "dw2": weights["w2"], "dw3": weights["w3"], "dws1": weights.get("ws1"),
+                "dws2": weights.get("ws2"), "dws3": weights.get("ws3"), "dgamma": weights["rms_gain"],
+                "dw_up": weights["w_up"]}
+        grads = {kk: (None if t is None else torch.empty_like(t)) for kk, t in like.items()}
+    if workspace is None:
+        workspace = torch.empty(max(backward_workspace_size(dims, x.dtype), 256), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    W = _weights_struct(weights, beta1, beta2, eps, gate, norm)
+    G = Grads(*[_ptr(grads.get(f)) for f in GRAD_FIELDS])
+    rc = lib().lmoe_backward(dims, W, _dtype_code(x.dtype), _ptr(x), _ptr(dy), _ptr(topk_idx), _ptr(topk_w),
+                             _ptr(scores), _ptr(fwd_workspace), fwd_workspace.numel(), G, _ptr(workspace),
+                             workspace.numel(), stream)
+    check(rc, "lmoe_backward")
+    return grads
 
 
 def qb_workspace_size(nbins):

@@ -18,6 +18,7 @@ WS_REGIONS = {"z": 0, "counts": 1, "offs": 2, "row_token": 3, "row_slot": 4, "hi
 
 # every function the header declares
 EXPORTS = ("lmoe_workspace_size", "lmoe_workspace_offset", "lmoe_forward", "lmoe_forward_timed", "lmoe_forward_static",
+           "lmoe_backward", "lmoe_backward_workspace_size",
            "lmoe_qb_update", "lmoe_qb_workspace_size", "lmoe_qb_margin_update", "lmoe_qb_margin_workspace_size",
            "lmoe_bias_signsgd", "lmoe_strerror")
 
@@ -34,6 +35,13 @@ class Weights(ctypes.Structure):
                                                "w2", "w3", "ws1", "ws2", "ws3", "rms_gain", "w_up")] + \
                [("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("gate", ctypes.c_int32), ("norm", ctypes.c_int32)]
+
+GRAD_FIELDS = ("dx", "dw_down", "dw_router", "dw1", "dw2", "dw3", "dws1", "dws2", "dws3", "dgamma", "dw_up")
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in GRAD_FIELDS]
+
 
 GATES = {"tanh": 0, "clip": 1}  # lmoe_gate
 NORMS = {"rms": 0, "none": 1, "both": 2}   # lmoe_norm
@@ -66,6 +74,12 @@ def lib():
         L.lmoe_forward_static.restype = ctypes.c_int
         L.lmoe_forward_static.argtypes = [P(Dims), P(Weights), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.lmoe_backward_workspace_size.restype = ctypes.c_size_t
+        L.lmoe_backward_workspace_size.argtypes = [P(Dims), ctypes.c_int]
+        L.lmoe_backward.restype = ctypes.c_int
+        L.lmoe_backward.argtypes = [P(Dims), P(Weights), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_size_t, P(Grads), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.lmoe_qb_update.restype = ctypes.c_int
         L.lmoe_qb_update.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,

@@ -34,14 +34,18 @@
 
 namespace lmoe {
 
-enum { EPI_STORE = 0, EPI_SIGMOID = 1, EPI_GLU = 2, EPI_ROWSCALE = 3, EPI_PARTIAL = 4, EPI_GLU_CLIP = 5 };
+enum { EPI_STORE = 0, EPI_SIGMOID = 1, EPI_GLU = 2, EPI_ROWSCALE = 3, EPI_PARTIAL = 4, EPI_GLU_CLIP = 5,
+       EPI_GLU_BWD = 6, EPI_GLU_CLIP_BWD = 7 };
 
 // Both gated epilogues: EPI_GLU caps its branches with the tanh softcap,
 // EPI_GLU_CLIP with the hard clip clamp(x; beta) = min(max(x, -beta), beta) that
 // the softcap replaces at the same ceilings (the cap ablation; "Kimi K3
 // Architecture Deep Dive" §1).  The clamp keeps NaN (its comparisons fail).
 template <int EPI>
-constexpr bool is_glu = EPI == EPI_GLU || EPI == EPI_GLU_CLIP;
+constexpr bool is_glu_bwd = EPI == EPI_GLU_BWD || EPI == EPI_GLU_CLIP_BWD;
+// every epilogue that takes W1 and W2 products of the same hidden units
+template <int EPI>
+constexpr bool is_glu = EPI == EPI_GLU || EPI == EPI_GLU_CLIP || is_glu_bwd<EPI>;
 
 LMOE_DEV float clampf_(float x, float beta) { return x < -beta ? -beta : (x > beta ? beta : x); }
 
@@ -51,6 +55,31 @@ LMOE_DEV float glu_(float x1, float x2, float beta1, float beta2) {
     return clampf_(x1, beta1) * sigmoid_hw(x1) * clampf_(x2, beta2);
   else
     return situf_(x1, beta1) * softcapf_(x2, beta2);
+}
+
+// Backward of the gate a = SiTU(x1) C(x2) (C the branch cap): given da,
+//   dx1 = da C(x2) SiTU'(x1),  dx2 = da SiTU(x1) C'(x2),
+// SiTU'(x) = C'(x) sigmoid(x) + C(x) sigmoid(x) (1 - sigmoid(x)); the softcap's
+// C'(x) = 1 - tanh^2(x / beta) = 1 - (C(x) / beta)^2, the clip's 1 inside
+// (-beta, beta) and 0 outside.
+template <int EPI>
+LMOE_DEV void glu_bwd_(float x1, float x2, float da, float beta1, float beta2, float &dx1, float &dx2) {
+  const float sg = sigmoid_hw(x1);
+  float c1, c2, g1, g2;
+  if constexpr (EPI == EPI_GLU_CLIP_BWD) {
+    c1 = clampf_(x1, beta1);
+    c2 = clampf_(x2, beta2);
+    g1 = fabsf(x1) < beta1 ? 1.0f : 0.0f;
+    g2 = fabsf(x2) < beta2 ? 1.0f : 0.0f;
+  } else {
+    c1 = softcapf_(x1, beta1);
+    c2 = softcapf_(x2, beta2);
+    const float t1 = c1 * (1.0f / beta1), t2 = c2 * (1.0f / beta2);
+    g1 = 1.0f - t1 * t1;
+    g2 = 1.0f - t2 * t2;
+  }
+  dx1 = da * c2 * (g1 * sg + c1 * sg * (1.0f - sg));
+  dx2 = da * (c1 * sg) * g2;
 }
 
 struct GemmArgs {
@@ -81,6 +110,15 @@ struct GemmArgs {
   int ksteps;               // K steps per range
   int b_split_row;          // EPI_PARTIAL: B rows >= this come from B2
   int32_t *sched;           // GROUPED: 8 tile counters, zero at launch (null: static tile walk)
+  const void *aux;          // EPI_GLU_BWD: da [rows, N/2] (work dtype), row stride ldaux
+  int64_t ldaux;
+  int krange;               // GROUPED K-range mode: table entry e = {group, first K step, K steps, 0};
+                            //   every entry covers cdiv(M, BM) x kr_tn tiles of the same A and B
+                            //   (rows of A from 0, its K range from the entry), written to
+                            //   C + group * c_group_stride (group >= n_routed: Csh + ...)
+  int kr_tn;                // K-range: N tiles per entry
+  void *Csh;
+  int64_t c_group_stride;
 };
 
 template <typename T> struct Mma;
@@ -121,18 +159,33 @@ template <int V> struct IC { static constexpr int value = V; };
 // (grouped: one expert's), N tile nt, split ks covering K steps [kbeg, kbeg + nk).
 struct TileI {
   const void *B, *B2;
+  void *C;  // output matrix of the tile
   int64_t m0;
   int rows, nt, ks, kbeg, nk;
 };
 
 // Logical tile l -> TileI.  Grouped: entry l / tiles_n of the device tile table.
 // Dense: split-major, then groups of 8 M tiles walked down before across.
-template <typename T, int BM, bool GROUPED>
+template <typename T, typename TOut, int BM, bool GROUPED>
 LMOE_DEV TileI decode_tile(const GemmArgs &p, int l, int nk_all) {
   TileI t;
   t.ks = 0;
   t.B = p.B;
   t.B2 = p.B2;
+  t.C = p.C;
+  if (GROUPED && p.krange) {
+    const int j = l / p.tiles_n, r = l % p.tiles_n;
+    const int4 e = p.tiles[j];
+    const int mt = r / p.kr_tn;
+    t.nt = r % p.kr_tn;
+    t.m0 = (int64_t)mt * BM;
+    t.rows = min(BM, p.M - (int)t.m0);
+    t.kbeg = e.y;
+    t.nk = e.z;
+    t.C = e.x >= p.n_routed ? (void *)((TOut *)p.Csh + (int64_t)(e.x - p.n_routed) * p.c_group_stride)
+                            : (void *)((TOut *)p.C + (int64_t)e.x * p.c_group_stride);
+    return t;
+  }
   if (GROUPED) {
     const int j = l / p.tiles_n;
     t.nt = l % p.tiles_n;
@@ -175,15 +228,15 @@ LMOE_DEV TileI decode_tile(const GemmArgs &p, int l, int nk_all) {
 // lines.
 template <typename TO, int EPI, int WTN, int TN>
 struct StagedStore {
-  static constexpr bool value = (EPI == EPI_ROWSCALE || EPI == EPI_STORE || is_glu<EPI>) &&
+  static constexpr bool value = (EPI == EPI_ROWSCALE || EPI == EPI_STORE || (is_glu<EPI> && !is_glu_bwd<EPI>)) &&
                                 sizeof(TO) == 2 && WTN == 64 && TN == 2;
 };
 constexpr int STAGE_BYTES_PER_WAVE = 32 * 128;
 
 template <typename TO, int EPI, int BN, int WTN, int WM, int TM, int TN>
-LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, int rows_valid, int nt, int ks,
-                         int wm, int wn, int half, int l32, unsigned char *stage) {
-  TO *C = (TO *)p.C;
+LMOE_DEV void store_tile(const GemmArgs &p, void *Cout, f32x16 (&acc)[TM][TN], int64_t m0, int rows_valid, int nt,
+                         int ks, int wm, int wn, int half, int l32, unsigned char *stage) {
+  TO *C = (TO *)Cout;
   if constexpr (StagedStore<TO, EPI, WTN, TN>::value) {
     constexpr bool GLU = is_glu<EPI>;
     constexpr int CPR = GLU ? 4 : 8;  // 16-byte chunks per staged row (32 or 64 outputs)
@@ -255,7 +308,24 @@ LMOE_DEV void store_tile(const GemmArgs &p, f32x16 (&acc)[TM][TN], int64_t m0, i
     const float rs = (EPI == EPI_ROWSCALE) ? p.row_scale[grow] : 1.0f;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      if (is_glu<EPI>) {
+      if (is_glu_bwd<EPI>) {
+        // gate backward: dx1 into columns [0, H), dx2 into [H, 2H) of the output
+        const int64_t H = p.N / 2;
+#pragma unroll
+        for (int b = 0; b < TN; b += 2) {
+          const int64_t h0 = (int64_t)nt * (BN / 2) + wn * (WTN / 2) + (b / 2) * 32 + g * 8 + half * 4;
+          const TO *dap = (const TO *)p.aux + grow * p.ldaux + h0;
+          TO *dst = C + grow * p.ldc + h0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (h0 + c >= H) continue;
+            float d1, d2;
+            glu_bwd_<EPI>(acc[a][b][4 * g + c], acc[a][b + 1][4 * g + c], to_f32(dap[c]), p.beta1, p.beta2, d1, d2);
+            dst[c] = from_f32<TO>(d1);
+            dst[H + c] = from_f32<TO>(d2);
+          }
+        }
+      } else if (is_glu<EPI>) {
 #pragma unroll
         for (int b = 0; b < TN; b += 2) {
           const int64_t h0 = (int64_t)nt * (BN / 2) + wn * (WTN / 2) + (b / 2) * 32 + g * 8 + half * 4;
@@ -412,7 +482,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   };
   int q_next = -1;  // dyn: the tile after the current one (-1: none)
   if (GROUPED && dyn) {
-    if (tid == 0) qslot[0] = grab();
+    if (tid == 0) {
+      qslot[0] = grab();
+      qslot[1] = -1;
+    }
     __syncthreads();
     q_next = qslot[0];
     __syncthreads();
@@ -420,7 +493,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   int tile_par = 0;  // dyn: parity of the tile count, selects the LDS slot
 
   const int nk_all = p.K / BKE;
-  auto decode = [&](int l) { return decode_tile<T, BM, GROUPED>(p, l, nk_all); };
+  auto decode = [&](int l) { return decode_tile<T, TO, BM, GROUPED>(p, l, nk_all); };
 
   // ---- per-thread source rows of the tile being loaded (32-bit row indices;
   // addresses are formed per K step).  Rows past the valid range are clamped
@@ -760,15 +833,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     }
 
     // published after step 0 of this tile; the slot is rewritten two tiles later,
-    // past a barrier every thread reaches only after this read
+    // past a barrier every thread reaches only after this read.  A K-range tile
+    // without K steps (an expert with no rows) has no step 0: it publishes here
+    // (nk is uniform over the work-group, so the barrier is too).
     if (GROUPED && dyn) {
+      if (nk == 0) {
+        if (tid == 0) qslot[tile_par] = grabbed;
+        __syncthreads();
+      }
       q_next = qslot[tile_par];
       tile_par ^= 1;
     }
 
     // ---- epilogue
-    if constexpr (BDMA) sE = sB0 + ((gbase + nk - 1) % NSB) * BN * 128 + (threadIdx.x >> 6) * STAGE_BYTES_PER_WAVE;
-    store_tile<TO, EPI, BN, WTN, WM, TM, TN>(p, acc, cur.m0, cur.rows, cur.nt, cur.ks, wm, wn, half, l32, sE);
+    // (a K-range tile may have no K step at all: its zero tile is still stored)
+    if constexpr (BDMA) sE = sB0 + ((gbase + nk + NSB - 1) % NSB) * BN * 128 + (threadIdx.x >> 6) * STAGE_BYTES_PER_WAVE;
+    store_tile<TO, EPI, BN, WTN, WM, TM, TN>(p, cur.C, acc, cur.m0, cur.rows, cur.nt, cur.ks, wm, wn, half, l32, sE);
     if constexpr (BDMA && STAGED) {
       // the next tile's first step loads B into the stage used for staging
       __builtin_amdgcn_s_waitcnt((7 << 4) | 0xF | (3 << 14));  // lgkmcnt(0) only

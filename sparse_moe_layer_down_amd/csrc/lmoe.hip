@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "../../include/lmoe.h"
+#include "bwd.hpp"
 #include "gemm.hpp"
 #include "norm.hpp"
 #include "qb.hpp"
@@ -228,6 +229,10 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   const int occ = pd.occ;
   constexpr int bke = 128 / (int)sizeof(T);
   a.tiles_n = (int)cdiv(a.N, C::BN);
+  if (GROUPED && a.krange) {  // every K-range entry covers all M x N tiles of its group
+    a.kr_tn = a.tiles_n;
+    a.tiles_n *= (int)cdiv(a.M, C::BM);
+  }
   if (!GROUPED) a.tiles_m = (int)cdiv(a.M, C::BM);
   a.n_logical = a.tiles_m * a.tiles_n * (GROUPED ? 1 : std::max(a.splits, 1));
   if (a.n_logical == 0) return hipSuccess;
@@ -235,7 +240,7 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   // cross-tile prefetch needs every tile's step count to be a multiple of 2 (LDS
   // buffer parity) and of the number of register sets
   constexpr int xm = (C::PF % 2 == 0) ? C::PF : 2 * C::PF;
-  a.xpf = (nk_all % xm == 0) && (a.splits <= 1 || a.ksteps % xm == 0);
+  a.xpf = !a.krange && (nk_all % xm == 0) && (a.splits <= 1 || a.ksteps % xm == 0);
   int64_t grid = std::min<int64_t>(a.n_logical, (int64_t)device_cus() * occ);
   if (grid >= 8) grid = grid / 8 * 8;
   if (a.kb_len == 0) a.kb_len = a.K;
@@ -460,6 +465,329 @@ hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass.  Operands whose contraction dimension is not contiguous are
+// transposed first (weights once per call, activations per call), so every
+// product runs in the same C = A B^T MFMA GEMM as the forward:
+//   dv = dy W_up;  dW_up = dy^T v                         (dense)
+//   norm backward -> du, dg; gain gradient; router backward -> dl
+//   da = g (du W3_e)             grouped over expert rows, du rows gathered
+//   dp1, dp2 = gate backward     the W1/W2 products recomputed from the stored z
+//   dz rows = dp1 W1_e + dp2 W2_e   grouped; + dl W_r; summed per token -> dz
+//   dx = dz W_down;  dW_down = dz^T x;  dW_r = dl^T z     (dense)
+//   dW1_e = dp1^T z, dW2_e = dp2^T z, dW3_e = (g du)^T a   one K-range GEMM each:
+//                                rows gathered and transposed per expert segment
+constexpr int BWD_SCHED = 3 * SCHED_COUNTERS;  // tile counters of the three K-range GEMMs
+
+enum {
+  B_WUPT = 0, B_WDOWNT, B_WRT, B_W3T, B_W12T, B_DV, B_DU32, B_DU, B_PROD, B_DG, B_DL, B_DA, B_DP, B_DZROWS, B_DZ,
+  B_DYT, B_VT, B_DZT, B_XT, B_ZT, B_DLT, B_ZTG, B_DOT, B_DPT, B_AT, B_ENTRIES, B_BLOCKS, B_NB, B_SCHED, B_SCHED2,
+  B_PART, B_COUNT_
+};
+
+struct BwdDims {
+  int64_t Tp, np, R, kblocks, Kmax;
+};
+BwdDims bwd_dims(const lmoe_dims &d) {
+  BwdDims b;
+  b.Tp = cdiv(d.T, 64) * 64;
+  b.np = cdiv(d.n, 64) * 64;
+  b.R = expert_rows(d);
+  // 64-row blocks of the experts' segments (each padded to whole blocks), plus
+  // one spare block: a tile of an empty segment still loads one step
+  b.kblocks = cdiv(b.R, 64) + d.n + d.n_shared;
+  b.Kmax = (b.kblocks + 1) * 64;
+  return b;
+}
+
+WsLayout bwd_layout(const lmoe_dims &d, int dtype) {
+  const int64_t es = dtype == LMOE_BF16 ? 2 : 4;
+  const int bke = (int)(128 / es);
+  const BwdDims b = bwd_dims(d);
+  const int64_t T = d.T, L = d.L, D = d.D, n = d.n, ns = d.n_shared, k = d.k;
+  int64_t sz[B_COUNT_];
+  sz[B_WUPT] = L * d.d * es;
+  sz[B_WDOWNT] = d.d * L * es;
+  sz[B_WRT] = L * b.np * es;
+  sz[B_W3T] = (n + ns) * D * L * es;
+  sz[B_W12T] = 2 * (n + ns) * L * D * es;
+  sz[B_DV] = T * L * 4;
+  sz[B_DU32] = T * L * 4;
+  sz[B_DU] = T * L * es;
+  sz[B_PROD] = T * L * 4;
+  sz[B_DG] = T * k * 4;
+  sz[B_DL] = T * b.np * es;
+  sz[B_DA] = b.R * D * es;
+  sz[B_DP] = b.R * 2 * D * es;
+  sz[B_DZROWS] = T * (k + ns + 1) * L * 4;
+  sz[B_DZ] = T * L * es;
+  sz[B_DYT] = d.d * b.Tp * es;
+  sz[B_VT] = L * b.Tp * es;
+  sz[B_DZT] = L * b.Tp * es;
+  sz[B_XT] = d.d * b.Tp * es;
+  sz[B_ZT] = L * b.Tp * es;
+  sz[B_DLT] = b.np * b.Tp * es;
+  sz[B_ZTG] = L * b.Kmax * es;
+  sz[B_DOT] = L * b.Kmax * es;
+  sz[B_DPT] = 2 * D * b.Kmax * es;
+  sz[B_AT] = D * b.Kmax * es;
+  sz[B_ENTRIES] = (n + ns) * 16;
+  sz[B_BLOCKS] = b.kblocks * 16;
+  sz[B_NB] = 16;
+  sz[B_SCHED] = BWD_SCHED * 4;
+  sz[B_SCHED2] = 3 * SCHED_COUNTERS * 4;  // the grouped dgrad / recompute GEMMs
+  int64_t part = 0;
+  const int64_t dense[6][3] = {{T, L, d.d}, {T, L, b.np}, {T, d.d, L}, {d.d, L, b.Tp}, {L, d.d, b.Tp}, {n, L, b.Tp}};
+  for (auto &m : dense) part = std::max(part, part_bytes<CfgDense>(m[0], m[1], m[2], bke));
+  sz[B_PART] = part;
+  WsLayout w;
+  int64_t o = 0;
+  for (int i = 0; i < B_COUNT_; ++i) {
+    w.off[i] = o;
+    o += align256(sz[i]);
+  }
+  w.total = o;
+  return w;
+}
+
+// out = in^T per batch: in [R, C] (row stride ld_in), out [C, >= cdiv(R, 64) * 64]
+template <typename T>
+hipError_t launch_transpose(const T *in, int64_t ld_in, int64_t in_bs, T *out, int64_t ld_out, int64_t out_bs, int R,
+                            int C, int batches, hipStream_t st, const int4 *blocks = nullptr, int nblk = 0,
+                            const int32_t *nb = nullptr, const int32_t *rows = nullptr,
+                            const float *rscale = nullptr) {
+  const unsigned gy = blocks ? (unsigned)nblk : (unsigned)cdiv(R, 64);
+  if (gy == 0 || C == 0 || batches == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)cdiv(C, 64), gy, (unsigned)batches), dim3(256), 0, st, in,
+                     ld_in, in_bs, out, ld_out, out_bs, R, C, blocks, nb, rows, rscale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, const T *dy, const int32_t *idx,
+                        const float *gw, const float *scores, const unsigned char *fws, const lmoe_grads &g,
+                        unsigned char *ws, hipStream_t st) {
+  const int dt = sizeof(T) == 2 ? LMOE_BF16 : LMOE_F32;
+  const WsLayout F = layout(d, dt);
+  const WsLayout B = bwd_layout(d, dt);
+  const BwdDims bd = bwd_dims(d);
+  const int T_ = (int)d.T, n = (int)d.n, k = (int)d.k, L = (int)d.L, D = (int)d.D, ns = (int)d.n_shared;
+  const int dd = (int)d.d, np_ = (int)bd.np, Tp = (int)bd.Tp;
+  const int64_t R = bd.R, Kmax = bd.Kmax;
+  // the forward's state
+  const T *z = (const T *)(fws + F.off[R_Z]);
+  const int32_t *counts = (const int32_t *)(fws + F.off[R_COUNTS]);
+  const int32_t *offs = (const int32_t *)(fws + F.off[R_OFFS]);
+  const int32_t *row_token = (const int32_t *)(fws + F.off[R_ROW_TOKEN]);
+  const int32_t *slot_row = (const int32_t *)(fws + F.off[R_SLOT_ROW]);
+  const T *hid = (const T *)(fws + F.off[R_HIDDEN]);
+  const unsigned char *ystage = fws + F.off[R_ROWS];
+  const T *v = (const T *)(fws + F.off[R_V]);
+  const int4 *tiles1 = (const int4 *)(fws + F.off[R_TILES1]);
+  const int4 *tiles2 = (const int4 *)(fws + F.off[R_TILES2]);
+  const int32_t *ntiles = (const int32_t *)(fws + F.off[R_NTILES]);
+  const float *row_w = (const float *)(fws + F.off[R_ROW_W]);
+  const bool wide_stage = sizeof(T) == 4 || std::isinf(w.beta1) || std::isinf(w.beta2);
+  // this call's buffers
+  T *wupT = (T *)(ws + B.off[B_WUPT]);
+  T *wdownT = (T *)(ws + B.off[B_WDOWNT]);
+  T *wrT = (T *)(ws + B.off[B_WRT]);
+  T *w3T = (T *)(ws + B.off[B_W3T]);
+  T *w12T = (T *)(ws + B.off[B_W12T]);
+  float *dv = (float *)(ws + B.off[B_DV]);
+  float *du32 = (float *)(ws + B.off[B_DU32]);
+  T *du = (T *)(ws + B.off[B_DU]);
+  float *prod = (float *)(ws + B.off[B_PROD]);
+  float *dg = (float *)(ws + B.off[B_DG]);
+  T *dl = (T *)(ws + B.off[B_DL]);
+  T *da = (T *)(ws + B.off[B_DA]);
+  T *dp = (T *)(ws + B.off[B_DP]);
+  float *dzrows = (float *)(ws + B.off[B_DZROWS]);
+  T *dz = (T *)(ws + B.off[B_DZ]);
+  T *dyT = (T *)(ws + B.off[B_DYT]);
+  T *vT = (T *)(ws + B.off[B_VT]);
+  T *dzT = (T *)(ws + B.off[B_DZT]);
+  T *xT = (T *)(ws + B.off[B_XT]);
+  T *zT = (T *)(ws + B.off[B_ZT]);
+  T *dlT = (T *)(ws + B.off[B_DLT]);
+  T *zTg = (T *)(ws + B.off[B_ZTG]);
+  T *doT = (T *)(ws + B.off[B_DOT]);
+  T *dpT = (T *)(ws + B.off[B_DPT]);
+  T *aT = (T *)(ws + B.off[B_AT]);
+  int4 *entries = (int4 *)(ws + B.off[B_ENTRIES]);
+  int4 *blocks = (int4 *)(ws + B.off[B_BLOCKS]);
+  int32_t *nb = (int32_t *)(ws + B.off[B_NB]);  // [0] block count, [1] entry count
+  int32_t *sched = (int32_t *)(ws + B.off[B_SCHED]);
+  int32_t *sched2 = (int32_t *)(ws + B.off[B_SCHED2]);
+  float *part = (float *)(ws + B.off[B_PART]);
+  constexpr int bke = 128 / (int)sizeof(T);
+  hipError_t e;
+#define LMOE_TRY(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
+
+  // weights transposed (contraction dimension contiguous)
+  LMOE_TRY(launch_transpose<T>((const T *)w.w_up, L, 0, wupT, dd, 0, dd, L, 1, st));
+  LMOE_TRY(launch_transpose<T>((const T *)w.w_down, dd, 0, wdownT, L, 0, L, dd, 1, st));
+  LMOE_TRY(launch_transpose<T>((const T *)w.w_router, L, 0, wrT, np_, 0, n, L, 1, st));
+  LMOE_TRY(launch_transpose<T>((const T *)w.w3, D, (int64_t)L * D, w3T, L, (int64_t)D * L, L, D, n, st));
+  LMOE_TRY(launch_transpose<T>((const T *)w.w1, L, (int64_t)D * L, w12T, D, (int64_t)L * D, D, L, n, st));
+  LMOE_TRY(launch_transpose<T>((const T *)w.w2, L, (int64_t)D * L, w12T + (int64_t)(n + ns) * L * D, D,
+                               (int64_t)L * D, D, L, n, st));
+  if (ns > 0) {
+    LMOE_TRY(launch_transpose<T>((const T *)w.ws3, D, (int64_t)L * D, w3T + (int64_t)n * D * L, L, (int64_t)D * L,
+                                 L, D, ns, st));
+    LMOE_TRY(launch_transpose<T>((const T *)w.ws1, L, (int64_t)D * L, w12T + (int64_t)n * L * D, D, (int64_t)L * D,
+                                 D, L, ns, st));
+    LMOE_TRY(launch_transpose<T>((const T *)w.ws2, L, (int64_t)D * L, w12T + (int64_t)(2 * n + ns) * L * D, D,
+                                 (int64_t)L * D, D, L, ns, st));
+  }
+  // dv = dy W_up
+  {
+    GemmArgs a = gargs();
+    a.A = dy; a.lda = dd; a.B = wupT; a.ldb = dd; a.C = dv; a.ldc = L; a.M = T_; a.N = L; a.K = dd;
+    LMOE_TRY((launch_dense<CfgDense, T, float, EPI_STORE>(a, part, st)));
+  }
+  // norm backward, routing-weight gradients; gain gradient
+  {
+    const T *gain = (const T *)w.rms_gain;
+    const int no_norm = w.norm == LMOE_NORM_NONE;
+    const dim3 wg((unsigned)cdiv(d.T, 4));
+    const int nch8 = L / 8;
+    auto go = [&](auto tag) -> hipError_t {
+      using TS = typename decltype(tag)::type;
+      const TS *ys = (const TS *)ystage;
+      if (nch8 <= 64) hipLaunchKernelGGL((norm_bwd_wave_kernel<T, TS, 1>), wg, dim3(256), 0, st, ys, slot_row, gw, gain, dv, du32, du, prod, dg, T_, L, k, ns, w.rms_eps, no_norm);
+      else if (nch8 <= 128) hipLaunchKernelGGL((norm_bwd_wave_kernel<T, TS, 2>), wg, dim3(256), 0, st, ys, slot_row, gw, gain, dv, du32, du, prod, dg, T_, L, k, ns, w.rms_eps, no_norm);
+      else if (nch8 <= 256) hipLaunchKernelGGL((norm_bwd_wave_kernel<T, TS, 4>), wg, dim3(256), 0, st, ys, slot_row, gw, gain, dv, du32, du, prod, dg, T_, L, k, ns, w.rms_eps, no_norm);
+      else if (nch8 <= 448) hipLaunchKernelGGL((norm_bwd_wave_kernel<T, TS, 7>), wg, dim3(256), 0, st, ys, slot_row, gw, gain, dv, du32, du, prod, dg, T_, L, k, ns, w.rms_eps, no_norm);
+      else hipLaunchKernelGGL((norm_bwd_wave_kernel<T, TS, 8>), wg, dim3(256), 0, st, ys, slot_row, gw, gain, dv, du32, du, prod, dg, T_, L, k, ns, w.rms_eps, no_norm);
+      return hipGetLastError();
+    };
+    if constexpr (sizeof(T) == 2) {
+      if (wide_stage) LMOE_TRY(go(TypeTag<float>{}));
+      else LMOE_TRY(go(TypeTag<f16>{}));
+    } else {
+      LMOE_TRY(go(TypeTag<float>{}));
+    }
+    if (no_norm)
+      hipLaunchKernelGGL(fill_zero_kernel<T>, dim3((unsigned)cdiv(L, 256)), dim3(256), 0, st, (T *)g.dgamma, (int64_t)L);
+    else
+      hipLaunchKernelGGL(colsum_kernel<T>, dim3((unsigned)cdiv(L, 256)), dim3(256), 0, st, prod, T_, L, (T *)g.dgamma);
+    LMOE_TRY(hipGetLastError());
+  }
+  // router backward (dense dl rows, zero off the chosen experts and past n)
+  hipLaunchKernelGGL(router_bwd_kernel<T>, dim3((unsigned)cdiv(d.T, 4)), dim3(256), 0, st, scores, idx, gw, dg, T_, n,
+                     np_, k, dl);
+  LMOE_TRY(hipGetLastError());
+  // expert segments for the weight gradients (and tile counters zeroed)
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, counts, offs, n, ns, T_, k, bke, entries, blocks, nb,
+                     sched, BWD_SCHED + 0);
+  LMOE_TRY(hipGetLastError());
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, sched2, (int64_t)3 * SCHED_COUNTERS, 0);
+  LMOE_TRY(hipGetLastError());
+  // da = g (du W3_e) for every expert row (du rows gathered by token)
+  {
+    GemmArgs a = gargs();
+    a.A = du; a.lda = L; a.a_rows = row_token; a.B = w3T; a.Bsh = w3T + (int64_t)n * D * L; a.n_routed = n;
+    a.ldb = L; a.b_group_stride = (int64_t)D * L; a.C = da; a.ldc = D; a.N = D; a.K = L; a.tiles = tiles2;
+    a.ntiles = ntiles + 1; a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w; a.sched = sched2;
+    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, T, EPI_ROWSCALE, true, true>(a, st)));
+    else LMOE_TRY((launch_gemm<CfgW3, T, T, EPI_ROWSCALE, true, true>(a, st)));
+  }
+  // gate backward: the W1/W2 products recomputed from z, dp1 | dp2 written [R, 2D]
+  {
+    GemmArgs a = gargs();
+    a.A = z; a.lda = L; a.a_rows = row_token; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
+    a.Bsh = w.ws1; a.B2sh = w.ws2; a.n_routed = n;
+    a.b_group_stride = (int64_t)D * L; a.C = dp; a.ldc = 2 * D;
+    a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, w12_bm(d));
+    a.sched = sched2 + SCHED_COUNTERS; a.beta1 = w.beta1; a.beta2 = w.beta2; a.aux = da; a.ldaux = D;
+    if (w.gate == LMOE_GATE_CLIP) {
+      if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_GLU_CLIP_BWD, true, true>(a, st)));
+      else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU_CLIP_BWD, true, true>(a, st)));
+    } else {
+      if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_GLU_BWD, true, true>(a, st)));
+      else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU_BWD, true, true>(a, st)));
+    }
+  }
+  // dz rows = dp1 W1_e + dp2 W2_e (B = [W1_e^T | W2_e^T] along K), fp32
+  {
+    GemmArgs a = gargs();
+    a.A = dp; a.lda = 2 * D; a.B = w12T; a.Bsh = w12T + (int64_t)n * L * D; a.n_routed = n; a.ldb = D;
+    a.b_group_stride = (int64_t)L * D; a.kb_len = D; a.kb_stride = (int64_t)(n + ns) * L * D;
+    a.C = dzrows; a.ldc = L; a.N = L; a.K = 2 * D; a.tiles = tiles1; a.ntiles = ntiles;
+    a.tiles_m = (int)max_tiles(d, w12_bm(d)); a.sched = sched2 + 2 * SCHED_COUNTERS;
+    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, float, EPI_STORE, false, true>(a, st)));
+    else LMOE_TRY((launch_gemm<CfgW12, T, float, EPI_STORE, false, true>(a, st)));
+  }
+  // the router's part, dl W_r, as one more row block of dz rows
+  {
+    GemmArgs a = gargs();
+    a.A = dl; a.lda = np_; a.B = wrT; a.ldb = np_; a.C = dzrows + (int64_t)T_ * (k + ns) * L; a.ldc = L;
+    a.M = T_; a.N = L; a.K = np_;
+    LMOE_TRY((launch_dense<CfgDense, T, float, EPI_STORE>(a, part, st)));
+  }
+  // dz = sum of the token's dz rows (routed slots, shared experts, router)
+  {
+    const int nch8 = L / 8;
+    const T *gain = (const T *)w.rms_gain;
+    const dim3 wg((unsigned)cdiv(d.T, 4));
+    if (nch8 <= 64) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 1>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    else if (nch8 <= 128) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 2>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    else if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 4>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    else if (nch8 <= 448) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 7>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    else hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 8>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    LMOE_TRY(hipGetLastError());
+  }
+  // dx = dz W_down
+  {
+    GemmArgs a = gargs();
+    a.A = dz; a.lda = L; a.B = wdownT; a.ldb = L; a.C = g.dx; a.ldc = dd; a.M = T_; a.N = dd; a.K = L;
+    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
+  }
+  // dense weight gradients: contraction over tokens (transposed, padded to Tp)
+  LMOE_TRY(launch_transpose<T>(dy, dd, 0, dyT, Tp, 0, T_, dd, 1, st));
+  LMOE_TRY(launch_transpose<T>(v, L, 0, vT, Tp, 0, T_, L, 1, st));
+  LMOE_TRY(launch_transpose<T>(dz, L, 0, dzT, Tp, 0, T_, L, 1, st));
+  LMOE_TRY(launch_transpose<T>(x, dd, 0, xT, Tp, 0, T_, dd, 1, st));
+  LMOE_TRY(launch_transpose<T>(z, L, 0, zT, Tp, 0, T_, L, 1, st));
+  LMOE_TRY(launch_transpose<T>(dl, np_, 0, dlT, Tp, 0, T_, np_, 1, st));
+  {
+    GemmArgs a = gargs();
+    a.A = dyT; a.lda = Tp; a.B = vT; a.ldb = Tp; a.C = g.dw_up; a.ldc = L; a.M = dd; a.N = L; a.K = Tp;
+    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
+  }
+  {
+    GemmArgs a = gargs();
+    a.A = dzT; a.lda = Tp; a.B = xT; a.ldb = Tp; a.C = g.dw_down; a.ldc = dd; a.M = L; a.N = dd; a.K = Tp;
+    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
+  }
+  {
+    GemmArgs a = gargs();
+    a.A = dlT; a.lda = Tp; a.B = zT; a.ldb = Tp; a.C = g.dw_router; a.ldc = L; a.M = n; a.N = L; a.K = Tp;
+    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
+  }
+  // expert weight gradients: rows gathered and transposed per expert segment
+  const int nblk = (int)bd.kblocks;
+  LMOE_TRY(launch_transpose<T>(z, L, 0, zTg, Kmax, 0, 0, L, 1, st, blocks, nblk, nb, row_token));
+  LMOE_TRY(launch_transpose<T>(du, L, 0, doT, Kmax, 0, 0, L, 1, st, blocks, nblk, nb, row_token, row_w));
+  LMOE_TRY(launch_transpose<T>(hid, D, 0, aT, Kmax, 0, 0, D, 1, st, blocks, nblk, nb));
+  LMOE_TRY(launch_transpose<T>(dp, 2 * D, 0, dpT, Kmax, 0, 0, 2 * D, 1, st, blocks, nblk, nb));
+  auto kgemm = [&](const T *A, int M, const T *Bm, int N, void *C, void *Csh, int64_t cstride, int32_t *sc) {
+    GemmArgs a = gargs();
+    a.A = A; a.lda = Kmax; a.B = Bm; a.ldb = Kmax; a.C = C; a.Csh = Csh; a.c_group_stride = cstride; a.ldc = N;
+    a.M = M; a.N = N; a.K = (int)Kmax; a.kb_len = Kmax; a.krange = 1; a.tiles = entries; a.ntiles = nb + 1;
+    a.tiles_m = n + ns; a.n_routed = n; a.sched = sc;
+    // (the 256 x 256 dense tile's LDS stages fill the whole 160 KB, with no room
+    // for the grouped walk's tile slot)
+    return launch_gemm<CfgW12, T, T, EPI_STORE, false, true>(a, st);
+  };
+  LMOE_TRY(kgemm(dpT, D, zTg, L, g.dw1, g.dws1, (int64_t)D * L, sched));
+  LMOE_TRY(kgemm(dpT + (int64_t)D * Kmax, D, zTg, L, g.dw2, g.dws2, (int64_t)D * L, sched + SCHED_COUNTERS));
+  LMOE_TRY(kgemm(doT, L, aT, D, g.dw3, g.dws3, (int64_t)L * D, sched + 2 * SCHED_COUNTERS));
+#undef LMOE_TRY
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -505,6 +833,7 @@ static int forward_impl(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   else
     e = run_forward<float>(*dims, *w, (const float *)x, (float *)y, topk_idx, topk_w, scores,
                            (unsigned char *)workspace, st, events);
+  if (e != hipSuccess) (void)hipGetLastError();  // leave no error behind for the caller's next HIP call
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
@@ -612,6 +941,64 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
   }
   return LMOE_OK;
+}
+
+size_t lmoe_backward_workspace_size(const lmoe_dims *dims, int dtype) {
+  if (check_dims(dims) != LMOE_OK || (dtype != LMOE_F32 && dtype != LMOE_BF16) || dims->L > 4096) return 0;
+  return (size_t)bwd_layout(*dims, dtype).total;
+}
+
+int lmoe_backward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, const void *dy,
+                  const int32_t *topk_idx, const float *topk_w, const float *scores, const void *fwd_workspace,
+                  size_t fwd_workspace_bytes, const lmoe_grads *grads, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+  int rc = check_dims(dims);
+  if (rc != LMOE_OK) return rc;
+  if (dims->L > 4096) return LMOE_ERR_SHAPE;
+  if (!w || !grads) return LMOE_ERR_NULL;
+  if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
+  if (!(w->beta1 > 0.0f) || !(w->beta2 > 0.0f) || !(w->rms_eps >= 0.0f) || w->rms_eps == INFINITY ||
+      (w->gate != LMOE_GATE_TANH && w->gate != LMOE_GATE_CLIP) || (w->norm != LMOE_NORM_RMS && w->norm != LMOE_NORM_NONE))
+    return LMOE_ERR_VALUE;
+  const lmoe_grads &g = *grads;
+  if (!g.dw_down || !g.dw_router || !g.dw1 || !g.dw2 || !g.dw3 || !g.dgamma || !g.dw_up) return LMOE_ERR_NULL;
+  if (dims->n_shared > 0 && (!g.dws1 || !g.dws2 || !g.dws3 || !w->ws1 || !w->ws2 || !w->ws3)) return LMOE_ERR_NULL;
+  if (dims->n_shared == 0 && (g.dws1 || g.dws2 || g.dws3)) return LMOE_ERR_SHAPE;
+  if (dims->T > 0 && (!x || !dy || !g.dx || !topk_idx || !topk_w || !scores || !fwd_workspace || !workspace ||
+                      !w->w_down || !w->w_router || !w->w1 || !w->w2 || !w->w3 || !w->rms_gain || !w->w_up))
+    return LMOE_ERR_NULL;
+  const void *ptrs[] = {x, dy, topk_idx, topk_w, scores, fwd_workspace, workspace, g.dx, g.dw_down, g.dw_router,
+                        g.dw1, g.dw2, g.dw3, g.dws1, g.dws2, g.dws3, g.dgamma, g.dw_up, w->w_down, w->w_router,
+                        w->w1, w->w2, w->w3, w->ws1, w->ws2, w->ws3, w->rms_gain, w->w_up};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return LMOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t es = dtype == LMOE_BF16 ? 2 : 4;
+  if (dims->T == 0) {  // no tokens: every weight gradient is zero
+    const int64_t n = dims->n, ns = dims->n_shared, L = dims->L, D = dims->D, d = dims->d;
+    struct { void *p; int64_t cnt; } z[] = {{g.dw_down, L * d}, {g.dw_router, n * L}, {g.dw1, n * D * L},
+                                            {g.dw2, n * D * L}, {g.dw3, n * L * D}, {g.dws1, ns * D * L},
+                                            {g.dws2, ns * D * L}, {g.dws3, ns * L * D}, {g.dgamma, L}, {g.dw_up, d * L}};
+    for (auto &q : z) {
+      if (!q.p || q.cnt == 0) continue;
+      const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(q.cnt, 256), 65536);
+      if (es == 2) hipLaunchKernelGGL(fill_zero_kernel<bf16>, dim3(blocks), dim3(256), 0, st, (bf16 *)q.p, q.cnt);
+      else hipLaunchKernelGGL(fill_zero_kernel<float>, dim3(blocks), dim3(256), 0, st, (float *)q.p, q.cnt);
+      if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+    }
+    return LMOE_OK;
+  }
+  if (fwd_workspace_bytes < (size_t)layout(*dims, dtype).total) return LMOE_ERR_WORKSPACE;
+  if (workspace_bytes < (size_t)bwd_layout(*dims, dtype).total) return LMOE_ERR_WORKSPACE;
+  hipError_t e;
+  if (dtype == LMOE_BF16)
+    e = run_backward<bf16>(*dims, *w, (const bf16 *)x, (const bf16 *)dy, topk_idx, topk_w, scores,
+                           (const unsigned char *)fwd_workspace, g, (unsigned char *)workspace, st);
+  else
+    e = run_backward<float>(*dims, *w, (const float *)x, (const float *)dy, topk_idx, topk_w, scores,
+                            (const unsigned char *)fwd_workspace, g, (unsigned char *)workspace, st);
+  if (e != hipSuccess) (void)hipGetLastError();
+  return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
 size_t lmoe_qb_margin_workspace_size(int64_t T) {

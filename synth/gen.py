@@ -11,7 +11,7 @@ DEV_LIB = os.path.join(_HERE, "libsynth_dev.so")
 # tensor ids of the generator streams
 TID = {
     "x": 0, "w_down": 1, "w_router": 2, "w1": 3, "w2": 4, "w3": 5,
-    "ws1": 6, "ws2": 7, "ws3": 8, "w_up": 9, "bias": 10, "scores": 13,
+    "ws1": 6, "ws2": 7, "ws3": 8, "w_up": 9, "bias": 10, "scores": 13, "dy": 14,
 }
 
 _host = None

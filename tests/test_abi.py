@@ -172,3 +172,25 @@ def test_balancing_entry_points_validation():
     assert g(None, 10, 896, 16, 0.01, FAKE, None) == -1
     assert g(FAKE, 10, 896, 16, 0.01, FAKE + 4, None) == -4
     assert g(None, 0, 896, 16, 0.01, FAKE, None) == 0                                 # empty batch: no-op
+
+
+def test_backward_validation():
+    """lmoe_backward validates on the host before launching anything."""
+    from sparse_moe_layer_down_amd._abi import Grads
+    b = lib().lmoe_backward
+    w = fake_weights()
+    full = Grads(*([FAKE] * 11))
+
+    def call_b(d, grads=full, ws=FAKE, wsb=1 << 40, fwsb=1 << 40, ww=w):
+        return b(ctypes.byref(d), ctypes.byref(ww), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, fwsb, ctypes.byref(grads),
+                 ws, wsb, None)
+
+    assert lmoe.backward_workspace_size(c2dims(), 1) > lmoe.workspace_size(c2dims(), 1)
+    assert lmoe.backward_workspace_size(c2dims(d=16384, L=8192), 1) == 0      # latent above 4096
+    assert call_b(c2dims(d=16384, L=8192)) == -2
+    assert call_b(c2dims(), ww=fake_weights(norm=2)) == -7                  # no backward of the extra norm
+    assert call_b(c2dims(), grads=Grads(*([FAKE] * 10 + [None]))) == -1      # dw_up missing
+    assert call_b(c2dims(n_shared=0), ww=fake_weights(n_shared=0)) == -2     # shared gradients without shared experts
+    assert call_b(c2dims(), fwsb=1000) == -5
+    assert call_b(c2dims(), wsb=1000) == -5
+    assert call_b(c2dims(), ws=None) == -1

@@ -173,3 +173,57 @@ def test_router_gradient_only_on_chosen_experts_and_bias_shift_invariant():
     g2 = ref.backward(x, params(a2), k, ns, "f64", dy, B1, B2, 1e-6)
     for key in ("dx", "dw_router", "dw1", "dw_up"):
         assert np.array_equal(g[key], g2[key])
+
+
+def _nudged_pair(cfg, rel, seed=0):
+    """The oracle's backward, plain and with every value nudged by a relative
+    N(0, rel) just before each of its work-dtype stores (a second correct
+    implementation whose pre-store values differ by rel)."""
+    import synth
+    P = synth.HostParams(cfg, cache=True)
+    x = P.x()
+    dy = synth.host_fill_values((cfg.T, cfg.d), cfg.x_seed, synth.TID["dy"], 0, 1.0, cfg.dtype)
+    args = (cfg.k, cfg.n_shared, cfg.dtype, dy, cfg.beta1, cfg.beta2, cfg.eps)
+    idx = ref.forward(x, P, cfg.k, cfg.n_shared, cfg.dtype, cfg.beta1, cfg.beta2, cfg.eps)["idx"]
+    a = ref.backward(x, P, *args, forced_idx=idx)
+    rng = np.random.default_rng(seed)
+    plain = ref.round_to
+    ref.round_to = lambda v, dt: plain(np.asarray(v, np.float64) * (1 + rel * rng.standard_normal(np.shape(v))), dt)
+    try:
+        b = ref.backward(x, P, *args, forced_idx=idx)
+    finally:
+        ref.round_to = plain
+    return a, b, np.bincount(idx.ravel(), minlength=cfg.n)
+
+
+BF16_SHAPES = {
+    "mid": dict(T=1024, d=512, L=256, n=64, k=8, n_shared=2, D=128, dtype="bf16"),
+    "sparse": dict(T=130, d=384, L=192, n=1024, k=3, n_shared=2, D=192, dtype="bf16"),  # most experts 0-1 tokens
+}
+
+
+@pytest.mark.parametrize("shape", list(BF16_SHAPES))
+def test_bf16_gradient_rule_sits_above_the_rounding_floor(shape):
+    """The bf16 matching rule for the gradients is not tighter than the
+    arithmetic allows: the oracle against itself, with pre-store values nudged
+    by 5e-4 (fp16 staging of the expert rows is 2^-11), meets it with 0.6 of
+    every bound."""
+    import bwd_rule
+    import synth
+    cfg = synth.get_config("C0").with_(x_seed=21, w_seed=21, bias_std=0.05, **BF16_SHAPES[shape])
+    a, b, counts = _nudged_pair(cfg, 5e-4)
+    for nm in ("dx", "dw_down", "dw_router", "dw1", "dw2", "dw3", "dws1", "dws2", "dws3", "dgamma", "dw_up"):
+        m, bad = bwd_rule.failures("bf16", cfg.d, nm, b[nm], a[nm], counts, scale=0.6)
+        assert not bad, (nm, bad)
+
+
+def test_routed_bank_maximum_is_ill_conditioned():
+    """Why the rule bounds a routed bank's bulk and each expert's RMS rather than
+    the bank's maximum: with about one token per expert, nudging the pre-store
+    values by only 1e-6 already moves some element of dW1 by more than the
+    forward's 2e-2 of the bank's RMS."""
+    import synth
+    cfg = synth.get_config("C0").with_(x_seed=21, w_seed=21, bias_std=0.05, **BF16_SHAPES["sparse"])
+    a, b, _ = _nudged_pair(cfg, 1e-6)
+    d = np.abs(a["dw1"] - b["dw1"]).max() / np.sqrt(np.mean(a["dw1"] ** 2))
+    assert d > 2e-2
