@@ -5,7 +5,7 @@ One step = one lmoe_forward over one batch of the K3-shaped prefill workload
 expert hidden 512, bf16, every weight resident in HBM), seeded synthetic
 inputs already in device memory.  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--config C2] [--no-cpu-baseline] [--only all|prefill|decode|qb|calib]
+  python bench.py [--steps K] [--warmup W] [--config C2] [--no-cpu-baseline] [--only all|prefill|backward|decode|qb|calib]
 """
 import argparse
 import json
@@ -29,7 +29,7 @@ def parse():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "qb", "calib"), default="all",
+    ap.add_argument("--only", choices=("all", "prefill", "backward", "decode", "qb", "calib"), default="all",
                     help="run one part alone (for profiler runs of one workload): the timed prefill forwards, "
                          "the decode forwards, the Quantile Balancing protocol, or 'calib': a single 1 GiB "
                          "device-to-device copy (a plain copy of known size, whose memory counters calibrate "
@@ -346,6 +346,8 @@ def main():
     out = {}
     if args.only in ("all", "prefill"):
         out = prefill(args, cfg, w, x, y, ws, dims, stream, lmoe, np, torch)
+    if args.only in ("all", "backward"):
+        out["backward"] = backward_protocol(cfg, w, x, ws, dims, lmoe, synth, torch, stream, steps=5)
     if args.only in ("all", "decode") and cfg.name == "C2":
         out["decode"] = decode_protocol(w, dev, lmoe, synth, steps=20)
     if args.only in ("all", "qb") and cfg.name == "C2":
@@ -360,6 +362,45 @@ def main():
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_tokens)
     print(json.dumps(out))
+
+
+def backward_protocol(cfg, w, x, ws, dims, lmoe, synth, torch, stream, steps):
+    """Timed backward passes (lmoe_backward) of the headline workload for a seeded
+    synthetic upstream gradient, after one forward that leaves the routing and
+    the forward workspace in place.  FLOPs: twice the forward's (each product
+    has a data and a weight gradient) plus the W1/W2 gate products recomputed
+    from the stored latent rather than kept from the forward."""
+    T = x.shape[0]
+    dev = x.device
+    dy = torch.empty_like(x)
+    synth.device_fill(dy, cfg.x_seed, synth.TID["dy"], 0, 1.0)
+    idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+    s = torch.empty((T, cfg.n), dtype=torch.float32, device=dev)
+    kw = dict(beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps)
+    lmoe.forward(x, w, cfg.k, topk_idx=idx, topk_w=tw, scores=s, workspace=ws, **kw)
+    bws = torch.empty(lmoe.backward_workspace_size(dims, x.dtype), dtype=torch.uint8, device=dev)
+    grads = lmoe.backward(x, dy, w, cfg.k, idx, tw, s, ws, workspace=bws, **kw)
+    for _ in range(2):
+        lmoe.backward(x, dy, w, cfg.k, idx, tw, s, ws, grads=grads, workspace=bws, **kw)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        lmoe.backward(x, dy, w, cfg.k, idx, tw, s, ws, grads=grads, workspace=bws, **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2 * cfg.flops_per_token() * T
+    recompute = (cfg.k + cfg.n_shared) * 2 * 2 * cfg.L * cfg.D * T
+    out = {"ms": ms, "tokens_per_s": T / (ms * 1e-3), "steps": steps, "tflops": flops / (ms * 1e-3) / 1e12,
+           "mfma_peak_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+           "tflops_with_recompute": (flops + recompute) / (ms * 1e-3) / 1e12,
+           "workspace_bytes": bws.numel()}
+    del grads, bws
+    torch.cuda.empty_cache()
+    return out
 
 
 def prefill(args, cfg, w, x, y, ws, dims, stream, lmoe, np, torch):

@@ -16,7 +16,8 @@
 //                        du = (gamma dv - u_hat mean(gamma dv u_hat)) / r,
 //                      dv * u_hat for the gain's gradient, and the routing
 //                      weights' gradients dg_j = du . o_j (o_j = staged row / g_j)
-//   colsum_kernel      gain gradient: column sums of dv * u_hat over tokens
+//   colsum_*_kernel    gain gradient: column sums of dv * u_hat over tokens
+//                      (row slices, then the slices' sums, both in fixed order)
 //   router_bwd_kernel  one wavefront per token: g_j = s_j / S over the chosen
 //                      experts, so ds_j = (dg_j - sum_j' dg_j' g_j') / S and
 //                      dl_j = ds_j s_j (1 - s_j); the row of dl is written dense
@@ -244,14 +245,29 @@ __global__ __launch_bounds__(256) void norm_bwd_wave_kernel(const TS *__restrict
   }
 }
 
-// out[c] = sum over rows t of in[t][c] (fp32, fixed order), converted to T
+// Column sums out[c] = sum over rows t of in[t][c] in two fixed-order stages
+// (deterministic): work-group (column block x, row slice y) sums its slice of
+// rows into part[y][c]; then the slices' partial sums are added in order.
+constexpr int COLSUM_SLICES = 64;
+
+__global__ __launch_bounds__(256) void colsum_partial_kernel(const float *__restrict__ in, int rows, int cols,
+                                                             float *__restrict__ part) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  const int per = (rows + COLSUM_SLICES - 1) / COLSUM_SLICES;
+  const int t0 = blockIdx.y * per, t1 = min(rows, t0 + per);
+  float s = 0.0f;
+  for (int t = t0; t < t1; ++t) s += in[(int64_t)t * cols + c];
+  part[(int64_t)blockIdx.y * cols + c] = s;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_kernel(const float *__restrict__ in, int rows, int cols,
-                                                     T *__restrict__ out) {
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restrict__ part, int cols,
+                                                           T *__restrict__ out) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= cols) return;
   float s = 0.0f;
-  for (int t = 0; t < rows; ++t) s += in[(int64_t)t * cols + c];
+  for (int y = 0; y < COLSUM_SLICES; ++y) s += part[(int64_t)y * cols + c];
   out[c] = from_f32<T>(s);
 }
 

@@ -482,7 +482,7 @@ constexpr int BWD_SCHED = 3 * SCHED_COUNTERS;  // tile counters of the three K-r
 enum {
   B_WUPT = 0, B_WDOWNT, B_WRT, B_W3T, B_W12T, B_DV, B_DU32, B_DU, B_PROD, B_DG, B_DL, B_DA, B_DP, B_DZROWS, B_DZ,
   B_DYT, B_VT, B_DZT, B_XT, B_ZT, B_DLT, B_ZTG, B_DOT, B_DPT, B_AT, B_ENTRIES, B_BLOCKS, B_NB, B_SCHED, B_SCHED2,
-  B_PART, B_COUNT_
+  B_PART, B_COLPART, B_COUNT_
 };
 
 struct BwdDims {
@@ -540,6 +540,7 @@ WsLayout bwd_layout(const lmoe_dims &d, int dtype) {
   const int64_t dense[6][3] = {{T, L, d.d}, {T, L, b.np}, {T, d.d, L}, {d.d, L, b.Tp}, {L, d.d, b.Tp}, {n, L, b.Tp}};
   for (auto &m : dense) part = std::max(part, part_bytes<CfgDense>(m[0], m[1], m[2], bke));
   sz[B_PART] = part;
+  sz[B_COLPART] = (int64_t)COLSUM_SLICES * L * 4;
   WsLayout w;
   int64_t o = 0;
   for (int i = 0; i < B_COUNT_; ++i) {
@@ -668,10 +669,15 @@ hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, c
     } else {
       LMOE_TRY(go(TypeTag<float>{}));
     }
-    if (no_norm)
+    if (no_norm) {
       hipLaunchKernelGGL(fill_zero_kernel<T>, dim3((unsigned)cdiv(L, 256)), dim3(256), 0, st, (T *)g.dgamma, (int64_t)L);
-    else
-      hipLaunchKernelGGL(colsum_kernel<T>, dim3((unsigned)cdiv(L, 256)), dim3(256), 0, st, prod, T_, L, (T *)g.dgamma);
+    } else {
+      float *colpart = (float *)(ws + B.off[B_COLPART]);
+      hipLaunchKernelGGL(colsum_partial_kernel, dim3((unsigned)cdiv(L, 256), COLSUM_SLICES), dim3(256), 0, st, prod,
+                         T_, L, colpart);
+      hipLaunchKernelGGL(colsum_final_kernel<T>, dim3((unsigned)cdiv(L, 256)), dim3(256), 0, st, colpart, L,
+                         (T *)g.dgamma);
+    }
     LMOE_TRY(hipGetLastError());
   }
   // router backward (dense dl rows, zero off the chosen experts and past n)
