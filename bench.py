@@ -74,8 +74,8 @@ def qb_protocol(w, dev, lmoe, synth):
         bias = torch.zeros(cfg.n, dtype=torch.float32, device=dev)
         w["router_bias"] = bias
         hist = torch.empty((cfg.n, nbins), dtype=torch.int32, device=dev)
-        qws = torch.empty(lmoe.qb_workspace_size(nbins), dtype=torch.uint8, device=dev)
-        mws = torch.empty(lmoe.qb_margin_workspace_size(cfg.T), dtype=torch.uint8, device=dev)
+        qws = torch.empty(lmoe.qb_workspace_size(cfg.n, nbins), dtype=torch.uint8, device=dev)
+        mws = torch.empty(lmoe.qb_margin_workspace_size(cfg.T, cfg.n, nbins), dtype=torch.uint8, device=dev)
         traj, mins, upd_ms = [], [], []
         for t in range(cfg.qb_steps + 1):
             x.copy_(synth.params.device_x(cfg, dev, step=t))

@@ -249,17 +249,19 @@ int lmoe_forward_timed(const lmoe_dims *dims, const lmoe_weights *w, int dtype, 
  *                         where read(h, c) = (j* + 1 - (c - G(j*+1)) / h[j*]) / B,
  *                         G(j) = sum_{j' >= j} h[j'], j* = max{j : G(j) >= c}.
  *                         Experts with an empty histogram keep their bias.
- *   workspace             device buffer of lmoe_qb_workspace_size(nbins) bytes when
- *                         solve != 0 (may be NULL otherwise)
+ *   workspace             device buffer of lmoe_qb_workspace_size(n, nbins) bytes
+ *                         when T > 0 or solve != 0 (may be NULL otherwise): the
+ *                         pooled histogram and the token runs' count slabs
  * T == 0 with accumulate == 0 clears the histogram.  Counts are int32: the
  * caller keeps every bin below 2^31 across accumulated batches. */
 int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins,
                    int32_t *hist, int accumulate, float *bias, int solve, void *workspace,
                    size_t workspace_bytes, void *stream);
 
-/* Bytes of device workspace lmoe_qb_update needs when solve != 0 (the pooled
- * histogram, int64 [nbins]); 0 for an invalid nbins. */
-size_t lmoe_qb_workspace_size(int32_t nbins);
+/* Bytes of device workspace lmoe_qb_update needs for n experts and nbins bins
+ * (the pooled histogram, int64 [nbins], then up to 16 int32 [n, nbins] slabs of
+ * per-run counts); 0 for an invalid n or nbins. */
+size_t lmoe_qb_workspace_size(int64_t n, int32_t nbins);
 
 /* Gradients of the layer (device pointers, work dtype, overwritten).  Shapes as
  * the weights they belong to; dws* NULL iff n_shared == 0. */
@@ -329,17 +331,17 @@ int lmoe_backward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const
  *   bias[e] = fp32(bias[e] - (2 q_e - 1))    (computed in fp64);
  * experts with an empty histogram keep their bias.  All operations are in a
  * fixed order, so the result is reproducible bit for bit.
- *   workspace             device buffer of lmoe_qb_margin_workspace_size(T)
- *                         bytes (the per-token thresholds); may be NULL when
- *                         T == 0
+ *   workspace             device buffer of lmoe_qb_margin_workspace_size(T, n,
+ *                         nbins) bytes (the per-token thresholds, then the
+ *                         token runs' count slabs); may be NULL when T == 0
  * T == 0 with accumulate == 0 clears the histogram. */
 int lmoe_qb_margin_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
                           int accumulate, float *bias, int solve, void *workspace, size_t workspace_bytes,
                           void *stream);
 
-/* Bytes of device workspace lmoe_qb_margin_update needs for T tokens (0 for an
- * invalid T). */
-size_t lmoe_qb_margin_workspace_size(int64_t T);
+/* Bytes of device workspace lmoe_qb_margin_update needs for T tokens, n experts
+ * and nbins bins (0 for an invalid T, n or nbins). */
+size_t lmoe_qb_margin_workspace_size(int64_t T, int64_t n, int32_t nbins);
 
 /* The fixed-step bias update of K2's loss-free balancing that Quantile
  * Balancing replaces ("Kimi K3 Architecture Deep Dive" §3: SignSGD-style,

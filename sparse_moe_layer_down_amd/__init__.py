@@ -161,16 +161,16 @@ def backward(x, dy, weights, k, topk_idx, topk_w, scores, fwd_workspace, grads=N
     return grads
 
 
-def qb_workspace_size(nbins):
-    return int(lib().lmoe_qb_workspace_size(int(nbins)))
+def qb_workspace_size(n, nbins):
+    return int(lib().lmoe_qb_workspace_size(int(n), int(nbins)))
 
 
 def qb_update(scores, k, hist, bias=None, accumulate=False, solve=True, workspace=None, stream=None):
     """Quantile Balancing: update the per-expert histogram and (optionally) solve the bias in place."""
     T, n = scores.shape
     nbins = hist.shape[1]
-    if solve and workspace is None:
-        workspace = torch.empty(qb_workspace_size(nbins), dtype=torch.uint8, device=hist.device)
+    if workspace is None and (solve or T > 0):
+        workspace = torch.empty(qb_workspace_size(n, nbins), dtype=torch.uint8, device=hist.device)
     if stream is None:
         stream = torch.cuda.current_stream(hist.device).cuda_stream
     rc = lib().lmoe_qb_update(_ptr(scores), T, n, int(k), int(nbins), _ptr(hist), int(bool(accumulate)),
@@ -180,8 +180,8 @@ def qb_update(scores, k, hist, bias=None, accumulate=False, solve=True, workspac
     return hist, bias
 
 
-def qb_margin_workspace_size(T):
-    return int(lib().lmoe_qb_margin_workspace_size(int(T)))
+def qb_margin_workspace_size(T, n, nbins):
+    return int(lib().lmoe_qb_margin_workspace_size(int(T), int(n), int(nbins)))
 
 
 def qb_margin_update(scores, k, hist, bias, accumulate=False, solve=True, workspace=None, stream=None):
@@ -190,7 +190,7 @@ def qb_margin_update(scores, k, hist, bias, accumulate=False, solve=True, worksp
     T, n = scores.shape
     nbins = hist.shape[1]
     if workspace is None and T > 0:
-        workspace = torch.empty(qb_margin_workspace_size(T), dtype=torch.uint8, device=hist.device)
+        workspace = torch.empty(qb_margin_workspace_size(T, n, nbins), dtype=torch.uint8, device=hist.device)
     if stream is None:
         stream = torch.cuda.current_stream(hist.device).cuda_stream
     rc = lib().lmoe_qb_margin_update(_ptr(scores), T, n, int(k), int(nbins), _ptr(hist), int(bool(accumulate)),

@@ -85,13 +85,13 @@ def lib():
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.lmoe_qb_workspace_size.restype = ctypes.c_size_t
-        L.lmoe_qb_workspace_size.argtypes = [ctypes.c_int32]
+        L.lmoe_qb_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32]
         L.lmoe_qb_margin_update.restype = ctypes.c_int
         L.lmoe_qb_margin_update.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                             ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.lmoe_qb_margin_workspace_size.restype = ctypes.c_size_t
-        L.lmoe_qb_margin_workspace_size.argtypes = [ctypes.c_int64]
+        L.lmoe_qb_margin_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
         L.lmoe_bias_signsgd.restype = ctypes.c_int
         L.lmoe_bias_signsgd.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]

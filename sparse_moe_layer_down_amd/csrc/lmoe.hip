@@ -437,31 +437,56 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   return hipSuccess;
 }
 
+// Geometry of the QB histogram launch, a function of (n, nbins) alone so that
+// the workspace size is too: experts per work-group (as many B-bin LDS
+// histograms as fit in 64 KB, at most 16), expert groups, and the most token
+// runs a launch uses.  Runs split the tokens so that the launch fills the GPU
+// in one round: as many work-groups as are resident at once (two per CU on a
+// 256-CU MI355X when a group's histograms take 64 KB of LDS; four when they
+// take at most 40 KB, as with 10000 bins and one expert per group).  Each run
+// but a lone one stores its counts to a slab of the workspace, and a merge
+// kernel sums the slabs.
+struct QbGeom {
+  int eg;
+  int64_t groups, runs;
+};
+QbGeom qb_geom(int64_t n, int nbins) {
+  QbGeom g;
+  g.eg = (int)std::min<int64_t>(16, std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4)));
+  g.groups = cdiv(n, g.eg);
+  const int64_t lds = (int64_t)g.eg * nbins * 4;
+  const int64_t slots = 256 * std::max<int64_t>(1, std::min<int64_t>(4, 163840 / lds));
+  g.runs = std::max<int64_t>(1, std::min<int64_t>(QB_MAX_RUNS, slots / g.groups));
+  return g;
+}
+
+int64_t qb_part_bytes(int64_t n, int nbins) {
+  const QbGeom g = qb_geom(n, nbins);
+  return g.runs > 1 ? align256(g.runs * n * nbins * 4) : 0;
+}
+
 // The histogram launch of both QB forms: B-bin histograms of every expert over
-// the T tokens, added to hist.  MARGIN: the binned value is the margin of the
+// the T > 0 tokens, written to hist (accumulate == 0) or added to it.  part:
+// the slabs (qb_part_bytes).  MARGIN: the binned value is the margin of the
 // score against the token's threshold (bias [n], thr [T]).
 template <bool MARGIN>
-hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_t *hist, const float *bias,
-                          const float2 *thr, hipStream_t st) {
+hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_t *hist, int32_t *part,
+                          int accumulate, const float *bias, const float2 *thr, hipStream_t st) {
   const int64_t n = ni;
-  const int nbins = kb;
-  // experts per work-group: as many B-bin LDS histograms as fit in 64 KB (max 16)
-  int eg = (int)std::min<int64_t>(16, std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4)));
-  const int64_t groups = cdiv(n, eg);
-  // token runs: every work-group merges its eg * nbins LDS bins into the global
-  // histogram with device atomics, so fewer runs mean fewer merges.  Groups of
-  // at least four experts (16-byte loads of four experts per token) are bound
-  // by those merges: about one work-group per CU.  Narrower groups (wide
-  // histograms, e.g. 10000 bins: one expert per group) walk their tokens with
-  // scalar loads and want more runs: about four work-groups per CU.  (Measured
-  // at 32768 tokens x 896 experts: 1000 bins 0.110 -> 0.096 ms, 10000 bins
-  // 0.49 -> 0.42 ms against two work-groups per CU.)
-  const int64_t target = (eg >= 4 ? 1 : 4) * (int64_t)device_cus();
-  int64_t runs = std::max<int64_t>(1, std::min<int64_t>(cdiv(target, groups), cdiv(T, 256)));
+  const QbGeom g = qb_geom(n, kb);
+  // runs of at least 256 tokens
+  int64_t runs = std::max<int64_t>(1, std::min<int64_t>(g.runs, cdiv(T, 256)));
   const int64_t tpb = cdiv(T, runs);
-  runs = cdiv(T, tpb);  // <= 4 * CUs: within the grid's y limit
-  hipLaunchKernelGGL(qb_hist_kernel<MARGIN>, dim3((unsigned)groups, (unsigned)runs), dim3(256),
-                     (size_t)eg * nbins * 4, st, scores, T, ni, kb, eg, tpb, hist, bias, thr);
+  runs = cdiv(T, tpb);
+  const int64_t items = g.groups * runs;
+  hipLaunchKernelGGL(qb_hist_kernel<MARGIN>, dim3((unsigned)(8 * cdiv(items, 8))), dim3(QB_HIST_THREADS),
+                     (size_t)g.eg * kb * 4, st, scores, T, ni, kb, g.eg, (int)g.groups, (int)runs, tpb, hist, part,
+                     accumulate, bias, thr);
+  if (runs > 1) {
+    const int64_t cnt = n * kb;
+    hipLaunchKernelGGL(qb_merge_kernel, dim3((unsigned)cdiv(cnt, 256)), dim3(256), 0, st, part, (int)runs, cnt, hist,
+                       accumulate);
+  }
   return hipGetLastError();
 }
 
@@ -908,9 +933,9 @@ int lmoe_forward_static(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, ws, LMOE_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
-size_t lmoe_qb_workspace_size(int32_t nbins) {
-  if (nbins < 1 || nbins > 16384) return 0;
-  return (size_t)align256((int64_t)nbins * 8);
+size_t lmoe_qb_workspace_size(int64_t n, int32_t nbins) {
+  if (nbins < 1 || nbins > 16384 || n < 1 || n > ((int64_t)1 << 20)) return 0;
+  return (size_t)(align256((int64_t)nbins * 8) + qb_part_bytes(n, nbins));
 }
 
 int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
@@ -918,22 +943,24 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
                    void *stream) {
   if (T < 0 || T >= ((int64_t)1 << 31) || n < 1 || n > ((int64_t)1 << 20) || k < 1 || k > n) return LMOE_ERR_SHAPE;
   if (nbins < 1 || nbins > 16384) return LMOE_ERR_VALUE;
-  if (!hist || (T > 0 && !scores) || (solve && (!bias || !workspace))) return LMOE_ERR_NULL;
+  const bool need_ws = solve || T > 0;
+  if (!hist || (T > 0 && !scores) || (solve && !bias) || (need_ws && !workspace)) return LMOE_ERR_NULL;
   if (!aligned16(hist) || (scores && !aligned16(scores)) || (bias && !aligned16(bias)) ||
       (workspace && !aligned16(workspace)))
     return LMOE_ERR_ALIGN;
-  if (solve && workspace_bytes < lmoe_qb_workspace_size(nbins)) return LMOE_ERR_WORKSPACE;
   if (n * nbins >= ((int64_t)1 << 40)) return LMOE_ERR_SHAPE;
+  if (need_ws && workspace_bytes < lmoe_qb_workspace_size(n, nbins)) return LMOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int ni = (int)n, kb = nbins;
-  if (!accumulate) {
+  if (T > 0) {
+    int32_t *part = (int32_t *)((unsigned char *)workspace + align256((int64_t)nbins * 8));
+    if (launch_qb_hist<false>(scores, T, ni, kb, hist, part, accumulate, nullptr, nullptr, st) != hipSuccess)
+      return LMOE_ERR_HIP;
+  } else if (!accumulate) {
     const int64_t cnt = n * nbins;
     hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(cnt, 256), 4096)), dim3(256), 0, st,
                        hist, cnt, 0);
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
-  }
-  if (T > 0) {
-    if (launch_qb_hist<false>(scores, T, ni, kb, hist, nullptr, nullptr, st) != hipSuccess) return LMOE_ERR_HIP;
   }
   if (solve) {
     unsigned long long *pooled = (unsigned long long *)workspace;
@@ -1007,9 +1034,9 @@ int lmoe_backward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const
   return e == hipSuccess ? LMOE_OK : LMOE_ERR_HIP;
 }
 
-size_t lmoe_qb_margin_workspace_size(int64_t T) {
-  if (T < 0 || T >= ((int64_t)1 << 31)) return 0;
-  return (size_t)align256(std::max<int64_t>(T, 1) * 8);
+size_t lmoe_qb_margin_workspace_size(int64_t T, int64_t n, int32_t nbins) {
+  if (T < 0 || T >= ((int64_t)1 << 31) || nbins < 1 || nbins > 16384 || n < 1 || n > 1024) return 0;
+  return (size_t)(align256(std::max<int64_t>(T, 1) * 8) + qb_part_bytes(n, nbins));
 }
 
 int lmoe_qb_margin_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
@@ -1020,10 +1047,10 @@ int lmoe_qb_margin_update(const float *scores, int64_t T, int64_t n, int64_t k, 
   if (!hist || !bias || (T > 0 && (!scores || !workspace))) return LMOE_ERR_NULL;
   if (!aligned16(hist) || !aligned16(bias) || (scores && !aligned16(scores)) || (workspace && !aligned16(workspace)))
     return LMOE_ERR_ALIGN;
-  if (T > 0 && workspace_bytes < lmoe_qb_margin_workspace_size(T)) return LMOE_ERR_WORKSPACE;
+  if (T > 0 && workspace_bytes < lmoe_qb_margin_workspace_size(T, n, nbins)) return LMOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int ni = (int)n, kb = nbins, Ti = (int)T;
-  if (!accumulate) {
+  if (T == 0 && !accumulate) {
     const int64_t cnt = n * nbins;
     hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)std::min<int64_t>(cdiv(cnt, 256), 4096)), dim3(256), 0, st,
                        hist, cnt, 0);
@@ -1031,6 +1058,7 @@ int lmoe_qb_margin_update(const float *scores, int64_t T, int64_t n, int64_t k, 
   }
   if (T > 0) {
     float2 *thr = (float2 *)workspace;
+    int32_t *part = (int32_t *)((unsigned char *)workspace + align256(T * 8));
     const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(T, 4), 65536);
     if (ni <= 64) hipLaunchKernelGGL(qb_thresholds_kernel<1>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
     else if (ni <= 128) hipLaunchKernelGGL(qb_thresholds_kernel<2>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
@@ -1039,7 +1067,7 @@ int lmoe_qb_margin_update(const float *scores, int64_t T, int64_t n, int64_t k, 
     else if (ni <= 896) hipLaunchKernelGGL(qb_thresholds_kernel<14>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
     else hipLaunchKernelGGL(qb_thresholds_kernel<16>, dim3(blocks), dim3(256), 0, st, scores, bias, Ti, ni, (int)k, thr);
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
-    if (launch_qb_hist<true>(scores, T, ni, kb, hist, bias, thr, st) != hipSuccess) return LMOE_ERR_HIP;
+    if (launch_qb_hist<true>(scores, T, ni, kb, hist, part, accumulate, bias, thr, st) != hipSuccess) return LMOE_ERR_HIP;
   }
   if (solve) {
     hipLaunchKernelGGL(qb_margin_solve_kernel, dim3((unsigned)cdiv(n, 4)), dim3(256), 0, st, hist, ni, kb, (int)k,

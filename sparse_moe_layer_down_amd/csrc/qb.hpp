@@ -5,8 +5,10 @@
 // moved to where it gets its target share).
 //
 //   qb_hist_kernel   LDS-privatised histogram: a work-group owns EG experts
-//                    x a run of tokens, counts in LDS with ds atomics, then adds
-//                    its non-zero bins to the global int32 histogram.
+//                    x a run of tokens and counts in LDS with ds atomics; with
+//                    one run it writes (or adds) its bins to the histogram,
+//                    with several it stores them to its run's slab.
+//   qb_merge_kernel  histogram (or histogram +) = the runs' slabs summed in order.
 //   qb_pool_kernel   pooled histogram sum_e H[e] (int64), per expert slice, atomically summed.
 //   qb_solve_kernel  one wavefront per expert: tail sums G(j) by a wave scan,
 //                    j* = max{j : G(j) >= c}, q by linear interpolation inside
@@ -57,28 +59,48 @@ LMOE_DEV float qb_margin_u(float s, float b, float tk, float tk1) {
   return (m + 1.0f) * 0.5f;
 }
 
-// grid: (expert groups, token runs); dynamic LDS = eg * nbins * 4 bytes.
-// When n, the group width and its first expert are multiples of 4, each thread reads four
-// adjacent experts of a token as one 16-B load and four tokens per iteration;
-// otherwise one thread walks the group's experts of one token at a time.
+// One work-group per (token run r, expert group g), walked through a 1-D grid
+// of 8 * ceil(groups * runs / 8) work-groups: work item w = r * groups + g, and
+// XCD x (work-groups are dispatched round-robin over the 8 XCDs) takes items
+// [x * chunk, (x + 1) * chunk) in order, so neighbouring expert groups of one
+// run, which read the same 128-byte lines of the score rows, share an L2.
+// Dynamic LDS = eg * nbins * 4 bytes.  When n, the group width and its first
+// expert are multiples of 4, each thread reads four adjacent experts of a token
+// as one 16-B load and eight tokens per iteration (the kernel is bound by these
+// strided loads, not by the LDS atomics, so it keeps many in flight); otherwise
+// one thread walks the group's experts of one token at a time.
+// Output: with runs == 1 the group's bins go to hist (stored, or added when
+// accumulate != 0: every bin of the group belongs to this work-group alone);
+// with runs > 1 to part[r][e][bin], summed by qb_merge_kernel.
 // MARGIN: bin qb_margin_u of the score (bias [n], thr [T] = {tk, tk1}) instead
 // of the score itself.
+constexpr int QB_HIST_THREADS = 512;
+constexpr int QB_MAX_RUNS = 16;  // token runs of one histogram launch (slabs in the workspace)
+
 template <bool MARGIN>
-__global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ scores, int64_t T, int n,
-                                                      int nbins, int eg, int64_t tokens_per_block,
-                                                      int32_t *__restrict__ hist, const float *__restrict__ bias,
+__global__ __launch_bounds__(QB_HIST_THREADS) void qb_hist_kernel(const float *__restrict__ scores, int64_t T, int n,
+                                                      int nbins, int eg, int groups, int runs,
+                                                      int64_t tokens_per_block, int32_t *__restrict__ hist,
+                                                      int32_t *__restrict__ part, int accumulate,
+                                                      const float *__restrict__ bias,
                                                       const float2 *__restrict__ thr) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int32_t *h = (int32_t *)smem_raw;
-  const int e0 = blockIdx.x * eg;
+  const int items = groups * runs;
+  const int chunk = (items + 7) / 8;
+  const int w = (int)(blockIdx.x % 8) * chunk + (int)(blockIdx.x / 8);
+  if (w >= items) return;  // uniform over the work-group, before any barrier
+  const int run = w / groups, g = w - run * groups;
+  const int e0 = g * eg;
   const int ne = min(eg, n - e0);
   for (int i = threadIdx.x; i < ne * nbins; i += blockDim.x) h[i] = 0;
   __syncthreads();
-  const int64_t t0 = (int64_t)blockIdx.y * tokens_per_block;
+  const int64_t t0 = (int64_t)run * tokens_per_block;
   const int64_t t1 = min(T, t0 + tokens_per_block);
   if ((n & 3) == 0 && (ne & 3) == 0 && (e0 & 3) == 0) {  // 16-byte aligned quads
+    constexpr int U = 8;                // tokens per thread and iteration
     const int nq = ne >> 2;            // 16-B quads per token
-    const int rows = 256 / nq;          // tokens per pass
+    const int rows = QB_HIST_THREADS / nq;  // tokens per pass
     const int tr = threadIdx.x / nq, q = threadIdx.x - tr * nq;
     if (tr < rows) {
       const float *base = scores + e0 + q * 4;
@@ -86,16 +108,16 @@ __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ 
       f32x4 bq = {0.0f, 0.0f, 0.0f, 0.0f};
       if (MARGIN) bq = *(const f32x4 *)(bias + e0 + q * 4);
       int64_t t = t0 + tr;
-      for (; t + 3 * rows < t1; t += 4 * rows) {
-        f32x4 v[4];
-        float2 th[4];
+      for (; t + (U - 1) * rows < t1; t += U * rows) {
+        f32x4 v[U];
+        float2 th[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
           v[u] = *(const f32x4 *)(base + (t + u * rows) * n);
           if (MARGIN) th[u] = thr[t + u * rows];
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const float x = MARGIN ? qb_margin_u(v[u][c], bq[c], th[u].x, th[u].y) : v[u][c];
@@ -114,7 +136,25 @@ __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ 
       }
     }
   } else {
-    for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+    constexpr int U = 4;  // tokens per thread and iteration
+    const int64_t bd = blockDim.x;
+    int64_t t = t0 + threadIdx.x;
+    for (; t + (U - 1) * bd < t1; t += U * bd) {
+      float2 th[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) th[u] = MARGIN ? thr[t + u * bd] : float2{0.0f, 0.0f};
+      for (int e = 0; e < ne; ++e) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = scores[(t + u * bd) * n + e0 + e];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float y = MARGIN ? qb_margin_u(x[u], bias[e0 + e], th[u].x, th[u].y) : x[u];
+          atomicAdd(&h[e * nbins + qb_bin(y, nbins)], 1);
+        }
+      }
+    }
+    for (; t < t1; t += bd) {
       const float *row = scores + t * n + e0;
       float2 th = {0.0f, 0.0f};
       if (MARGIN) th = thr[t];
@@ -125,22 +165,32 @@ __global__ __launch_bounds__(256) void qb_hist_kernel(const float *__restrict__ 
     }
   }
   __syncthreads();
-  if ((nbins & 1) == 0) {
-    // two adjacent bins of one expert per 64-bit atomic: the pair is 8-byte
-    // aligned (even bin, even row length, 16-byte aligned histogram) and the low
-    // count cannot carry into the high one while both stay non-negative int32
-    for (int i = 2 * threadIdx.x; i < ne * nbins; i += 2 * blockDim.x) {
-      const uint32_t a = (uint32_t)h[i], b = (uint32_t)h[i + 1];
-      if (a | b)
-        atomicAdd((unsigned long long *)&hist[(int64_t)(e0 + i / nbins) * nbins + (i % nbins)],
-                  ((unsigned long long)b << 32) | a);
-    }
+  // the group's bins are contiguous ([e0, e0 + ne) x nbins) in hist and in the slab
+  const int64_t off = (int64_t)e0 * nbins;
+  const int cnt = ne * nbins;
+  if (runs > 1) {
+    int32_t *dst = part + (int64_t)run * n * nbins + off;
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) dst[i] = h[i];
+  } else if (accumulate) {
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) hist[off + i] += h[i];
   } else {
-    for (int i = threadIdx.x; i < ne * nbins; i += blockDim.x) {
-      const int v = h[i];
-      if (v) atomicAdd(&hist[(int64_t)(e0 + i / nbins) * nbins + (i % nbins)], v);
-    }
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) hist[off + i] = h[i];
   }
+}
+
+// hist[i] = (accumulate ? hist[i] : 0) + sum over r < runs of part[r][i], r in
+// order; one element per thread, the runs' loads issued together.
+__global__ __launch_bounds__(256) void qb_merge_kernel(const int32_t *__restrict__ part, int runs, int64_t cnt,
+                                                       int32_t *__restrict__ hist, int accumulate) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= cnt) return;
+  int32_t v[QB_MAX_RUNS];
+#pragma unroll
+  for (int r = 0; r < QB_MAX_RUNS; ++r) v[r] = r < runs ? part[r * cnt + i] : 0;
+  int32_t s = accumulate ? hist[i] : 0;
+#pragma unroll
+  for (int r = 0; r < QB_MAX_RUNS; ++r) s += v[r];
+  hist[i] = s;
 }
 
 // pooled[j] = sum_e hist[e][j]: grid (bin chunks of 64, expert slices); a
@@ -154,8 +204,16 @@ __global__ __launch_bounds__(256) void qb_pool_kernel(const int32_t *__restrict_
   const int stripe = threadIdx.x >> 6;
   const int ea = blockIdx.y * QB_POOL_SLICE, eb = min(n, ea + QB_POOL_SLICE);
   long long s = 0;
-  if (j < nbins)
-    for (int e = ea + stripe; e < eb; e += 4) s += hist[(int64_t)e * nbins + j];
+  if (j < nbins) {
+    int32_t v[QB_POOL_SLICE / 4];
+#pragma unroll
+    for (int i = 0; i < QB_POOL_SLICE / 4; ++i) {
+      const int e = ea + stripe + 4 * i;
+      v[i] = e < eb ? hist[(int64_t)e * nbins + j] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < QB_POOL_SLICE / 4; ++i) s += v[i];
+  }
   part[stripe][threadIdx.x & 63] = s;
   __syncthreads();
   if (stripe == 0 && j < nbins) {
@@ -169,16 +227,44 @@ __global__ void fill_u64_kernel(unsigned long long *p, int64_t n) {
     p[i] = 0ull;
 }
 
-// Upper-tail read of one histogram by a full wavefront.  Returns q, or a NaN
-// when the histogram is empty.  c = N * k / n where N is the histogram's mass.
+// Upper-tail read of one histogram by a full wavefront: lane l owns bins
+// [l * per, (l + 1) * per), per = ceil(nbins / 64).  Returns q, or a NaN when
+// the histogram is empty.  c = N * k / n where N is the histogram's mass.
+// Up to QB_LANE_BINS bins per lane (nbins <= 1024) a lane's bins are first
+// loaded into registers (all loads in flight at once) and both passes use that
+// copy; wider histograms are read in chunks of QB_LANE_BINS bins, each chunk's
+// loads issued together.  Both forms perform the same sequence of integer and
+// fp64 operations as a bin-by-bin walk.
+constexpr int QB_LANE_BINS = 16;
+
 template <typename CT>
-LMOE_DEV double qb_read_wave(const CT *h, int nbins, long long k, long long n) {
+LMOE_DEV void qb_lane_load(const CT *h, int nbins, long long (&v)[QB_LANE_BINS]) {
+  const int per = (nbins + 63) / 64;
+  const int lo = min((int)(threadIdx.x & 63) * per, nbins), hi = min(lo + per, nbins);
+#pragma unroll
+  for (int i = 0; i < QB_LANE_BINS; ++i) v[i] = lo + i < hi ? (long long)h[lo + i] : 0;
+}
+
+// CACHED: v holds the lane's bins (qb_lane_load); otherwise h is read.
+template <bool CACHED, typename CT>
+LMOE_DEV double qb_read_wave(const CT *h, const long long (&v)[QB_LANE_BINS], int nbins, long long k, long long n) {
 #pragma clang fp contract(off)
   const int lane = threadIdx.x & 63;
   const int per = (nbins + 63) / 64;
   const int lo = min(lane * per, nbins), hi = min(lo + per, nbins);
   long long mine = 0;
-  for (int j = lo; j < hi; ++j) mine += (long long)h[j];
+  if (CACHED) {
+#pragma unroll
+    for (int i = 0; i < QB_LANE_BINS; ++i) mine += v[i];
+  } else {  // chunks of QB_LANE_BINS bins, each chunk's loads in flight together
+    for (int j0 = lo; j0 < hi; j0 += QB_LANE_BINS) {
+      long long w[QB_LANE_BINS];
+#pragma unroll
+      for (int i = 0; i < QB_LANE_BINS; ++i) w[i] = j0 + i < hi ? (long long)h[j0 + i] : 0;
+#pragma unroll
+      for (int i = 0; i < QB_LANE_BINS; ++i) mine += w[i];
+    }
+  }
   // suffix sum over lanes above: G at the top of my range
   long long incl = mine;  // inclusive suffix scan (lanes >= me)
 #pragma unroll
@@ -192,15 +278,44 @@ LMOE_DEV double qb_read_wave(const CT *h, int nbins, long long k, long long n) {
   long long G = incl - mine;  // G(hi)
   int jcand = -1;
   long long Gnext = 0, hj = 0;
-  for (int j = hi - 1; j >= lo; --j) {
-    const long long gj = G + (long long)h[j];
-    if ((double)gj >= c) {
-      jcand = j;
-      Gnext = G;
-      hj = (long long)h[j];
-      break;
+  // the highest bin j of my range with G(j) >= c
+  if (CACHED) {
+    bool found = false;
+#pragma unroll
+    for (int i = QB_LANE_BINS - 1; i >= 0; --i) {
+      if (!found && lo + i < hi) {
+        const long long gj = G + v[i];
+        if ((double)gj >= c) {
+          jcand = lo + i;
+          Gnext = G;
+          hj = v[i];
+          found = true;
+        } else {
+          G = gj;
+        }
+      }
     }
-    G = gj;
+  } else {  // the same walk from the top, a chunk of loads at a time
+    bool found = false;
+    for (int j0 = lo + (hi - lo - 1) / QB_LANE_BINS * QB_LANE_BINS; !found && j0 >= lo; j0 -= QB_LANE_BINS) {
+      long long w[QB_LANE_BINS];
+#pragma unroll
+      for (int i = 0; i < QB_LANE_BINS; ++i) w[i] = j0 + i < hi ? (long long)h[j0 + i] : 0;
+#pragma unroll
+      for (int i = QB_LANE_BINS - 1; i >= 0; --i) {
+        if (!found && j0 + i < hi) {
+          const long long gj = G + w[i];
+          if ((double)gj >= c) {
+            jcand = j0 + i;
+            Gnext = G;
+            hj = w[i];
+            found = true;
+          } else {
+            G = gj;
+          }
+        }
+      }
+    }
   }
   // j* = max over lanes of jcand
   int js = jcand;
@@ -222,8 +337,18 @@ __global__ __launch_bounds__(256) void qb_solve_kernel(const int32_t *__restrict
 #pragma clang fp contract(off)
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   if (e >= n) return;  // wave-uniform
-  const double tau = qb_read_wave(pooled, nbins, (long long)k, (long long)n);
-  const double q = qb_read_wave(hist + (int64_t)e * nbins, nbins, (long long)k, (long long)n);
+  const int32_t *he = hist + (int64_t)e * nbins;
+  double tau, q;
+  long long vp[QB_LANE_BINS], vh[QB_LANE_BINS];
+  if (nbins <= 64 * QB_LANE_BINS) {  // both histograms' loads in flight together
+    qb_lane_load(pooled, nbins, vp);
+    qb_lane_load(he, nbins, vh);
+    tau = qb_read_wave<true>(pooled, vp, nbins, (long long)k, (long long)n);
+    q = qb_read_wave<true>(he, vh, nbins, (long long)k, (long long)n);
+  } else {
+    tau = qb_read_wave<false>(pooled, vp, nbins, (long long)k, (long long)n);
+    q = qb_read_wave<false>(he, vh, nbins, (long long)k, (long long)n);
+  }
   if (tau != tau || q != q) return;
   if ((threadIdx.x & 63) == 0) bias[e] = (float)(tau - q);
 }
@@ -281,7 +406,15 @@ __global__ __launch_bounds__(256) void qb_margin_solve_kernel(const int32_t *__r
 #pragma clang fp contract(off)
   const int e = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   if (e >= n) return;  // wave-uniform
-  const double q = qb_read_wave(hist + (int64_t)e * nbins, nbins, (long long)k, (long long)n);
+  const int32_t *he = hist + (int64_t)e * nbins;
+  long long vh[QB_LANE_BINS];
+  double q;
+  if (nbins <= 64 * QB_LANE_BINS) {
+    qb_lane_load(he, nbins, vh);
+    q = qb_read_wave<true>(he, vh, nbins, (long long)k, (long long)n);
+  } else {
+    q = qb_read_wave<false>(he, vh, nbins, (long long)k, (long long)n);
+  }
   if (q != q) return;
   if ((threadIdx.x & 63) == 0) bias[e] = (float)((double)bias[e] - (2.0 * q - 1.0));
 }

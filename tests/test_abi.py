@@ -127,8 +127,15 @@ def test_qb_validation():
     assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, None, 1, FAKE, 1 << 20, None) == -1  # solve without bias
     assert q(FAKE, 10, 896, 16, 1000, FAKE + 4, 0, FAKE, 1, FAKE, 1 << 20, None) == -4
     assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, FAKE, 1, FAKE, 16, None) == -5
-    assert lmoe.qb_workspace_size(1000) == 8192
-    assert lmoe.qb_workspace_size(0) == 0
+    # the pooled histogram (int64 per bin), then one int32 [n, nbins] count slab per token run:
+    # 16-expert groups of 64 KB of LDS, two resident per CU: runs = min(16, 512 // groups)
+    # (56 groups at n = 896: 9 runs)
+    assert lmoe.qb_workspace_size(896, 1000) == 8192 + 9 * 896 * 1000 * 4
+    assert lmoe.qb_workspace_size(8, 1000) == 8192 + 16 * 8 * 1000 * 4
+    # one expert per group at 10000 bins (40 KB, four per CU): 896 groups fill 1024 slots in one run
+    assert lmoe.qb_workspace_size(896, 10000) == 80128
+    assert lmoe.qb_workspace_size(200, 10000) == 80128 + 5 * 200 * 10000 * 4
+    assert lmoe.qb_workspace_size(896, 0) == 0 and lmoe.qb_workspace_size(0, 1000) == 0
 
 
 def test_strerror():
@@ -163,7 +170,8 @@ def test_balancing_entry_points_validation():
     assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, FAKE, 1, None, 0, None) == -1          # thresholds need a workspace
     assert q(FAKE, 10, 896, 16, 1000, FAKE, 0, FAKE, 1, FAKE, 16, None) == -5
     assert q(FAKE, 10, 896, 16, 1000, FAKE + 4, 0, FAKE, 1, FAKE, 1 << 20, None) == -4
-    assert lmoe.qb_margin_workspace_size(32768) == 32768 * 8 and lmoe.qb_margin_workspace_size(-1) == 0
+    assert lmoe.qb_margin_workspace_size(32768, 896, 1000) == 32768 * 8 + 9 * 896 * 1000 * 4
+    assert lmoe.qb_margin_workspace_size(-1, 896, 1000) == 0 and lmoe.qb_margin_workspace_size(8, 1025, 1000) == 0
     g = lib().lmoe_bias_signsgd
     assert g(FAKE, 10, 896, 16, float("inf"), FAKE, None) == -7
     assert g(FAKE, 10, 896, 16, float("nan"), FAKE, None) == -7

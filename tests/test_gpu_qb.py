@@ -63,6 +63,12 @@ def test_accumulate_is_the_cross_batch_sum():
     H, B = ref.qb_update(np.concatenate([a, bb]), nbins, k)
     assert np.array_equal(hab, H)
     assert same_bits(bias, B)
+    # a batch of at most 256 tokens is one run, added in place rather than through the slabs
+    c = host_scores(200, n, seed=3, skew=2.0)
+    habc, bias = gpu_qb(c, k, nbins, hist=hab, accumulate=True, solve=True)
+    H, B = ref.qb_update(np.concatenate([a, bb, c]), nbins, k)
+    assert np.array_equal(habc, H)
+    assert same_bits(bias, B)
 
 
 def test_c4_shaped_batch():
