@@ -86,7 +86,7 @@ struct GemmArgs {
   const void *A;            // [rows, lda]
   int64_t lda;
   const int32_t *a_rows;    // GATHER: source row of A for each dispatched row
-  const void *B;            // [N, ldb] (GLU: W1 rows)
+  const void *B;            // [N, ldb] (GLU: W1 rows); BKN: [K, ldb], K rows of N columns
   const void *B2;           // GLU: W2 rows
   int64_t ldb;
   int64_t b_group_stride;   // GROUPED: elements between experts' B matrices
@@ -94,7 +94,8 @@ struct GemmArgs {
   const void *B2sh;         //   and its second matrix (GLU: W2)
   int n_routed;             // GROUPED: expert ids below this index B / B2
   int64_t kb_len;           // B is split along K into batches of kb_len columns,
-  int64_t kb_stride;        //   batch s starts at B + s * kb_stride
+  int64_t kb_stride;        //   batch s starts at B + s * kb_stride (BKN: K rows >= kb_len
+                            //   are rows k - kb_len of B2)
   void *C;
   int64_t ldc;
   int M, N, K;              // dense M; N = rows of B (GLU: 2 x hidden units)
@@ -152,6 +153,14 @@ template <> struct Mma<float> {
 // lanes per pass: any 8 consecutive rows get 8 distinct chunk slots, and within
 // any 16 consecutive rows the even and the odd rows each get 8 distinct slots.
 LMOE_DEV int swz(int r, int c) { return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4); }
+
+// The B tile of a GEMM whose B is stored [K, N] (BKN): each thread writes the
+// transposed pieces of 8 (bf16) or 4 (fp32) consecutive tile rows, so the chunk
+// slot also takes row bits 3..5; fragment reads keep the property above (any 8
+// consecutive rows get 8 distinct slots, and within 16 rows the even and the odd
+// rows each get 8), and the transposed writes of 8 (16 for 8-byte pieces)
+// consecutive lanes fall on distinct banks.
+LMOE_DEV int swz_kn(int r, int c) { return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 7)) << 4); }
 
 template <int V> struct IC { static constexpr int value = V; };
 
@@ -402,7 +411,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // for the loads of the next one (an LDS store after such loads would make the
 // compiler wait for all of them).
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int PF, int EPI, bool GATHER, bool GROUPED,
-          bool BDMA = false>
+          bool BDMA = false, bool BKN = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int WTN = BN / WN;
@@ -420,6 +429,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   static_assert(PF >= 1 && PF <= 4, "prefetch distance");
   static_assert(NG == 2 || NG == 4, "16-K groups per 128-byte K step");
   static_assert(!BDMA || (PF == 2 && RPP == 64 && EPI != EPI_PARTIAL), "load to LDS: two-step pipeline, 8 waves");
+  // BKN: B stored [K, N]; each thread loads KR = B_LD rows of one 16-byte column
+  // chunk and writes them transposed (through registers, so not with BDMA)
+  static_assert(!BKN || (!BDMA && !is_glu<EPI> && EPI != EPI_PARTIAL && (NT == 256 || NT == 512) && BN == 256),
+                "B stored [K, N]: register-staged, plain epilogues, 256-column tiles");
+  static_assert(!BKN || B_LD * (NT / 64) * 64 * EPT == BKE * BN, "B stored [K, N]: one column chunk per thread");
   constexpr int NSB = BDMA ? 3 : 2;  // LDS stages of B
   constexpr bool STAGED = StagedStore<TO, EPI, WTN, TN>::value;
   static_assert(!BDMA || !STAGED || (NT / 64) * STAGE_BYTES_PER_WAVE <= BN * 128, "staging fits one B stage");
@@ -446,6 +460,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   // BDMA: the chunk this lane loads so that its LDS slot (lane & 7 of row lrow)
   // holds what swz() expects: slot ^ (row & 7) ^ ((row >> 3) & 1)
   int lbc = (tid & 7) ^ ((tid >> 3) & 7) ^ ((tid >> 6) & 1);
+  // BKN: this thread's column chunk (kn_nb: EPT columns) and K group (kn_kg: B_LD
+  // rows), chosen so that the loads of a wave cover whole 512-byte row segments
+  // and the transposed LDS writes are free of bank conflicts under swz_kn:
+  //   bf16, 8 waves: 8 chunks x 2 K groups per 16 lanes; bf16, 4 waves: 8 chunks
+  //   per 8 lanes; fp32: lane = chunk, wave = K group
+  int kn_nb = 0, kn_kg = 0;
+  if constexpr (BKN) {
+    if constexpr (sizeof(T) == 2 && NT == 512) {
+      kn_nb = (lane & 7) + 8 * (lane >> 4);
+      kn_kg = 2 * wave + ((lane >> 3) & 1);
+    } else if constexpr (sizeof(T) == 2) {
+      kn_nb = (lane & 7) + 8 * ((lane >> 3) & 3);
+      kn_kg = 2 * wave + (lane >> 5);
+    } else {
+      kn_nb = lane;
+      kn_kg = wave;
+    }
+  }
 
   // ---- persistent walk over the logical tiles.  Each XCD (work-groups are
   // dispatched round-robin over the 8 XCDs) takes one contiguous range of
@@ -533,6 +565,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     const int bc = BDMA ? lbc : lchunk;
     lb1 = (const T *)t.B + bc * EPT;
     lb2 = ((is_glu<EPI> || EPI == EPI_PARTIAL) && t.B2) ? (const T *)t.B2 + bc * EPT : lb1;
+    if constexpr (BKN) {  // the thread's column chunk (clamped onto the last one: never stored)
+      const int col = min(t.nt * BN + kn_nb * EPT, p.N - EPT);
+      lb1 = (const T *)t.B + col;
+      lb2 = t.B2 ? (const T *)t.B2 + col : lb1;
+    }
     lkbeg = t.kbeg;
   };
   const T *const Abase = (const T *)p.A + lchunk * EPT;
@@ -545,6 +582,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   auto gloadB = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
     const int k0 = (lkbeg + kt) * BKE;
+    if constexpr (BKN) {  // rows k0 + kg * B_LD + i of B (K rows past kb_len: of B2)
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) {
+        const int k = k0 + kn_kg * B_LD + i;
+        const bool second = kbatch && k >= (int)p.kb_len;
+        const u32x4 *bp = (const u32x4 *)((second ? lb2 : lb1) + (int64_t)(second ? k - (int)p.kb_len : k) * p.ldb);
+        rb[S][i] = GROUPED ? __builtin_nontemporal_load(bp) : *bp;
+      }
+      return;
+    }
     int64_t boff = k0;
     if (kbatch) {  // uniform; only a K-batched B (several matrices side by side along K)
       const int s = k0 / (int)p.kb_len;
@@ -598,8 +645,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     unsigned char *sB = sB0 + buf * BN * 128;
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) *(u32x4 *)(sA + swz(lrow + i * RPP, lchunk)) = ra[S][i];
+    if constexpr (BKN) {
+      // column j of the chunk is tile row kn_nb * EPT + j; its B_LD K values
+      // (rows kn_kg * B_LD .. of the step) are element j of each loaded chunk
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) *(u32x4 *)(sB + swz(lrow + i * RPP, lchunk)) = rb[S][i];
+      for (int j = 0; j < EPT; ++j) {
+        const int r = kn_nb * EPT + j;
+        if constexpr (sizeof(T) == 2) {
+          // bf16 pairs (k, k + 1) of column j: halves j & 1 of word j >> 1
+          const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+          uint32_t w[B_LD / 2];
+#pragma unroll
+          for (int q = 0; q < B_LD / 2; ++q)
+            w[q] = __builtin_amdgcn_perm(rb[S][2 * q + 1][j >> 1], rb[S][2 * q][j >> 1], sel);
+          if constexpr (B_LD == 4) {  // 8 bytes: half kn_kg & 1 of chunk kn_kg >> 1
+            u32x2 v2 = {w[0], w[1]};
+            *(u32x2 *)(sB + swz_kn(r, kn_kg >> 1) + (kn_kg & 1) * 8) = v2;
+          } else {
+            u32x4 v4 = {w[0], w[1], w[2], w[3]};
+            *(u32x4 *)(sB + swz_kn(r, kn_kg)) = v4;
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < B_LD / 4; ++h) {
+            u32x4 v4 = {rb[S][4 * h][j], rb[S][4 * h + 1][j], rb[S][4 * h + 2][j], rb[S][4 * h + 3][j]};
+            *(u32x4 *)(sB + swz_kn(r, kn_kg * (B_LD / 4) + h)) = v4;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) *(u32x4 *)(sB + swz(lrow + i * RPP, lchunk)) = rb[S][i];
+    }
   };
 
   f32x16 acc[TM][TN];
@@ -616,7 +693,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       for (int b = 0; b < TN; ++b) {
         const int r = wn * WTN + b * 32 + l32;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) bfg[f][b][c] = *(const u32x4 *)(sB + swz(r, g * 2 * CPL + half * CPL + c));
+        for (int c = 0; c < CPL; ++c) {
+          const int ch = g * 2 * CPL + half * CPL + c;
+          bfg[f][b][c] = *(const u32x4 *)(sB + (BKN ? swz_kn(r, ch) : swz(r, ch)));
+        }
       }
 #pragma unroll
       for (int a = 0; a < TM; ++a) {

@@ -54,6 +54,9 @@ using CfgSkinny = Cfg<64, 256, 1, 4, 2>;   // dense GEMMs with M <= 64 (decode),
 using CfgW12 = Cfg<192, 256, 2, 4, 2, true>;
 using CfgUp = Cfg<192, 256, 2, 4, 2, true>;      // W_up (N = d): 192-row tiles divide its tile rounds better
 using CfgW3 = Cfg<192, 256, 2, 4, 2, true>;
+// the backward's expert data-gradient GEMMs read the expert weights in their
+// stored [K, N] layout, transposed on the way into LDS (through registers)
+using CfgExpertKN = Cfg<192, 256, 2, 4, 1, false>;
 // experts with few rows each (decode): 32-row tiles
 using CfgW12Small = Cfg<32, 256, 1, 4, 2>;
 using CfgW3Small = Cfg<32, 256, 1, 4, 2>;
@@ -196,7 +199,7 @@ int device_cus() {
 
 // Persistent launch: one work-group per resident slot (CUs x work-groups per
 // CU), each walking its share of the logical tiles.
-template <typename C, typename T, typename TO, int EPI, bool GATHER, bool GROUPED>
+template <typename C, typename T, typename TO, int EPI, bool GATHER, bool GROUPED, bool BKN = false>
 hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   constexpr int threads = 64 * C::WM * C::WN;
   constexpr bool staged = StagedStore<TO, EPI, C::BN / C::WN, C::BN / C::WN / 32>::value;
@@ -205,7 +208,7 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   constexpr int lds = (bd ? 2 * C::BM * 128 + 3 * C::BN * 128  // staging lives in a B stage
                           : 2 * (C::BM + C::BN) * 128 + (staged ? (threads / 64) * STAGE_BYTES_PER_WAVE : 0)) +
                       (GROUPED ? 16 : 0);
-  auto kern = gemm_kernel<T, TO, C::BM, C::BN, C::WM, C::WN, C::PF, EPI, GATHER, GROUPED, bd>;
+  auto kern = gemm_kernel<T, TO, C::BM, C::BN, C::WM, C::WN, C::PF, EPI, GATHER, GROUPED, bd, BKN>;
   // once per device (and per kernel): raise the kernel's LDS limit and query
   // how many of its work-groups fit on a CU
   struct PerDevice {
@@ -491,9 +494,11 @@ hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_
 }
 
 // ---------------------------------------------------------------------------
-// Backward pass.  Operands whose contraction dimension is not contiguous are
-// transposed first (weights once per call, activations per call), so every
-// product runs in the same C = A B^T MFMA GEMM as the forward:
+// Backward pass.  Products run in the forward's C = A B^T MFMA GEMM; the expert
+// data-gradient products read the expert weights in their stored [K, N] layout
+// (transposed on the way into LDS), the other operands whose contraction
+// dimension is not contiguous are transposed first (the dense weights and the
+// activations, per call):
 //   dv = dy W_up;  dW_up = dy^T v                         (dense)
 //   norm backward -> du, dg; gain gradient; router backward -> dl
 //   da = g (du W3_e)             grouped over expert rows, du rows gathered
@@ -505,7 +510,7 @@ hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_
 constexpr int BWD_SCHED = 3 * SCHED_COUNTERS;  // tile counters of the three K-range GEMMs
 
 enum {
-  B_WUPT = 0, B_WDOWNT, B_WRT, B_W3T, B_W12T, B_DV, B_DU32, B_DU, B_PROD, B_DG, B_DL, B_DA, B_DP, B_DZROWS, B_DZ,
+  B_WUPT = 0, B_WDOWNT, B_WRT, B_DV, B_DU32, B_DU, B_PROD, B_DG, B_DL, B_DA, B_DP, B_DZROWS, B_DZ,
   B_DYT, B_VT, B_DZT, B_XT, B_ZT, B_DLT, B_ZTG, B_DOT, B_DPT, B_AT, B_ENTRIES, B_BLOCKS, B_NB, B_SCHED, B_SCHED2,
   B_PART, B_COLPART, B_COUNT_
 };
@@ -534,8 +539,6 @@ WsLayout bwd_layout(const lmoe_dims &d, int dtype) {
   sz[B_WUPT] = L * d.d * es;
   sz[B_WDOWNT] = d.d * L * es;
   sz[B_WRT] = L * b.np * es;
-  sz[B_W3T] = (n + ns) * D * L * es;
-  sz[B_W12T] = 2 * (n + ns) * L * D * es;
   sz[B_DV] = T * L * 4;
   sz[B_DU32] = T * L * 4;
   sz[B_DU] = T * L * es;
@@ -618,8 +621,6 @@ hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, c
   T *wupT = (T *)(ws + B.off[B_WUPT]);
   T *wdownT = (T *)(ws + B.off[B_WDOWNT]);
   T *wrT = (T *)(ws + B.off[B_WRT]);
-  T *w3T = (T *)(ws + B.off[B_W3T]);
-  T *w12T = (T *)(ws + B.off[B_W12T]);
   float *dv = (float *)(ws + B.off[B_DV]);
   float *du32 = (float *)(ws + B.off[B_DU32]);
   T *du = (T *)(ws + B.off[B_DU]);
@@ -654,18 +655,6 @@ hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, c
   LMOE_TRY(launch_transpose<T>((const T *)w.w_up, L, 0, wupT, dd, 0, dd, L, 1, st));
   LMOE_TRY(launch_transpose<T>((const T *)w.w_down, dd, 0, wdownT, L, 0, L, dd, 1, st));
   LMOE_TRY(launch_transpose<T>((const T *)w.w_router, L, 0, wrT, np_, 0, n, L, 1, st));
-  LMOE_TRY(launch_transpose<T>((const T *)w.w3, D, (int64_t)L * D, w3T, L, (int64_t)D * L, L, D, n, st));
-  LMOE_TRY(launch_transpose<T>((const T *)w.w1, L, (int64_t)D * L, w12T, D, (int64_t)L * D, D, L, n, st));
-  LMOE_TRY(launch_transpose<T>((const T *)w.w2, L, (int64_t)D * L, w12T + (int64_t)(n + ns) * L * D, D,
-                               (int64_t)L * D, D, L, n, st));
-  if (ns > 0) {
-    LMOE_TRY(launch_transpose<T>((const T *)w.ws3, D, (int64_t)L * D, w3T + (int64_t)n * D * L, L, (int64_t)D * L,
-                                 L, D, ns, st));
-    LMOE_TRY(launch_transpose<T>((const T *)w.ws1, L, (int64_t)D * L, w12T + (int64_t)n * L * D, D, (int64_t)L * D,
-                                 D, L, ns, st));
-    LMOE_TRY(launch_transpose<T>((const T *)w.ws2, L, (int64_t)D * L, w12T + (int64_t)(2 * n + ns) * L * D, D,
-                                 (int64_t)L * D, D, L, ns, st));
-  }
   // dv = dy W_up
   {
     GemmArgs a = gargs();
@@ -715,14 +704,15 @@ hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, c
   LMOE_TRY(hipGetLastError());
   hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(64), 0, st, sched2, (int64_t)3 * SCHED_COUNTERS, 0);
   LMOE_TRY(hipGetLastError());
-  // da = g (du W3_e) for every expert row (du rows gathered by token)
+  // da = g (du W3_e) for every expert row (du rows gathered by token); W3_e [L, D]
+  // is read as stored: K = L rows of N = D columns
   {
     GemmArgs a = gargs();
-    a.A = du; a.lda = L; a.a_rows = row_token; a.B = w3T; a.Bsh = w3T + (int64_t)n * D * L; a.n_routed = n;
-    a.ldb = L; a.b_group_stride = (int64_t)D * L; a.C = da; a.ldc = D; a.N = D; a.K = L; a.tiles = tiles2;
+    a.A = du; a.lda = L; a.a_rows = row_token; a.B = w.w3; a.Bsh = w.ws3; a.n_routed = n;
+    a.ldb = D; a.b_group_stride = (int64_t)L * D; a.C = da; a.ldc = D; a.N = D; a.K = L; a.tiles = tiles2;
     a.ntiles = ntiles + 1; a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w; a.sched = sched2;
-    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, T, EPI_ROWSCALE, true, true>(a, st)));
-    else LMOE_TRY((launch_gemm<CfgW3, T, T, EPI_ROWSCALE, true, true>(a, st)));
+    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW3Small, T, T, EPI_ROWSCALE, true, true, true>(a, st)));
+    else LMOE_TRY((launch_gemm<CfgExpertKN, T, T, EPI_ROWSCALE, true, true, true>(a, st)));
   }
   // gate backward: the W1/W2 products recomputed from z, dp1 | dp2 written [R, 2D]
   {
@@ -740,15 +730,16 @@ hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, c
       else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU_BWD, true, true>(a, st)));
     }
   }
-  // dz rows = dp1 W1_e + dp2 W2_e (B = [W1_e^T | W2_e^T] along K), fp32
+  // dz rows = dp1 W1_e + dp2 W2_e, fp32: W1_e and W2_e [D, L] read as stored, one
+  // K = 2D contraction whose rows k >= D come from W2_e
   {
     GemmArgs a = gargs();
-    a.A = dp; a.lda = 2 * D; a.B = w12T; a.Bsh = w12T + (int64_t)n * L * D; a.n_routed = n; a.ldb = D;
-    a.b_group_stride = (int64_t)L * D; a.kb_len = D; a.kb_stride = (int64_t)(n + ns) * L * D;
+    a.A = dp; a.lda = 2 * D; a.B = w.w1; a.B2 = w.w2; a.Bsh = w.ws1; a.B2sh = w.ws2; a.n_routed = n; a.ldb = L;
+    a.b_group_stride = (int64_t)D * L; a.kb_len = D;
     a.C = dzrows; a.ldc = L; a.N = L; a.K = 2 * D; a.tiles = tiles1; a.ntiles = ntiles;
     a.tiles_m = (int)max_tiles(d, w12_bm(d)); a.sched = sched2 + 2 * SCHED_COUNTERS;
-    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, float, EPI_STORE, false, true>(a, st)));
-    else LMOE_TRY((launch_gemm<CfgW12, T, float, EPI_STORE, false, true>(a, st)));
+    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, float, EPI_STORE, false, true, true>(a, st)));
+    else LMOE_TRY((launch_gemm<CfgExpertKN, T, float, EPI_STORE, false, true, true>(a, st)));
   }
   // the router's part, dl W_r, as one more row block of dz rows
   {
