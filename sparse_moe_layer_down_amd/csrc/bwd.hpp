@@ -8,8 +8,8 @@
 //                      experts' weight gradients, gathered ones whose 64-wide
 //                      column blocks each belong to one expert's segment of rows
 //   bwd_scan_kernel    per-expert segments of the padded row axis of those
-//                      gathered operands, the K-range tile table and the
-//                      column-block table
+//                      gathered operands (whole 64-row blocks, at least two per
+//                      expert), the K-range tile table and the column-block table
 //   norm_bwd_wave_kernel  one wavefront per token: the aggregated latent u is
 //                      summed again from the forward's staged rows, then the
 //                      RMSNorm backward ("Kimi K3 Architecture Deep Dive" §2)
@@ -111,7 +111,9 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(const int32_t *__restric
   for (int j = 0; j < per; ++j) {
     const int e = threadIdx.x * per + j;
     const int R = e < n ? counts[e] : (e < nseg ? T : 0);
-    mine[j] = (R + TP_TILE - 1) / TP_TILE;
+    // at least two blocks per segment (zero blocks past its rows), so that every
+    // K-range tile has at least two K steps and the GEMM can prefetch across tiles
+    mine[j] = e < nseg ? max(2, (R + TP_TILE - 1) / TP_TILE) : 0;
     tot += mine[j];
   }
   sc[threadIdx.x] = tot;
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(const int32_t *__restric
     const int row0 = e < n ? offs[e] : T * k + (e - n) * T;
     entries[e] = make_int4(e, base * spb, mine[j] * spb, 0);
     for (int q = 0; q < mine[j]; ++q)
-      blocks[base + q] = make_int4(row0 + q * TP_TILE, min(TP_TILE, R - q * TP_TILE), e, 0);
+      blocks[base + q] = make_int4(row0 + q * TP_TILE, max(0, min(TP_TILE, R - q * TP_TILE)), e, 0);
     base += mine[j];
   }
   if (threadIdx.x == 1023) {

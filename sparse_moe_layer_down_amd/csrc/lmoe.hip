@@ -243,7 +243,10 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   // cross-tile prefetch needs every tile's step count to be a multiple of 2 (LDS
   // buffer parity) and of the number of register sets
   constexpr int xm = (C::PF % 2 == 0) ? C::PF : 2 * C::PF;
-  a.xpf = !a.krange && (nk_all % xm == 0) && (a.splits <= 1 || a.ksteps % xm == 0);
+  // (K-range tiles have varying step counts, at least two each by construction
+  // of their table; the load-to-LDS pipeline indexes its stages by a global step
+  // count, so it prefetches across them)
+  a.xpf = a.krange ? (C::BD ? 1 : 0) : (nk_all % xm == 0) && (a.splits <= 1 || a.ksteps % xm == 0);
   int64_t grid = std::min<int64_t>(a.n_logical, (int64_t)device_cus() * occ);
   if (grid >= 8) grid = grid / 8 * 8;
   if (a.kb_len == 0) a.kb_len = a.K;
@@ -523,9 +526,9 @@ BwdDims bwd_dims(const lmoe_dims &d) {
   b.Tp = cdiv(d.T, 64) * 64;
   b.np = cdiv(d.n, 64) * 64;
   b.R = expert_rows(d);
-  // 64-row blocks of the experts' segments (each padded to whole blocks), plus
-  // one spare block: a tile of an empty segment still loads one step
-  b.kblocks = cdiv(b.R, 64) + d.n + d.n_shared;
+  // 64-row blocks of the experts' segments (each padded to whole blocks, and to
+  // at least two: at most two more blocks per segment), plus one spare block
+  b.kblocks = cdiv(b.R, 64) + 2 * (d.n + d.n_shared);
   b.Kmax = (b.kblocks + 1) * 64;
   return b;
 }
