@@ -25,7 +25,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 COPY_BYTES = 1 << 30
-EPI = {0: "store", 1: "sigmoid", 2: "SiTU-GLU", 3: "rowscale", 4: "split-K partial", 5: "clip-GLU"}
+EPI = {0: "store", 1: "sigmoid", 2: "SiTU-GLU", 3: "rowscale", 4: "split-K partial", 5: "clip-GLU",
+       6: "gate backward", 7: "clip gate backward"}
 
 
 def source_sha256():
@@ -41,16 +42,19 @@ def source_sha256():
 
 def label(name):
     """Readable name for a kernel symbol (mangled or demangled)."""
-    m = re.search(r"gemm_kernelI(DF16b|f)(DF16b|DF16_|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELi(\d)ELi(\d)ELb(\d)ELb(\d)E", name)
+    m = re.search(r"gemm_kernelI(DF16b|f)(DF16b|DF16_|f)Li(\d+)ELi(\d+)ELi(\d)ELi(\d)ELi(\d)ELi(\d)ELb(\d)ELb(\d)E"
+                  r"(?:Lb(\d)E)?(?:Lb(\d)E)?", name)
     if m:
         out = {"f": "fp32", "DF16b": "bf16", "DF16_": "fp16"}[m.group(2)]
         return (f"gemm {m.group(3)}x{m.group(4)} waves {m.group(5)}x{m.group(6)} pf{m.group(7)} "
-                f"epi={EPI[int(m.group(8))]} out={out} gather={m.group(9)} grouped={m.group(10)}")
-    m = re.search(r"gemm_kernel<[^,]*, (\d+), (\d+), (\d), (\d), (\d), (\d), (\w+), (\w+)>", name)
+                f"epi={EPI[int(m.group(8))]} out={out} gather={m.group(9)} grouped={m.group(10)}"
+                + (" B[K,N]" if m.group(12) == "1" else ""))
+    m = re.search(r"gemm_kernel<[^,]*, (\d+), (\d+), (\d), (\d), (\d), (\d), (\w+), (\w+)(?:, (\w+))?(?:, (\w+))?>",
+                  name)
     if m:  # rocprofv3 demangles only the instances with a float output type
         return (f"gemm {m.group(1)}x{m.group(2)} waves {m.group(3)}x{m.group(4)} pf{m.group(5)} "
                 f"epi={EPI[int(m.group(6))]} out=fp32 gather={int(m.group(7) == 'true')} "
-                f"grouped={int(m.group(8) == 'true')}")
+                f"grouped={int(m.group(8) == 'true')}" + (" B[K,N]" if m.group(10) == "true" else ""))
     m = re.search(r"(\w+_kernel)", name)
     if not m:
         return name[:60]
@@ -62,7 +66,16 @@ def label(name):
 
 def stage(lab, name):
     rules = [("SiTU-GLU out=bf16 gather=1 grouped=1", "expert W1/W2 + SiTU-GLU"),
+             ("gate backward", "backward: gate (W1/W2 products recomputed)"),
+             ("rowscale out=bf16 gather=1 grouped=1 B[K,N]", "backward: da (W3 read in place)"),
+             ("grouped=1 B[K,N]", "backward: dz rows (W1, W2 read in place)"),
              ("rowscale", "expert W3 x row weight"),
+             ("store out=bf16 gather=0 grouped=1", "backward: expert weight gradients (K-range)"),
+             ("norm_bwd", "backward: RMSNorm backward, routing-weight gradients"),
+             ("colsum", "backward: gain gradient"),
+             ("router_bwd", "backward: router-logit gradients"),
+             ("bwd_scan", "backward: expert segments"),
+             ("transpose", "backward: transposes"),
              ("epi=sigmoid", "router scores"),
              ("store out=bf16 gather=0 grouped=0", "W_down / W_up"),
              ("split-K", "split-K partial sums"),
@@ -75,6 +88,7 @@ def stage(lab, name):
              ("qb_margin_solve", "QB margin form: bias solve"),
              ("signsgd", "fixed-step (SignSGD) bias update"),
              ("qb_hist", "QB histogram"),
+             ("qb_merge", "QB histogram: the runs' counts merged"),
              ("qb_pool", "QB pooled histogram"),
              ("qb_solve", "QB bias solve"),
              ("synth", "input synthesis (outside the timed region)")]
@@ -118,6 +132,22 @@ def _durations(stats_csv):
     return {label(r["Name"]): float(r["AverageNs"]) * 1e-9 for r in csv.DictReader(open(stats_csv))}
 
 
+def _grid_durations(stats_csv):
+    """Average duration (s) per (kernel name, grid size) from the kernel_trace.csv
+    written beside a kernel_stats.csv (empty if there is none)."""
+    if not stats_csv or not stats_csv.endswith("_kernel_stats.csv"):
+        return {}
+    trace = stats_csv[: -len("_kernel_stats.csv")] + "_kernel_trace.csv"
+    if not os.path.exists(trace):
+        return {}
+    acc = {}
+    for r in csv.DictReader(open(trace)):
+        key = (r["Kernel_Name"], int(r.get("Grid_Size_X") or 0) * int(r.get("Grid_Size_Y") or 1) *
+               int(r.get("Grid_Size_Z") or 1))
+        acc.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
 def calibration(calib_fetch, calib_write):
     """KiB the counters read for the 1 GiB device copy of `bench.py --only calib`
     (run alone in its own profiled process, so every copy dispatch there is that
@@ -137,6 +167,7 @@ def counters(fetch_dir, write_dir, out, cmd, title=PREFILL, stats_csv=None, cali
     (kernel, grid size), so launches of one kernel with different grids (e.g.
     the QB histogram at 1000 and at 10000 bins) stay apart."""
     dur = _durations(stats_csv)
+    gdur = _grid_durations(stats_csv)
     fetch, nf = _means(fetch_dir, "FETCH_SIZE", by_grid=True)
     write, _ = _means(write_dir, "WRITE_SIZE", by_grid=True)
     cf, cw = calibration(calib_fetch, calib_write)
@@ -152,7 +183,8 @@ def counters(fetch_dir, write_dir, out, cmd, title=PREFILL, stats_csv=None, cali
         f.write(f"Commands (from the repository root, one MI355X):\n\n```\n{cmd}\n```\n\n")
         if dur:
             f.write("GB/s = scaled traffic over the kernel's average duration in the kernel trace of the same "
-                    "workload (a separate run of the same command without counters).\n\n")
+                    "workload (a separate run of the same command without counters), per launch grid where the "
+                    "trace's dispatch list gives one.\n\n")
         f.write("| kernel | stage | grid | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled traffic (GB) | GB/s |\n"
                 "|---|---|---|---|---|---|---|---|\n")
         for key in sorted(fetch, key=lambda k: -fetch[k]):
@@ -164,7 +196,8 @@ def counters(fetch_dir, write_dir, out, cmd, title=PREFILL, stats_csv=None, cali
             w = write.get(key, 0.0)
             gb = (fetch[key] * ff + w * wf) * 1024 / 1e9
             tag = "experts_w12: " if st == "expert W1/W2 + SiTU-GLU" else ""
-            rate = f"{gb / dur[lab]:.0f}" if dur.get(lab) and "copyBuffer" not in k else ""
+            t = gdur.get((k, grid)) or dur.get(lab)
+            rate = f"{gb / t:.0f}" if t and "copyBuffer" not in k else ""
             f.write(f"| `{lab}` | {tag}{st} | {grid} | {nf[key]} | {fetch[key]:.0f} | {w:.0f} | {gb:.3f} | {rate} |\n")
         rw = [key for key in fetch if stage(label(key[0]), key[0]) == "expert W1/W2 + SiTU-GLU"]
         if len(rw) == 1:

@@ -20,6 +20,20 @@ def test_labels_and_stages():
     assert profsum.stage(profsum.label("void lmoe::topk_kernel<14>(...)"), "topk_kernel") == "top-k + routing weights"
 
 
+def test_backward_labels():
+    da = "_ZN4lmoe11gemm_kernelIDF16bDF16bLi192ELi256ELi2ELi4ELi1ELi3ELb1ELb1ELb0ELb1EEEvNS_8GemmArgsE"
+    lab = profsum.label(da)
+    assert lab.endswith("B[K,N]") and profsum.stage(lab, da) == "backward: da (W3 read in place)"
+    dz = "void gemm_kernel<bool _Accum, 192, 256, 2, 4, 1, 0, false, true, false, true>"
+    assert profsum.stage(profsum.label(dz), dz) == "backward: dz rows (W1, W2 read in place)"
+    kr = "_ZN4lmoe11gemm_kernelIDF16bDF16bLi192ELi256ELi2ELi4ELi2ELi0ELb0ELb1ELb1ELb0EEEvNS_8GemmArgsE"
+    assert profsum.stage(profsum.label(kr), kr) == "backward: expert weight gradients (K-range)"
+    gate = "_ZN4lmoe11gemm_kernelIDF16bDF16bLi192ELi256ELi2ELi4ELi2ELi6ELb1ELb1ELb1ELb0EEEvNS_8GemmArgsE"
+    assert profsum.stage(profsum.label(gate), gate).startswith("backward: gate")
+    w12 = "_ZN4lmoe11gemm_kernelIDF16bDF16bLi192ELi256ELi2ELi4ELi2ELi2ELb1ELb1ELb1ELb0EEEvNS_8GemmArgsE"
+    assert profsum.stage(profsum.label(w12), w12) == "expert W1/W2 + SiTU-GLU"
+
+
 def _write_pass(d, counter, values):
     """values: {kernel: [value, ...]} or {kernel: [(value, grid), ...]}."""
     d.mkdir()
