@@ -271,14 +271,17 @@ LMOE_DEV void store_tile(const GemmArgs &p, void *Cout, f32x16 (&acc)[TM][TN], i
             else
               o[c] = acc[a][b][4 * g + c] * rs;
           }
-          store4((TO *)(stage + l32 * 128 + ((j ^ (l32 & 7)) << 4) + half * 8), o);
+          // the 8-byte half also flips with row bit 3, so the 16 lanes of one
+          // write pass (rows 0..15 or 16..31, one half) hit 16 distinct 8-byte slots
+          store4((TO *)(stage + l32 * 128 + ((j ^ (l32 & 7)) << 4) + ((half ^ ((l32 >> 3) & 1)) << 3)), o);
         }
-        // read back whole rows: CPR lanes per row
+        // read back whole rows: CPR lanes per row (halves swapped back on rows with bit 3 set)
         constexpr int RPI = 64 / CPR;  // rows per pass
 #pragma unroll
         for (int i = 0; i < 32 / RPI; ++i) {
           const int r = lane / CPR + RPI * i, c = lane % CPR;
-          const u32x4 v = *(const u32x4 *)(stage + r * 128 + ((c ^ (r & 7)) << 4));
+          u32x4 v = *(const u32x4 *)(stage + r * 128 + ((c ^ (r & 7)) << 4));
+          if ((r >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
           if (r0 + r < rows_valid) {
             u32x4 *dst = (u32x4 *)(C + (m0 + r0 + r) * p.ldc + c_base + c * 8);
             // staged expert rows are read once, by the combine: stream them
