@@ -237,7 +237,7 @@ LMOE_DEV TileI decode_tile(const GemmArgs &p, int l, int nk_all) {
 // lines.
 template <typename TO, int EPI, int WTN, int TN>
 struct StagedStore {
-  static constexpr bool value = (EPI == EPI_ROWSCALE || EPI == EPI_STORE || (is_glu<EPI> && !is_glu_bwd<EPI>)) &&
+  static constexpr bool value = (EPI == EPI_ROWSCALE || EPI == EPI_STORE || is_glu<EPI>) &&
                                 sizeof(TO) == 2 && WTN == 64 && TN == 2;
 };
 constexpr int STAGE_BYTES_PER_WAVE = 32 * 128;
@@ -248,42 +248,61 @@ LMOE_DEV void store_tile(const GemmArgs &p, void *Cout, f32x16 (&acc)[TM][TN], i
   TO *C = (TO *)Cout;
   if constexpr (StagedStore<TO, EPI, WTN, TN>::value) {
     constexpr bool GLU = is_glu<EPI>;
-    constexpr int CPR = GLU ? 4 : 8;  // 16-byte chunks per staged row (32 or 64 outputs)
+    constexpr bool GBWD = is_glu_bwd<EPI>;  // two outputs per hidden unit: dp1 | dp2
+    constexpr int CPR = GLU ? 4 : 8;  // 16-byte chunks of one output per staged row (32 or 64 outputs)
+    constexpr int CPRR = GBWD ? 8 : CPR;  // chunks per staged row (gate backward: dp1 in 0..3, dp2 in 4..7)
     const int lane = half * 32 + l32;
     const int nout = GLU ? p.N / 2 : p.N;
     const int64_t c_base = GLU ? (int64_t)nt * (BN / 2) + wn * (WTN / 2) : (int64_t)nt * BN + wn * WTN;
-    const bool full = (p.ldc % 8) == 0 && c_base + CPR * 8 <= nout;
+    const bool full = (p.ldc % 8) == 0 && c_base + CPR * 8 <= nout && (!GBWD || (p.ldaux % 4) == 0);
 #pragma unroll
     for (int a = 0; a < TM; ++a) {
       const int r0 = (a * WM + wm) * 32;  // first tile row of this subtile
       if (r0 >= rows_valid) continue;     // wave-uniform
       const float rs = (EPI == EPI_ROWSCALE) ? p.row_scale[m0 + min(r0 + l32, rows_valid - 1)] : 1.0f;
       if (full) {
-        // write: lane (half, l32) owns row l32, outputs (chunk j) * 8 + half*4 .. +3
+        // the gate backward's da row of this lane (rows past the valid range read a valid row)
+        const TO *darow = GBWD ? (const TO *)p.aux + (m0 + min(r0 + l32, rows_valid - 1)) * p.ldaux + c_base + half * 4
+                               : nullptr;
+        // write: lane (half, l32) owns row l32, outputs (chunk j) * 8 + half*4 .. +3; the
+        // 8-byte half also flips with row bit 3, so the 16 lanes of one write pass (rows
+        // 0..15 or 16..31, one half) hit 16 distinct 8-byte slots
+        const int hoff = (half ^ ((l32 >> 3) & 1)) << 3;
 #pragma unroll
         for (int j = 0; j < CPR; ++j) {
           const int b = j / 4, g = j % 4;
-          float o[4];
+          float o[4], o2[4];
+          if constexpr (GBWD) {
+            const u32x2 dv = *(const u32x2 *)(darow + g * 8);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (GLU)
-              o[c] = glu_<EPI>(acc[a][0][4 * g + c], acc[a][1][4 * g + c], p.beta1, p.beta2);
-            else
-              o[c] = acc[a][b][4 * g + c] * rs;
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t w = dv[c >> 1];
+              const TO dac = __builtin_bit_cast(TO, (unsigned short)((c & 1) ? (w >> 16) : (w & 0xFFFFu)));
+              glu_bwd_<EPI>(acc[a][0][4 * g + c], acc[a][1][4 * g + c], to_f32(dac), p.beta1, p.beta2, o[c], o2[c]);
+            }
+            store4((TO *)(stage + l32 * 128 + (((j + 4) ^ (l32 & 7)) << 4) + hoff), o2);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              if (GLU)
+                o[c] = glu_<EPI>(acc[a][0][4 * g + c], acc[a][1][4 * g + c], p.beta1, p.beta2);
+              else
+                o[c] = acc[a][b][4 * g + c] * rs;
+            }
           }
-          // the 8-byte half also flips with row bit 3, so the 16 lanes of one
-          // write pass (rows 0..15 or 16..31, one half) hit 16 distinct 8-byte slots
-          store4((TO *)(stage + l32 * 128 + ((j ^ (l32 & 7)) << 4) + ((half ^ ((l32 >> 3) & 1)) << 3)), o);
+          store4((TO *)(stage + l32 * 128 + ((j ^ (l32 & 7)) << 4) + hoff), o);
         }
-        // read back whole rows: CPR lanes per row (halves swapped back on rows with bit 3 set)
-        constexpr int RPI = 64 / CPR;  // rows per pass
+        // read back whole rows: CPRR lanes per row (halves swapped back on rows with bit 3 set)
+        constexpr int RPI = 64 / CPRR;  // rows per pass
 #pragma unroll
         for (int i = 0; i < 32 / RPI; ++i) {
-          const int r = lane / CPR + RPI * i, c = lane % CPR;
+          const int r = lane / CPRR + RPI * i, c = lane % CPRR;
           u32x4 v = *(const u32x4 *)(stage + r * 128 + ((c ^ (r & 7)) << 4));
           if ((r >> 3) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
           if (r0 + r < rows_valid) {
-            u32x4 *dst = (u32x4 *)(C + (m0 + r0 + r) * p.ldc + c_base + c * 8);
+            // gate backward: chunks 4..7 are dp2, H = p.N / 2 columns further on
+            const int64_t col = GBWD ? (c < CPR ? c_base + c * 8 : p.N / 2 + c_base + (c - CPR) * 8) : c_base + c * 8;
+            u32x4 *dst = (u32x4 *)(C + (m0 + r0 + r) * p.ldc + col);
             // staged expert rows are read once, by the combine: stream them
             if (EPI == EPI_ROWSCALE)
               __builtin_nontemporal_store(v, dst);
@@ -303,9 +322,17 @@ LMOE_DEV void store_tile(const GemmArgs &p, void *Cout, f32x16 (&acc)[TM][TN], i
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           if (c0 + c >= nout) continue;
-          const float v = GLU ? glu_<EPI>(acc[a][0][4 * g + c], acc[a][1][4 * g + c], p.beta1, p.beta2)
-                              : acc[a][b][4 * g + c] * rs;
-          C[(m0 + rl) * p.ldc + c0 + c] = from_f32<TO>(v);
+          if constexpr (GBWD) {
+            float d1, d2;
+            const float dac = to_f32(((const TO *)p.aux)[(m0 + rl) * p.ldaux + c0 + c]);
+            glu_bwd_<EPI>(acc[a][0][4 * g + c], acc[a][1][4 * g + c], dac, p.beta1, p.beta2, d1, d2);
+            C[(m0 + rl) * p.ldc + c0 + c] = from_f32<TO>(d1);
+            C[(m0 + rl) * p.ldc + nout + c0 + c] = from_f32<TO>(d2);
+          } else {
+            const float v = GLU ? glu_<EPI>(acc[a][0][4 * g + c], acc[a][1][4 * g + c], p.beta1, p.beta2)
+                                : acc[a][b][4 * g + c] * rs;
+            C[(m0 + rl) * p.ldc + c0 + c] = from_f32<TO>(v);
+          }
         }
       }
     }
