@@ -70,6 +70,8 @@ def qb_protocol(w, dev, lmoe, synth):
     idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
     s = torch.empty((cfg.T, cfg.n), dtype=torch.float32, device=dev)
 
+    fwd_ms = []  # every forward of the protocol, timed alone with events
+
     def run(method, nbins=cfg.nbins, step=0.0):
         bias = torch.zeros(cfg.n, dtype=torch.float32, device=dev)
         w["router_bias"] = bias
@@ -79,8 +81,13 @@ def qb_protocol(w, dev, lmoe, synth):
         traj, mins, upd_ms = [], [], []
         for t in range(cfg.qb_steps + 1):
             x.copy_(synth.params.device_x(cfg, dev, step=t))
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record()
             lmoe.forward(x, w, cfg.k, y=y, topk_idx=idx, scores=s, workspace=ws, beta1=cfg.beta1,
                          beta2=cfg.beta2, eps=cfg.eps)
+            f1.record()
+            torch.cuda.synchronize()
+            fwd_ms.append((method, nbins, t, f0.elapsed_time(f1)))
             load = torch.bincount(idx.flatten().long(), minlength=cfg.n).double()
             m = load.mean()
             traj.append(float(load.max() / m))
@@ -111,6 +118,20 @@ def qb_protocol(w, dev, lmoe, synth):
     out["bins_10000"] = run("qb", nbins=10000)
     out["margin"] = run("margin")
     out["signsgd"] = {f"step_{st:g}": run("signsgd", step=st) for st in (1e-3, 1e-2, 1e-1)}
+    # the C4 forward itself (T = 32768 tokens): at step 0 (bias 0, the skewed routing) and once
+    # Quantile Balancing (1000 bins) has set the bias (steps 1-20)
+    def med(v):
+        v = sorted(v)
+        return float(v[len(v) // 2])
+
+    flops = cfg.flops_per_token() * cfg.T
+    out["forward"] = {}
+    for key, sel in (("skewed_step0", [m for (_, _, t, m) in fwd_ms if t == 0]),
+                     ("qb_balanced", [m for (me, nb, t, m) in fwd_ms if me == "qb" and nb == cfg.nbins and t > 0])):
+        fm = med(sel)
+        out["forward"][key] = {"ms_median": fm, "forwards": len(sel), "tokens_per_s": cfg.T / (fm * 1e-3),
+                               "tflops": flops / (fm * 1e-3) / 1e12,
+                               "mfma_peak_frac": flops / (fm * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     return out
 
 
