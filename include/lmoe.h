@@ -306,7 +306,16 @@ size_t lmoe_backward_workspace_size(const lmoe_dims *dims, int dtype);
  * du, g du, da, dp1, dp2, dl and dz are stored in the work dtype between steps;
  * sums run in fp32.  Restrictions: LMOE_NORM_BOTH is not supported
  * (LMOE_ERR_VALUE); L <= 4096 (LMOE_ERR_SHAPE).  T == 0 writes zero weight
- * gradients.  workspace: lmoe_backward_workspace_size() bytes. */
+ * gradients.  workspace: lmoe_backward_workspace_size() bytes.
+ * Ownership and errors: every buffer is the caller's (device pointers, 16-byte
+ * aligned, LMOE_ERR_ALIGN otherwise); the gradients must not overlap each
+ * other, the inputs or either workspace; the expert weights are read in their
+ * stored layout.  All arguments are checked before anything is launched
+ * (LMOE_ERR_NULL for a missing required pointer or, with shared experts, a
+ * missing shared gradient; LMOE_ERR_SHAPE for shared gradients without shared
+ * experts; LMOE_ERR_WORKSPACE when either workspace is too small); a launch
+ * that fails returns LMOE_ERR_HIP.  The call does not synchronise with the
+ * host; calls that share a workspace must not overlap. */
 int lmoe_backward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const void *x, const void *dy,
                   const int32_t *topk_idx, const float *topk_w, const float *scores, const void *fwd_workspace,
                   size_t fwd_workspace_bytes, const lmoe_grads *grads, void *workspace, size_t workspace_bytes,
