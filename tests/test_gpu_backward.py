@@ -157,3 +157,48 @@ def test_backward_k3_prefill_sampled():
     bad.append(check_grad(cfg.dtype, cfg.d, "dw_up", gpu["dw_up"][rows], wup, "C2 bwd dw_up rows"))
     bad = [b for b in bad if b]
     assert not bad, "; ".join(bad)
+
+
+def test_backward_replays_from_a_hip_graph():
+    """The backward enqueues kernels only (its tile counters are zeroed by a
+    kernel, not a memset; no host synchronisation), and every output element is
+    computed by one work-group, so a captured backward replays bit for bit: each
+    of several replays, with a new upstream gradient copied in before two of them
+    and unrelated eager forwards between them, equals the eager backward."""
+    cfg = synth.get_config("C1").with_(T=512)
+    dev = torch.device("cuda:0")
+    w = synth.device_params(cfg, device=dev, with_x=False)
+    x = synth.params.device_x(cfg, dev)
+    T = x.shape[0]
+    dy1 = torch.empty_like(x)
+    synth.device_fill(dy1, cfg.x_seed, synth.TID["dy"], 0, 1.0)
+    dy2 = torch.empty_like(x)
+    synth.device_fill(dy2, cfg.x_seed + 1, synth.TID["dy"], 0, 1.0)
+    idx = torch.empty((T, cfg.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, cfg.k), dtype=torch.float32, device=dev)
+    s = torch.empty((T, cfg.n), dtype=torch.float32, device=dev)
+    dims = lmoe.dims_of(x, w, cfg.k)
+    ws = lmoe.make_workspace(dims, x.dtype, dev)
+    kw = dict(beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps)
+    lmoe.forward(x, w, cfg.k, topk_idx=idx, topk_w=tw, scores=s, workspace=ws, **kw)
+    bws = torch.empty(lmoe.backward_workspace_size(dims, x.dtype), dtype=torch.uint8, device=dev)
+    refs = []
+    for dy in (dy1, dy2):
+        g = lmoe.backward(x, dy, w, cfg.k, idx, tw, s, ws, workspace=bws, **kw)
+        refs.append({kk: v.clone() for kk, v in g.items() if v is not None})
+    dyin = dy1.clone()
+    grads = lmoe.backward(x, dyin, w, cfg.k, idx, tw, s, ws, workspace=bws, **kw)  # the buffers the graph writes
+    x_other = synth.params.device_x(cfg.with_(x_seed=9), dev)
+    ws_other = lmoe.make_workspace(dims, x.dtype, dev)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lmoe.backward(x, dyin, w, cfg.k, idx, tw, s, ws, grads=grads, workspace=bws, **kw)
+    for i, (src, want) in enumerate([(dy1, refs[0]), (dy2, refs[1]), (dy2, refs[1]), (dy1, refs[0])]):
+        dyin.copy_(src)
+        lmoe.forward(x_other, w, cfg.k, workspace=ws_other, **kw)  # unrelated eager work on the stream
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for kk, v in want.items():
+            assert torch.equal(grads[kk], v), f"replay {i}: {kk}"
