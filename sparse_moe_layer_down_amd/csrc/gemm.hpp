@@ -120,6 +120,7 @@ struct GemmArgs {
   int kr_tn;                // K-range: N tiles per entry
   void *Csh;
   int64_t c_group_stride;
+  int64_t a_nrows;          // load-to-LDS grouped GEMMs: rows of A (its byte offsets must stay below 4 GiB)
 };
 
 template <typename T> struct Mma;
@@ -426,6 +427,15 @@ LMOE_DEV void store_tile(const GemmArgs &p, void *Cout, f32x16 (&acc)[TM][TN], i
 // how many K steps ahead the global loads run (PF register sets).  M subtiles of 32 rows are interleaved over the
 // wave rows (wave wm owns subtiles wm, wm + WM, ...) so that a partially
 // filled M tile still spreads its valid rows over the waves.
+// Buffer resource over 4 GiB from base p (raw addressing: offsets below
+// 2^32 - 1 are in range).  The address is made explicitly uniform, so the
+// resource lives in scalar registers.
+LMOE_DEV __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p) {
+  const uint64_t a = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, -1, 0x00020000);
+}
 // s_waitcnt with lgkmcnt(0), expcnt untouched and vmcnt(N), N < 64
 template <int N> LMOE_DEV void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -567,11 +577,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   bool b_w2[B_LD];  // GLU / split-K: row comes from B2
   const T *lb1, *lb2;  // B (and B2) of the tile being loaded, at this thread's 16-B chunk
   int lkbeg;        // first K step
+  // BDMA: buffer resources of A and of the tile's B (or B2) matrix this wave
+  // loads from, and the byte offset of this lane's chunk of each B row it loads
+  // (the K offset goes in soffset)
+  const __amdgpu_buffer_rsrc_t rsA = uniform_rsrc(p.A);
+  __amdgpu_buffer_rsrc_t rsB = rsA;
+  int b_vo[B_LD];  // (int: with an unsigned array here the host pass silently drops the kernel)
+  // (BDMA: out[i] is the byte offset of the lane's chunk of row i from A,
+  // which the host keeps below 4 GiB)
   auto rows_of = [&](const TileI &t, int (&out)[A_LD]) {
 #pragma unroll
     for (int i = 0; i < A_LD; ++i) {
       const int r = min(lrow + i * RPP, t.rows - 1);
-      out[i] = GATHER ? p.a_rows[t.m0 + r] : (int)(t.m0 + r);
+      const int row = GATHER ? p.a_rows[t.m0 + r] : (int)(t.m0 + r);
+      out[i] = BDMA ? (int)((uint32_t)row * (uint32_t)(p.lda * sizeof(T)) + (uint32_t)lbc * 16u) : row;
     }
   };
   auto set_b = [&](const TileI &t) {
@@ -600,10 +619,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       lb1 = (const T *)t.B + col;
       lb2 = t.B2 ? (const T *)t.B2 + col : lb1;
     }
-    lkbeg = t.kbeg;
+    if constexpr (BDMA) {
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) b_vo[i] = (int)((uint32_t)b_row[i] * (uint32_t)(p.ldb * sizeof(T)) + (uint32_t)lbc * 16u);
+      // GLU: the 8 rows of each of the wave's loads lie in one 32-row block, of W1
+      // or W2, and adding 64 rows (a load pass) keeps the block's parity, so the
+      // wave reads one matrix throughout
+      const bool w2 = is_glu<EPI> && ((((8 * wave) % WTN) / 32) & 1) != 0;
+      rsB = uniform_rsrc((w2 && t.B2) ? t.B2 : t.B);
+    }
+    lkbeg = __builtin_amdgcn_readfirstlane(t.kbeg);  // uniform (a buffer offset operand)
   };
   const T *const Abase = (const T *)p.A + lchunk * EPT;
-  const T *const AbaseD = (const T *)p.A + lbc * EPT;  // BDMA: this lane's swizzled chunk
 
   // register sets of staged global loads (see the pipeline below)
   u32x4 ra[NSET][A_LD], rb[NSET][B_LD];
@@ -645,23 +672,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       const int s = k0 / (int)p.kb_len;
       boff = (int64_t)s * p.kb_stride + (k0 - s * (int)p.kb_len);
     }
+    const uint32_t so = (uint32_t)(boff * (int64_t)sizeof(T));
     unsigned char *dst = sB0 + (g % NSB) * BN * 128 + wave * 8 * 128;
 #pragma unroll
     for (int i = 0; i < B_LD; ++i) {
-      const T *src = (b_w2[i] ? lb2 : lb1) + (int64_t)b_row[i] * p.ldb + boff;
       // expert weights are streamed once (non-temporal); dense B is re-read by other M tiles
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(dst + i * RPP * 128), 16, 0, GROUPED ? 2 : 0);
+      if constexpr (GROUPED)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t *)(dst + i * RPP * 128), 16, (uint32_t)b_vo[i], so, 0, 2);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t *)(dst + i * RPP * 128), 16, (uint32_t)b_vo[i], so, 0, 0);
     }
   };
   // BDMA: A of tile step kt into the LDS stage of global step g (rows as for B)
   auto dmaA = [&](int kt, int g) {
-    const int64_t k0 = (int64_t)(lkbeg + kt) * BKE;
+    const uint32_t so = (uint32_t)((lkbeg + kt) * BKE * (int)sizeof(T));
     unsigned char *dst = sA0 + (g & 1) * BM * 128 + wave * 8 * 128;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const T *src = AbaseD + (int64_t)a_row[i] * p.lda + k0;
-      __builtin_amdgcn_global_load_lds((const void *)src, (lds_void_t *)(dst + i * RPP * 128), 16, 0, 0);
-    }
+    for (int i = 0; i < A_LD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void_t *)(dst + i * RPP * 128), 16, (uint32_t)a_row[i], so, 0, 0);
   };
   auto gloadA = [&](auto SETC, int kt) {
     constexpr int S = decltype(SETC)::value;
@@ -771,6 +799,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     if (NG > 3) mma(IC<1>{});
   };
 
+  // BDMA K steps run as fenced phases over two fragment register sets: phase i
+  // issues the LDS reads of 16-K group i + 1 and then the MFMAs of group i (whose
+  // reads the previous phase issued), and the group-0 reads of the next step are
+  // issued right after the barrier that makes its operands visible, ahead of the
+  // MFMAs of the step's last group.  The fences keep the compiler from pulling
+  // reads next to the MFMAs that consume them, so each wait covers only reads
+  // issued a full phase earlier.  SK (a compile-time flag, chosen once per tile)
+  // drops the wave's last M subtile when it holds only padding rows.
+  u32x4 fa[2][TM][CPL], fb[2][TN][CPL];
+  auto rd = [&](auto SKC, auto GC, auto SC, int oa, int ob) {
+    constexpr bool SK = decltype(SKC)::value != 0;
+    constexpr int g = decltype(GC)::value, f = decltype(SC)::value;
+    const unsigned char *sA = sA0 + oa, *sB = sB0 + ob;
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      const int r = wn * WTN + b * 32 + l32;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) fb[f][b][c] = *(const u32x4 *)(sB + swz(r, g * 2 * CPL + half * CPL + c));
+    }
+#pragma unroll
+    for (int a = 0; a < TM - (SK ? 1 : 0); ++a) {
+      const int r = (a * WM + wm) * 32 + l32;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) fa[f][a][c] = *(const u32x4 *)(sA + swz(r, g * 2 * CPL + half * CPL + c));
+    }
+  };
+  auto mm = [&](auto SKC, auto SC) {
+    constexpr bool SK = decltype(SKC)::value != 0;
+    constexpr int f = decltype(SC)::value;
+#pragma unroll
+    for (int a = 0; a < TM - (SK ? 1 : 0); ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) Mma<T>::run(fb[f][b], fa[f][a], acc[a][b]);
+  };
+  auto phase = [&](auto SKC, auto GC, auto SN, auto SM, int oa, int ob) {
+    constexpr bool SK = decltype(SKC)::value != 0;
+    constexpr int NR = (TN + TM - (SK ? 1 : 0)) * CPL;
+    constexpr int NM = TN * (TM - (SK ? 1 : 0)) * (sizeof(T) == 4 ? 8 : 1);
+    rd(SKC, GC, SN, oa, ob);
+    mm(SKC, SM);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // the reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // then the MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   // Pipeline (one barrier per K step).
   //  PF == 1: A(kt+1), B(kt+1) are loaded at the start of step kt and stored to
   //           the other LDS buffer after the step's MFMAs.
@@ -872,43 +945,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     auto step = [&](auto SETC, auto CHECKC, int kt) {
       constexpr int S = decltype(SETC)::value;  // == kt % NSET
       constexpr bool CHECK = decltype(CHECKC)::value != 0;
-      if constexpr (BDMA) {
-        const int g = gbase + kt;
-        bool b_iss = false;
-        {  // A of step kt + 1 (or the next tile's step 0)
-          const int j = kt + 1;
-          if (!CHECK || j < nk) {
-            dmaA(j, g + 1);
-          } else if (xnext) {
-            if (j == nk) {
-#pragma unroll
-              for (int i = 0; i < A_LD; ++i) a_row[i] = n_row[i];
-            }
-            dmaA(j - nk, g + 1);
-          }
-        }
-        {  // B of step kt + 2 (or of the next tile's step kt + 2 - nk)
-          const int j = kt + 2;
-          if (!CHECK || j < nk) {
-            dmaB(j, g + 2);
-            b_iss = true;
-          } else if (xnext) {
-            if (j == nk) set_b(nxt);
-            dmaB(j - nk, g + 2);
-            b_iss = true;
-          }
-        }
-        compute(g & 1, sB0 + (g % NSB) * BN * 128, [] {});
-        if (GROUPED && dyn && kt == 0 && tid == 0) qslot[tile_par] = grabbed;
-        // A and B of step kt + 1 must be in LDS: only this step's B loads (if
-        // any) were issued after them
-        if (b_iss) wait_vm_lgkm0<B_LD>();
-        else wait_vm_lgkm0<0>();
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        return;
-      }
       const bool st_next = !CHECK || kt + 1 < nk || xnext;
       const unsigned char *sBk = sB0 + (kt & 1) * BN * 128;
       if (PF == 1) {
@@ -924,6 +960,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
       if (GROUPED && dyn && kt == 0 && tid == 0) qslot[tile_par] = grabbed;
       __syncthreads();
     };
+    // BDMA: one K step (see the phase comment above)
+    auto pstep = [&](auto SKC, auto CHECKC, int kt) {
+      constexpr bool CHECK = decltype(CHECKC)::value != 0;
+      const int g = gbase + kt;
+      bool b_iss = false;
+      {  // A of step kt + 1 (or the next tile's step 0)
+        const int j = kt + 1;
+        if (!CHECK || j < nk) {
+          dmaA(j, g + 1);
+        } else if (xnext) {
+          if (j == nk) {
+#pragma unroll
+            for (int i = 0; i < A_LD; ++i) a_row[i] = n_row[i];
+          }
+          dmaA(j - nk, g + 1);
+        }
+      }
+      {  // B of step kt + 2 (or of the next tile's step kt + 2 - nk)
+        const int j = kt + 2;
+        if (!CHECK || j < nk) {
+          dmaB(j, g + 2);
+          b_iss = true;
+        } else if (xnext) {
+          if (j == nk) set_b(nxt);
+          dmaB(j - nk, g + 2);
+          b_iss = true;
+        }
+      }
+      const int oa = (g & 1) * BM * 128, ob = (g % NSB) * BN * 128;
+      __builtin_amdgcn_sched_barrier(0);
+      phase(SKC, IC<1>{}, IC<1>{}, IC<0>{}, oa, ob);
+      if constexpr (NG == 4) {
+        phase(SKC, IC<2>{}, IC<0>{}, IC<1>{}, oa, ob);
+        phase(SKC, IC<3>{}, IC<1>{}, IC<0>{}, oa, ob);
+      }
+      if (GROUPED && dyn && kt == 0 && tid == 0) qslot[tile_par] = grabbed;
+      // A and B of step kt + 1 must be in LDS (only this step's B loads, if
+      // any, were issued after them) and this step's reads done
+      if (b_iss) wait_vm_lgkm0<B_LD>();
+      else wait_vm_lgkm0<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (!CHECK || kt + 1 < nk) rd(SKC, IC<0>{}, IC<0>{}, ((g + 1) & 1) * BM * 128, ((g + 1) % NSB) * BN * 128);
+      mm(SKC, IC<1>{});
+      __builtin_amdgcn_sched_barrier(0);
+    };
     // NSET consecutive steps (register set indices known at compile time)
     auto steps = [&](auto CHECKC, int kt) {
       constexpr bool CHECK = decltype(CHECKC)::value != 0;
@@ -936,7 +1019,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     // hold copies of a valid row and are never stored): the K loop stays free
     // of branches, and the MFMA time of a full tile is still below the time to
     // stream its weights.
-    {
+    if constexpr (BDMA) {
+      auto kloop = [&](auto SKC) {
+        if (nk > 0) rd(SKC, IC<0>{}, IC<0>{}, (gbase & 1) * BM * 128, (gbase % NSB) * BN * 128);
+        int kt = 0;
+        for (; kt + 2 < nk; ++kt) pstep(SKC, IC<0>{}, kt);
+        for (; kt < nk; ++kt) pstep(SKC, IC<1>{}, kt);
+      };
+      if (skip_last) kloop(IC<1>{});
+      else kloop(IC<0>{});
+    } else {
       int kt = 0;
       for (; kt + NSET + PF <= nk; kt += NSET) steps(IC<0>{}, kt);
       for (; kt < nk; kt += NSET) steps(IC<1>{}, kt);

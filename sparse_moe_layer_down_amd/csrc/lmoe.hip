@@ -239,6 +239,14 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   if (!GROUPED) a.tiles_m = (int)cdiv(a.M, C::BM);
   a.n_logical = a.tiles_m * a.tiles_n * (GROUPED ? 1 : std::max(a.splits, 1));
   if (a.n_logical == 0) return hipSuccess;
+  if constexpr (bd) {
+    // the load-to-LDS path addresses A and each B matrix through 32-bit byte
+    // offsets (buffer loads): both must span less than 4 GiB
+    const int64_t arows = GROUPED && !a.krange ? a.a_nrows : a.M;
+    if (arows <= 0 || arows * a.lda * (int64_t)sizeof(T) >= ((int64_t)1 << 32) ||
+        (int64_t)a.N * a.ldb * (int64_t)sizeof(T) >= ((int64_t)1 << 32))
+      return hipErrorInvalidValue;
+  }
   const int nk_all = a.K / bke;
   // cross-tile prefetch needs every tile's step count to be a multiple of 2 (LDS
   // buffer parity) and of the number of register sets
@@ -377,7 +385,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
   LMOE_MARK(4);
   {
     GemmArgs a = gargs();
-    a.A = z; a.lda = L; a.a_rows = row_token; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
+    a.A = z; a.lda = L; a.a_rows = row_token; a.a_nrows = T_; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
     a.Bsh = w.ws1; a.B2sh = w.ws2; a.n_routed = n;
     a.b_group_stride = (int64_t)D * L; a.C = hid; a.ldc = D;
     a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, w12_bm(d));
@@ -399,7 +407,8 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
     LMOE_MARK(5);
     {
       GemmArgs a = gargs();
-      a.A = hid; a.lda = D; a.B = w.w3; a.Bsh = w.ws3; a.n_routed = n; a.ldb = D; a.b_group_stride = (int64_t)L * D;
+      a.A = hid; a.lda = D; a.a_nrows = expert_rows(d); a.B = w.w3; a.Bsh = w.ws3; a.n_routed = n; a.ldb = D;
+      a.b_group_stride = (int64_t)L * D;
       a.C = (TS *)ystage; a.ldc = L; a.N = L; a.K = D; a.tiles = tiles2; a.ntiles = ntiles + 1;
       a.tiles_m = (int)max_tiles(d, w3_bm(d)); a.row_scale = row_w;
       a.sched = ntiles + 2 + SCHED_COUNTERS;
@@ -720,7 +729,7 @@ hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, c
   // gate backward: the W1/W2 products recomputed from z, dp1 | dp2 written [R, 2D]
   {
     GemmArgs a = gargs();
-    a.A = z; a.lda = L; a.a_rows = row_token; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
+    a.A = z; a.lda = L; a.a_rows = row_token; a.a_nrows = T_; a.B = w.w1; a.B2 = w.w2; a.ldb = L;
     a.Bsh = w.ws1; a.B2sh = w.ws2; a.n_routed = n;
     a.b_group_stride = (int64_t)D * L; a.C = dp; a.ldc = 2 * D;
     a.N = 2 * D; a.K = L; a.tiles = tiles1; a.ntiles = ntiles; a.tiles_m = (int)max_tiles(d, w12_bm(d));
