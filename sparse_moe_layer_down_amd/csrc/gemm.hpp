@@ -665,17 +665,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
   };
   // BDMA: B of tile step kt into the LDS stage of global step g; instruction i of
   // wave w writes tile rows 8w + 64i .. +7 (1 KB), one row chunk per lane
-  auto dmaB = [&](int kt, int g) {
-    const int k0 = (lkbeg + kt) * BKE;
-    int64_t boff = k0;
-    if (kbatch) {
-      const int s = k0 / (int)p.kb_len;
-      boff = (int64_t)s * p.kb_stride + (k0 - s * (int)p.kb_len);
-    }
-    const uint32_t so = (uint32_t)(boff * (int64_t)sizeof(T));
+  // (B is one matrix along K here: no K batches, checked at launch)
+  auto dmaBr = [&](auto I0, auto I1, int kt, int g) {
+    const uint32_t so = (uint32_t)((lkbeg + kt) * BKE * (int)sizeof(T));
     unsigned char *dst = sB0 + (g % NSB) * BN * 128 + wave * 8 * 128;
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
+    for (int i = decltype(I0)::value; i < decltype(I1)::value; ++i) {
       // expert weights are streamed once (non-temporal); dense B is re-read by other M tiles
       if constexpr (GROUPED)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t *)(dst + i * RPP * 128), 16, (uint32_t)b_vo[i], so, 0, 2);
@@ -683,6 +678,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void_t *)(dst + i * RPP * 128), 16, (uint32_t)b_vo[i], so, 0, 0);
     }
   };
+  auto dmaB = [&](int kt, int g) { dmaBr(IC<0>{}, IC<B_LD>{}, kt, g); };
   // BDMA: A of tile step kt into the LDS stage of global step g (rows as for B)
   auto dmaA = [&](int kt, int g) {
     const uint32_t so = (uint32_t)((lkbeg + kt) * BKE * (int)sizeof(T));
@@ -833,14 +829,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int b = 0; b < TN; ++b) Mma<T>::run(fb[f][b], fa[f][a], acc[a][b]);
   };
-  auto phase = [&](auto SKC, auto GC, auto SN, auto SM, int oa, int ob) {
+  // (dma issues ND global-to-LDS loads of later steps, one after each of the
+  // phase's first MFMAs, so no wave stalls on a burst of them while its MFMAs
+  // could run)
+  auto phase = [&](auto SKC, auto GC, auto SN, auto SM, int oa, int ob, auto &&dma, auto NDC) {
     constexpr bool SK = decltype(SKC)::value != 0;
     constexpr int NR = (TN + TM - (SK ? 1 : 0)) * CPL;
     constexpr int NM = TN * (TM - (SK ? 1 : 0)) * (sizeof(T) == 4 ? 8 : 1);
+    constexpr int ND = decltype(NDC)::value;
+    static_assert(ND <= NM, "one load per MFMA at most");
     rd(SKC, GC, SN, oa, ob);
     mm(SKC, SM);
+    dma();
     __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // the reads first
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);  // then the MFMAs
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // an MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // a load
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - ND, 0);  // the other MFMAs
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -964,36 +971,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
     auto pstep = [&](auto SKC, auto CHECKC, int kt) {
       constexpr bool CHECK = decltype(CHECKC)::value != 0;
       const int g = gbase + kt;
-      bool b_iss = false;
-      {  // A of step kt + 1 (or the next tile's step 0)
-        const int j = kt + 1;
-        if (!CHECK || j < nk) {
-          dmaA(j, g + 1);
-        } else if (xnext) {
-          if (j == nk) {
+      // A of step kt + 1 and B of step kt + 2 (past the tile's end: the next
+      // tile's first steps, whose source rows are switched in just before)
+      const int ja = kt + 1, jb = kt + 2;
+      const bool a_iss = !CHECK || ja < nk || xnext;
+      const bool b_iss = !CHECK || jb < nk || xnext;
+      if (CHECK && ja == nk && xnext) {
 #pragma unroll
-            for (int i = 0; i < A_LD; ++i) a_row[i] = n_row[i];
-          }
-          dmaA(j - nk, g + 1);
-        }
+        for (int i = 0; i < A_LD; ++i) a_row[i] = n_row[i];
       }
-      {  // B of step kt + 2 (or of the next tile's step kt + 2 - nk)
-        const int j = kt + 2;
-        if (!CHECK || j < nk) {
-          dmaB(j, g + 2);
-          b_iss = true;
-        } else if (xnext) {
-          if (j == nk) set_b(nxt);
-          dmaB(j - nk, g + 2);
-          b_iss = true;
-        }
-      }
+      const int ka = (!CHECK || ja < nk) ? ja : ja - nk;
+      const int kb = (!CHECK || jb < nk) ? jb : jb - nk;
+      auto dA = [&] {
+        if (a_iss) dmaA(ka, g + 1);
+      };
+      // (the B rows switch after the A loads, which still use this tile's K start)
+      auto dB0 = [&] {
+        if (CHECK && jb == nk && xnext) set_b(nxt);
+        if (b_iss) dmaBr(IC<0>{}, IC<B_LD / 2>{}, kb, g + 2);
+      };
+      auto dB1 = [&] {
+        if (b_iss) dmaBr(IC<B_LD / 2>{}, IC<B_LD>{}, kb, g + 2);
+      };
       const int oa = (g & 1) * BM * 128, ob = (g % NSB) * BN * 128;
       __builtin_amdgcn_sched_barrier(0);
-      phase(SKC, IC<1>{}, IC<1>{}, IC<0>{}, oa, ob);
       if constexpr (NG == 4) {
-        phase(SKC, IC<2>{}, IC<0>{}, IC<1>{}, oa, ob);
-        phase(SKC, IC<3>{}, IC<1>{}, IC<0>{}, oa, ob);
+        phase(SKC, IC<1>{}, IC<1>{}, IC<0>{}, oa, ob, dA, IC<A_LD>{});
+        phase(SKC, IC<2>{}, IC<0>{}, IC<1>{}, oa, ob, dB0, IC<B_LD / 2>{});
+        phase(SKC, IC<3>{}, IC<1>{}, IC<0>{}, oa, ob, dB1, IC<B_LD - B_LD / 2>{});
+      } else {
+        phase(SKC, IC<1>{}, IC<1>{}, IC<0>{}, oa, ob, [&] { dA(); dB0(); dB1(); }, IC<A_LD + B_LD>{});
       }
       if (GROUPED && dyn && kt == 0 && tid == 0) qslot[tile_par] = grabbed;
       // A and B of step kt + 1 must be in LDS (only this step's B loads, if

@@ -241,10 +241,11 @@ hipError_t launch_gemm(GemmArgs a, hipStream_t st) {
   if (a.n_logical == 0) return hipSuccess;
   if constexpr (bd) {
     // the load-to-LDS path addresses A and each B matrix through 32-bit byte
-    // offsets (buffer loads): both must span less than 4 GiB
+    // offsets (buffer loads): both must span less than 4 GiB; B is one matrix
+    // along K (no K batches)
     const int64_t arows = GROUPED && !a.krange ? a.a_nrows : a.M;
     if (arows <= 0 || arows * a.lda * (int64_t)sizeof(T) >= ((int64_t)1 << 32) ||
-        (int64_t)a.N * a.ldb * (int64_t)sizeof(T) >= ((int64_t)1 << 32))
+        (int64_t)a.N * a.ldb * (int64_t)sizeof(T) >= ((int64_t)1 << 32) || (a.kb_len != 0 && a.kb_len != a.K))
       return hipErrorInvalidValue;
   }
   const int nk_all = a.K / bke;
