@@ -68,7 +68,15 @@ typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
  *   n         routed experts, 1..1024
  *   k         experts chosen per token, 1..min(n, 64)
  *   n_shared  shared experts, 0..8
- *   D         expert hidden width; multiple of 64                              */
+ *   D         expert hidden width; multiple of 64
+ * Also d <= 65536, L <= 8192, D <= 65536 and T * (k + n_shared) < 2^31; and,
+ * since the large GEMMs address each operand through 32-bit byte offsets,
+ * every activation and weight matrix they read must span less than 4 GiB at
+ * the work dtype: T*d, T*L, T*(k + n_shared)*D, L*d, n*L and 2*D*L elements
+ * (lmoe_backward adds d, L and n rounded up to 64 times T rounded up to 64,
+ * and L and 2*D times the padded expert-row count, about T*(k + n_shared) +
+ * 128*(n + n_shared)).  Dims outside these rules give LMOE_ERR_SHAPE (and a
+ * workspace size of 0).                                                      */
 typedef struct {
   int64_t T, d, L, n, k, n_shared, D;
 } lmoe_dims;

@@ -543,6 +543,19 @@ BwdDims bwd_dims(const lmoe_dims &d) {
   return b;
 }
 
+// The load-to-LDS GEMMs address each operand through 32-bit byte offsets
+// (buffer loads), so every matrix they read must span less than 4 GiB; the
+// forward's and (backward) the backward's operands, at the work dtype.
+bool spans_fit(const lmoe_dims &d, int dtype, bool backward) {
+  const int64_t es = dtype == LMOE_BF16 ? 2 : 4;
+  int64_t m = std::max({d.T * d.d, d.T * d.L, expert_rows(d) * d.D, d.L * d.d, d.n * d.L, 2 * d.D * d.L});
+  if (backward) {
+    const BwdDims b = bwd_dims(d);
+    m = std::max({m, d.T * b.np, d.d * b.Tp, d.L * b.Tp, b.np * b.Tp, d.L * b.Kmax, 2 * d.D * b.Kmax});
+  }
+  return m * es < ((int64_t)1 << 32);
+}
+
 WsLayout bwd_layout(const lmoe_dims &d, int dtype) {
   const int64_t es = dtype == LMOE_BF16 ? 2 : 4;
   const int bke = (int)(128 / es);
@@ -829,6 +842,7 @@ extern "C" {
 
 size_t lmoe_workspace_size(const lmoe_dims *dims, int dtype) {
   if (check_dims(dims) != LMOE_OK || (dtype != LMOE_F32 && dtype != LMOE_BF16)) return 0;
+  if (!spans_fit(*dims, dtype, false)) return 0;
   return (size_t)layout(*dims, dtype).total;
 }
 
@@ -845,6 +859,7 @@ static int forward_impl(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   if (rc != LMOE_OK) return rc;
   if (!w) return LMOE_ERR_NULL;
   if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
+  if (!spans_fit(*dims, dtype, false)) return LMOE_ERR_SHAPE;
   if (!(w->beta1 > 0.0f) || !(w->beta2 > 0.0f) || !(w->rms_eps >= 0.0f) || w->rms_eps == INFINITY ||
       (w->gate != LMOE_GATE_TANH && w->gate != LMOE_GATE_CLIP) || (w->norm != LMOE_NORM_RMS && w->norm != LMOE_NORM_NONE && w->norm != LMOE_NORM_BOTH))
     return LMOE_ERR_VALUE;
@@ -928,6 +943,7 @@ int lmoe_forward_static(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   int rc = check_dims(dims);
   if (rc != LMOE_OK) return rc;
   if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
+  if (!spans_fit(*dims, dtype, false)) return LMOE_ERR_SHAPE;
   const int64_t need = layout(*dims, dtype).total;
   if (need > (int64_t)LMOE_STATIC_SCRATCH_BYTES) return LMOE_ERR_SCRATCH;
   if (dims->T == 0) return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, nullptr, 0, stream, nullptr);
@@ -982,6 +998,7 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
 
 size_t lmoe_backward_workspace_size(const lmoe_dims *dims, int dtype) {
   if (check_dims(dims) != LMOE_OK || (dtype != LMOE_F32 && dtype != LMOE_BF16) || dims->L > 4096) return 0;
+  if (!spans_fit(*dims, dtype, true)) return 0;
   return (size_t)bwd_layout(*dims, dtype).total;
 }
 
@@ -994,6 +1011,7 @@ int lmoe_backward(const lmoe_dims *dims, const lmoe_weights *w, int dtype, const
   if (dims->L > 4096) return LMOE_ERR_SHAPE;
   if (!w || !grads) return LMOE_ERR_NULL;
   if (dtype != LMOE_F32 && dtype != LMOE_BF16) return LMOE_ERR_DTYPE;
+  if (!spans_fit(*dims, dtype, true)) return LMOE_ERR_SHAPE;
   if (!(w->beta1 > 0.0f) || !(w->beta2 > 0.0f) || !(w->rms_eps >= 0.0f) || w->rms_eps == INFINITY ||
       (w->gate != LMOE_GATE_TANH && w->gate != LMOE_GATE_CLIP) || (w->norm != LMOE_NORM_RMS && w->norm != LMOE_NORM_NONE))
     return LMOE_ERR_VALUE;

@@ -80,6 +80,24 @@ def test_shape_errors(dims, code):
     assert call(dims, fake_weights()) == code
 
 
+def test_operand_span_limit():
+    """The load-to-LDS GEMMs address each operand through 32-bit byte offsets, so
+    dims whose operands would span 4 GiB or more are rejected up front: at
+    T = 150000 and d = 7168, x is 4.3 GB in fp32 (rejected) and 2.15 GB in bf16
+    (accepted); the backward's gathered-row transposes [L, ~T(k + n_s)] reach
+    5.05 GB at T = 32768 in bf16 (rejected) and 1.88 GB at T = 8192."""
+    big = c2dims(T=150000)
+    assert lmoe.workspace_size(big, 0) == 0
+    assert call(big, fake_weights(), dtype=0) == -2
+    assert lib().lmoe_forward_static(ctypes.byref(big), ctypes.byref(fake_weights()), 0, FAKE, FAKE, None, None,
+                                     None, None) == -2
+    assert lmoe.workspace_size(big, 1) > 0
+    bws = lib().lmoe_backward_workspace_size
+    assert bws(ctypes.byref(c2dims(T=32768)), 1) == 0
+    assert bws(ctypes.byref(c2dims(T=8192)), 1) > 0
+    assert bws(ctypes.byref(c2dims(T=16384)), 1) > 0
+
+
 def test_other_errors():
     d = c2dims()
     assert call(d, fake_weights(), dtype=5) == -3
