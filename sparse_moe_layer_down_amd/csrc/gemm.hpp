@@ -21,9 +21,10 @@
 //                 from b_split_row on are taken from B2 (W1 and W2 stacked).
 //
 // Tiling: BM x BN output tile per work-group of WM x WN waves; BK = 128 bytes
-// of K per step (64 bf16 or 32 fp32).  Operands go global -> registers -> LDS;
-// the global loads run PF steps ahead through a ring of register sets and LDS
-// is double buffered; LDS rows are 128 B with the 16-B chunks XOR-swizzled by
+// of K per step (64 bf16 or 32 fp32).  Two load pipelines: load to LDS (BDMA,
+// below) for the eight-wave tiles, and global -> registers -> LDS for the rest,
+// where the global loads run PF steps ahead through a ring of register sets and
+// LDS is double buffered.  LDS rows are 128 B with the 16-B chunks XOR-swizzled by
 // (row & 7) so the MFMA fragment reads of 32 rows at one K offset spread
 // over all banks.  bf16 uses v_mfma_f32_32x32x16_bf16 (each lane holds 8
 // consecutive K of one row); fp32 uses v_mfma_f32_32x32x2_f32, eight per
@@ -443,13 +444,15 @@ template <int N> LMOE_DEV void wait_vm_lgkm0() {
 }
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// BDMA (grouped GEMMs): both operands go straight from global memory into LDS
-// (the gfx950 global-load-to-LDS path) instead of through registers: B through
-// a ring of three stages, two steps ahead, A through two stages, one step
-// ahead; a lane loads the 16-byte chunk of its row that the swizzle expects at
-// its LDS slot.  With no LDS stores left in the K loop, each step waits only
-// for the loads of the next one (an LDS store after such loads would make the
-// compiler wait for all of them).
+// BDMA: both operands go straight from global memory into LDS (buffer loads
+// with an LDS destination) instead of through registers: B through a ring of
+// three stages, two steps ahead, A through two stages, one step ahead; a lane
+// loads the 16-byte chunk of its row that the swizzle expects at its LDS slot.
+// Buffer loads rather than the FLAT-encoded global-load-to-LDS: the compiler
+// counts those as possible LDS accesses that complete out of order and turns
+// every later LDS wait into a full lgkmcnt(0).  With no LDS stores left in the
+// K loop, each step waits only for the loads of the next one (an LDS store
+// after such loads would make the compiler wait for all of them).
 template <typename T, typename TO, int BM, int BN, int WM, int WN, int PF, int EPI, bool GATHER, bool GROUPED,
           bool BDMA = false, bool BKN = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs p) {
