@@ -454,24 +454,62 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
 }
 
 // Geometry of the QB histogram launch, a function of (n, nbins) alone so that
-// the workspace size is too: experts per work-group (as many B-bin LDS
-// histograms as fit in 64 KB, at most 16), expert groups, and the most token
-// runs a launch uses.  Runs split the tokens so that the launch fills the GPU
-// in one round: as many work-groups as are resident at once (two per CU on a
-// 256-CU MI355X when a group's histograms take 64 KB of LDS; four when they
-// take at most 40 KB, as with 10000 bins and one expert per group).  Each run
-// but a lone one stores its counts to a slab of the workspace, and a merge
-// kernel sums the slabs.
+// the workspace size is too: experts per work-group, expert groups, and the
+// most token runs a launch uses.  Up to 10240 bins a group is a multiple of 4
+// experts, as many B-bin LDS histograms as fit in the 160 KB of a CU, at most 32
+// (a 128-byte line of a score row), so that each thread reads 16 bytes of a
+// score row at once; wider histograms take one expert per group.
+// Runs split the tokens so that the launch fills the GPU in one round: as many
+// work-groups as are resident at once (one per CU on a 256-CU MI355X when a
+// group's histograms take over 80 KB of LDS, two from 64 KB, four when they take
+// at most 40 KB, as with 10000 bins and one expert per group).  Each run but a
+// lone one stores its counts to a slab of the workspace, and a merge kernel
+// sums the slabs.
+// Raises a kernel's dynamic LDS limit to `bytes`, once per device and kernel
+// (up to 8 kernels).
+hipError_t set_lds_limit(const void *kern, int bytes) {
+  struct Entry {
+    std::atomic<const void *> kern{nullptr};
+    std::atomic<int> state{0};  // 0 unset, 1 done, 2 failed
+  };
+  static Entry table[MAX_DEVICES][8];
+  static std::mutex mu;
+  const int dev = current_device();
+  if (dev < 0) return hipErrorInvalidDevice;
+  for (Entry &e : table[dev]) {
+    if (e.kern.load(std::memory_order_acquire) == kern) {
+      const int st = e.state.load(std::memory_order_acquire);
+      if (st != 0) return st == 1 ? hipSuccess : hipErrorInvalidValue;
+    }
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  for (Entry &e : table[dev]) {
+    const void *k = e.kern.load(std::memory_order_acquire);
+    if (k == kern) return e.state.load() == 1 ? hipSuccess : hipErrorInvalidValue;
+    if (k == nullptr) {
+      const hipError_t r = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+      e.state.store(r == hipSuccess ? 1 : 2, std::memory_order_release);
+      e.kern.store(kern, std::memory_order_release);
+      return r;
+    }
+  }
+  return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);  // table full
+}
+
+constexpr int QB_LDS_MAX = 163840;  // LDS of one MI355X CU
+
 struct QbGeom {
   int eg;
   int64_t groups, runs;
 };
 QbGeom qb_geom(int64_t n, int nbins) {
   QbGeom g;
-  g.eg = (int)std::min<int64_t>(16, std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4)));
+  const int64_t quads = QB_LDS_MAX / ((int64_t)nbins * 16);  // 4-expert groups that fit in LDS
+  g.eg = quads >= 1 ? (int)std::min<int64_t>(std::min<int64_t>(32, 4 * quads), cdiv(n, 4) * 4)
+                    : (int)std::max<int64_t>(1, 65536 / ((int64_t)nbins * 4));
   g.groups = cdiv(n, g.eg);
   const int64_t lds = (int64_t)g.eg * nbins * 4;
-  const int64_t slots = 256 * std::max<int64_t>(1, std::min<int64_t>(4, 163840 / lds));
+  const int64_t slots = 256 * std::max<int64_t>(1, std::min<int64_t>(4, QB_LDS_MAX / lds));
   g.runs = std::max<int64_t>(1, std::min<int64_t>(QB_MAX_RUNS, slots / g.groups));
   return g;
 }
@@ -484,10 +522,13 @@ int64_t qb_part_bytes(int64_t n, int nbins) {
 // The histogram launch of both QB forms: B-bin histograms of every expert over
 // the T > 0 tokens, written to hist (accumulate == 0) or added to it.  part:
 // the slabs (qb_part_bytes).  MARGIN: the binned value is the margin of the
-// score against the token's threshold (bias [n], thr [T]).
+// score against the token's threshold (bias [n], thr [T]).  pooled (may be
+// null): when the launch merges several runs' slabs, it also leaves the pooled
+// histogram sum_e hist[e] there and sets *pooled_done.
 template <bool MARGIN>
 hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_t *hist, int32_t *part,
-                          int accumulate, const float *bias, const float2 *thr, hipStream_t st) {
+                          int accumulate, const float *bias, const float2 *thr, hipStream_t st,
+                          unsigned long long *pooled = nullptr, bool *pooled_done = nullptr) {
   const int64_t n = ni;
   const QbGeom g = qb_geom(n, kb);
   // runs of at least 256 tokens
@@ -495,10 +536,19 @@ hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_
   const int64_t tpb = cdiv(T, runs);
   runs = cdiv(T, tpb);
   const int64_t items = g.groups * runs;
-  hipLaunchKernelGGL(qb_hist_kernel<MARGIN>, dim3((unsigned)(8 * cdiv(items, 8))), dim3(QB_HIST_THREADS),
-                     (size_t)g.eg * kb * 4, st, scores, T, ni, kb, g.eg, (int)g.groups, (int)runs, tpb, hist, part,
-                     accumulate, bias, thr);
-  if (runs > 1) {
+  const bool fuse_pool = pooled != nullptr && runs > 1;
+  if (pooled_done) *pooled_done = fuse_pool;
+  const bool quad = (n % 4) == 0 && (g.eg % 4) == 0;  // every group's width and first expert too
+  auto kern = quad ? qb_hist_kernel<MARGIN, true> : qb_hist_kernel<MARGIN, false>;
+  const size_t lds = (size_t)g.eg * kb * 4;
+  if (lds > 65536 && set_lds_limit((const void *)kern, QB_LDS_MAX) != hipSuccess) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(8 * cdiv(items, 8))), dim3(QB_HIST_THREADS), lds, st, scores,
+                     T, ni, kb, g.eg, (int)g.groups, (int)runs, tpb, hist, part, accumulate, bias, thr,
+                     fuse_pool ? pooled : nullptr);
+  if (fuse_pool) {
+    hipLaunchKernelGGL(qb_merge_pool_kernel, dim3((unsigned)cdiv(kb, 64), (unsigned)cdiv(n, QB_MP_SLICE)), dim3(256),
+                       0, st, part, (int)runs, ni, kb, hist, accumulate, pooled);
+  } else if (runs > 1) {
     const int64_t cnt = n * kb;
     hipLaunchKernelGGL(qb_merge_kernel, dim3((unsigned)cdiv(cnt, 256)), dim3(256), 0, st, part, (int)runs, cnt, hist,
                        accumulate);
@@ -953,9 +1003,13 @@ int lmoe_forward_static(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, ws, LMOE_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
+// QB update workspace: the pooled histogram (nbins int64) and tau (one double),
+// then the runs' slabs.
+int64_t qb_pooled_bytes(int nbins) { return align256((int64_t)nbins * 8 + 8); }
+
 size_t lmoe_qb_workspace_size(int64_t n, int32_t nbins) {
   if (nbins < 1 || nbins > 16384 || n < 1 || n > ((int64_t)1 << 20)) return 0;
-  return (size_t)(align256((int64_t)nbins * 8) + qb_part_bytes(n, nbins));
+  return (size_t)(qb_pooled_bytes(nbins) + qb_part_bytes(n, nbins));
 }
 
 int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
@@ -972,9 +1026,12 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
   if (need_ws && workspace_bytes < lmoe_qb_workspace_size(n, nbins)) return LMOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   const int ni = (int)n, kb = nbins;
+  unsigned long long *pooled = solve ? (unsigned long long *)workspace : nullptr;
+  bool pooled_done = false;
   if (T > 0) {
-    int32_t *part = (int32_t *)((unsigned char *)workspace + align256((int64_t)nbins * 8));
-    if (launch_qb_hist<false>(scores, T, ni, kb, hist, part, accumulate, nullptr, nullptr, st) != hipSuccess)
+    int32_t *part = (int32_t *)((unsigned char *)workspace + qb_pooled_bytes(nbins));
+    if (launch_qb_hist<false>(scores, T, ni, kb, hist, part, accumulate, nullptr, nullptr, st, pooled,
+                              &pooled_done) != hipSuccess)
       return LMOE_ERR_HIP;
   } else if (!accumulate) {
     const int64_t cnt = n * nbins;
@@ -983,14 +1040,29 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
   }
   if (solve) {
-    unsigned long long *pooled = (unsigned long long *)workspace;
-    hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)cdiv(nbins, 256)), dim3(256), 0, st, pooled, (int64_t)nbins);
-    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
-    hipLaunchKernelGGL(qb_pool_kernel, dim3((unsigned)cdiv(nbins, 64), (unsigned)cdiv(n, QB_POOL_SLICE)), dim3(256), 0,
-                       st, hist, ni, kb, pooled);
-    if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
-    hipLaunchKernelGGL(qb_solve_kernel, dim3((unsigned)cdiv(n, 4)), dim3(256), 0, st, hist, pooled, ni, kb, (int)k,
-                       bias);
+    if (!pooled_done) {
+      hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)cdiv(nbins, 256)), dim3(256), 0, st, pooled, (int64_t)nbins);
+      if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+      hipLaunchKernelGGL(qb_pool_kernel, dim3((unsigned)cdiv(nbins, 64), (unsigned)cdiv(n, QB_POOL_SLICE)), dim3(256),
+                         0, st, hist, ni, kb, pooled);
+      if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+    }
+    if (nbins <= 64 * QB_LANE_BINS) {
+      hipLaunchKernelGGL(qb_solve_kernel, dim3((unsigned)cdiv(n, 4)), dim3(256), 0, st, hist, pooled, ni, kb, (int)k,
+                         bias);
+    } else {
+      double *tau = (double *)(pooled + nbins);
+      const int tau_lds = nbins * 8;
+      if (tau_lds > 65536 && set_lds_limit((const void *)qb_tau_kernel, QB_LDS_MAX) != hipSuccess) return LMOE_ERR_HIP;
+      hipLaunchKernelGGL(qb_tau_kernel, dim3(1), dim3(1024), (size_t)tau_lds, st, pooled, ni, kb, (int)k, tau);
+      if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
+      const int wpb = (int)std::max<int64_t>(1, std::min<int64_t>(4, QB_LDS_MAX / ((int64_t)nbins * 4)));
+      const int solve_lds = wpb * nbins * 4;
+      if (solve_lds > 65536 && set_lds_limit((const void *)qb_solve_wide_kernel, QB_LDS_MAX) != hipSuccess)
+        return LMOE_ERR_HIP;
+      hipLaunchKernelGGL(qb_solve_wide_kernel, dim3((unsigned)cdiv(n, wpb)), dim3(64 * wpb), (size_t)solve_lds, st,
+                         hist, tau, ni, kb, (int)k, wpb, bias);
+    }
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
   }
   return LMOE_OK;

@@ -9,7 +9,11 @@
 //                    one run it writes (or adds) its bins to the histogram,
 //                    with several it stores them to its run's slab.
 //   qb_merge_kernel  histogram (or histogram +) = the runs' slabs summed in order.
+//   qb_merge_pool_kernel  the same merge, also summing the pooled histogram (used
+//                    when the update solves).
 //   qb_pool_kernel   pooled histogram sum_e H[e] (int64), per expert slice, atomically summed.
+//   qb_tau_kernel, qb_solve_wide_kernel  the same solve for histograms of more
+//                    than 1024 bins, tau read once and each expert's bins staged in LDS
 //   qb_solve_kernel  one wavefront per expert: tail sums G(j) by a wave scan,
 //                    j* = max{j : G(j) >= c}, q by linear interpolation inside
 //                    bin j*, bias = fp32(tau - q) with tau read the same way
@@ -64,32 +68,37 @@ LMOE_DEV float qb_margin_u(float s, float b, float tk, float tk1) {
 // XCD x (work-groups are dispatched round-robin over the 8 XCDs) takes items
 // [x * chunk, (x + 1) * chunk) in order, so neighbouring expert groups of one
 // run, which read the same 128-byte lines of the score rows, share an L2.
-// Dynamic LDS = eg * nbins * 4 bytes.  When n, the group width and its first
-// expert are multiples of 4, each thread reads four adjacent experts of a token
-// as one 16-B load and eight tokens per iteration (the kernel is bound by these
-// strided loads, not by the LDS atomics, so it keeps many in flight); otherwise
-// one thread walks the group's experts of one token at a time.
+// Dynamic LDS = eg * nbins * 4 bytes.  QUAD (n and the group width multiples
+// of 4): each thread reads four adjacent experts of a token as one 16-B load,
+// in batches of tokens (the kernel is bound by these strided loads, not by the
+// LDS atomics, so it keeps many in flight); otherwise one thread walks the
+// group's experts of one token at a time.  (Two instantiations, so that each
+// path gets its own register allocation and occupancy.)
 // Output: with runs == 1 the group's bins go to hist (stored, or added when
 // accumulate != 0: every bin of the group belongs to this work-group alone);
 // with runs > 1 to part[r][e][bin], summed by qb_merge_kernel.
 // MARGIN: bin qb_margin_u of the score (bias [n], thr [T] = {tk, tk1}) instead
-// of the score itself.
+// of the score itself.  pooled (may be null): nbins counters that work-group 0
+// zeroes for a later qb_merge_pool_kernel.
 constexpr int QB_HIST_THREADS = 512;
 constexpr int QB_MAX_RUNS = 16;  // token runs of one histogram launch (slabs in the workspace)
 
-template <bool MARGIN>
+template <bool MARGIN, bool QUAD>
 __global__ __launch_bounds__(QB_HIST_THREADS) void qb_hist_kernel(const float *__restrict__ scores, int64_t T, int n,
                                                       int nbins, int eg, int groups, int runs,
                                                       int64_t tokens_per_block, int32_t *__restrict__ hist,
                                                       int32_t *__restrict__ part, int accumulate,
                                                       const float *__restrict__ bias,
-                                                      const float2 *__restrict__ thr) {
+                                                      const float2 *__restrict__ thr,
+                                                      unsigned long long *__restrict__ pooled) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int32_t *h = (int32_t *)smem_raw;
   const int items = groups * runs;
   const int chunk = (items + 7) / 8;
   const int w = (int)(blockIdx.x % 8) * chunk + (int)(blockIdx.x / 8);
   if (w >= items) return;  // uniform over the work-group, before any barrier
+  if (pooled && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < nbins; i += blockDim.x) pooled[i] = 0ull;
   const int run = w / groups, g = w - run * groups;
   const int e0 = g * eg;
   const int ne = min(eg, n - e0);
@@ -97,8 +106,8 @@ __global__ __launch_bounds__(QB_HIST_THREADS) void qb_hist_kernel(const float *_
   __syncthreads();
   const int64_t t0 = (int64_t)run * tokens_per_block;
   const int64_t t1 = min(T, t0 + tokens_per_block);
-  if ((n & 3) == 0 && (ne & 3) == 0 && (e0 & 3) == 0) {  // 16-byte aligned quads
-    constexpr int U = 8;                // tokens per thread and iteration
+  if constexpr (QUAD) {  // 16-byte aligned quads (ne and e0 are multiples of 4 too)
+    constexpr int U = 4;                // tokens per thread and batch
     const int nq = ne >> 2;            // 16-B quads per token
     const int rows = QB_HIST_THREADS / nq;  // tokens per pass
     const int tr = threadIdx.x / nq, q = threadIdx.x - tr * nq;
@@ -107,32 +116,44 @@ __global__ __launch_bounds__(QB_HIST_THREADS) void qb_hist_kernel(const float *_
       int32_t *hq = h + q * 4 * nbins;
       f32x4 bq = {0.0f, 0.0f, 0.0f, 0.0f};
       if (MARGIN) bq = *(const f32x4 *)(bias + e0 + q * 4);
-      int64_t t = t0 + tr;
-      for (; t + (U - 1) * rows < t1; t += U * rows) {
-        f32x4 v[U];
-        float2 th[U];
+      // Batches of U tokens (rows apart) alternate between two register sets:
+      // the loads of the next batch are issued before the atomics of the
+      // current one, and a short last batch is masked rather than walked a
+      // token at a time, so a run costs about one memory latency per batch.
+      const int64_t step = (int64_t)U * rows;
+      f32x4 va[U], vb[U];
+      float2 tha[U], thb[U];
+      auto load = [&](int64_t tb, f32x4 (&v)[U], float2 (&th)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          v[u] = *(const f32x4 *)(base + (t + u * rows) * n);
-          if (MARGIN) th[u] = thr[t + u * rows];
+          const int64_t t = tb + (int64_t)u * rows;
+          if (t < t1) {
+            v[u] = *(const f32x4 *)(base + t * n);
+            if (MARGIN) th[u] = thr[t];
+          }
         }
+      };
+      auto count = [&](int64_t tb, const f32x4 (&v)[U], const float2 (&th)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
+          if (tb + (int64_t)u * rows < t1) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float x = MARGIN ? qb_margin_u(v[u][c], bq[c], th[u].x, th[u].y) : v[u][c];
-            atomicAdd(&hq[c * nbins + qb_bin(x, nbins)], 1);
+            for (int c = 0; c < 4; ++c) {
+              const float x = MARGIN ? qb_margin_u(v[u][c], bq[c], th[u].x, th[u].y) : v[u][c];
+              atomicAdd(&hq[c * nbins + qb_bin(x, nbins)], 1);
+            }
           }
-      }
-      for (; t < t1; t += rows) {
-        const f32x4 v = *(const f32x4 *)(base + t * n);
-        float2 th = {0.0f, 0.0f};
-        if (MARGIN) th = thr[t];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float x = MARGIN ? qb_margin_u(v[c], bq[c], th.x, th.y) : v[c];
-          atomicAdd(&hq[c * nbins + qb_bin(x, nbins)], 1);
-        }
+      };
+      int64_t tb = t0 + tr;
+      if (tb < t1) load(tb, va, tha);
+      while (tb < t1) {
+        if (tb + step < t1) load(tb + step, vb, thb);
+        count(tb, va, tha);
+        tb += step;
+        if (tb >= t1) break;
+        if (tb + step < t1) load(tb + step, va, tha);
+        count(tb, vb, thb);
+        tb += step;
       }
     }
   } else {
@@ -191,6 +212,47 @@ __global__ __launch_bounds__(256) void qb_merge_kernel(const int32_t *__restrict
 #pragma unroll
   for (int r = 0; r < QB_MAX_RUNS; ++r) s += v[r];
   hist[i] = s;
+}
+
+// The merge of several runs' slabs fused with the pooled sum:
+//   hist[e][j] = (accumulate ? hist[e][j] : 0) + sum over runs r (in order) of part[r][e][j]
+//   pooled[j] += sum over the block's experts e of the new hist[e][j]
+// (pooled zeroed beforehand).  Grid (bin chunks of 64, expert slices of
+// QB_MP_SLICE); a block of 256 threads = 64 bins x 4 expert stripes sums its
+// slice and adds it to pooled with one 64-bit atomic per bin.
+constexpr int QB_MP_SLICE = 32;
+__global__ __launch_bounds__(256) void qb_merge_pool_kernel(const int32_t *__restrict__ part, int runs, int n,
+                                                            int nbins, int32_t *__restrict__ hist, int accumulate,
+                                                            unsigned long long *__restrict__ pooled) {
+  __shared__ long long red[4][64];
+  const int lane = threadIdx.x & 63, stripe = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
+  const int ea = blockIdx.y * QB_MP_SLICE, eb = min(n, ea + QB_MP_SLICE);
+  const int64_t cnt = (int64_t)n * nbins;
+  long long s = 0;
+  if (j < nbins) {
+#pragma unroll
+    for (int i = 0; i < QB_MP_SLICE / 4; ++i) {
+      const int e = ea + stripe + 4 * i;
+      if (e < eb) {
+        const int64_t idx = (int64_t)e * nbins + j;
+        int32_t v[QB_MAX_RUNS];
+#pragma unroll
+        for (int r = 0; r < QB_MAX_RUNS; ++r) v[r] = r < runs ? part[r * cnt + idx] : 0;
+        int32_t hv = accumulate ? hist[idx] : 0;
+#pragma unroll
+        for (int r = 0; r < QB_MAX_RUNS; ++r) hv += v[r];
+        hist[idx] = hv;
+        s += hv;
+      }
+    }
+  }
+  red[stripe][lane] = s;
+  __syncthreads();
+  if (stripe == 0 && j < nbins) {
+    const long long v = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+    if (v) atomicAdd(&pooled[j], (unsigned long long)v);
+  }
 }
 
 // pooled[j] = sum_e hist[e][j]: grid (bin chunks of 64, expert slices); a
@@ -351,6 +413,82 @@ __global__ __launch_bounds__(256) void qb_solve_kernel(const int32_t *__restrict
   }
   if (tau != tau || q != q) return;
   if ((threadIdx.x & 63) == 0) bias[e] = (float)(tau - q);
+}
+
+// Histograms wider than a lane's register copy (nbins > 64 * QB_LANE_BINS).
+// qb_tau_kernel reads tau from the pooled histogram once (one work-group stages
+// it in LDS, wave 0 reads it) and qb_solve_wide_kernel gives each expert one
+// wave that stages the expert's histogram in its own LDS region (coalesced
+// loads) before reading q; the reads are those of qb_read_wave, so the bias is
+// the same bits as qb_solve_kernel's.
+// Copies `count` 4- or 8-byte counters from global memory to LDS with `nth`
+// threads (this one is `id`): 16-byte loads when both sides are 16-byte
+// aligned, each thread's loads of a batch (up to B of them) issued before any
+// of its LDS stores, so a batch costs one memory latency.
+template <int B, typename E>
+LMOE_DEV void qb_stage_lds(E *dst, const E *__restrict__ src, int count, int id, int nth) {
+  constexpr int PER = 16 / (int)sizeof(E);
+  int done = 0;
+  if ((((uintptr_t)src | (uintptr_t)dst) & 15) == 0) {
+    const int nv = count / PER;
+    const u32x4 *s4 = (const u32x4 *)src;
+    u32x4 *d4 = (u32x4 *)dst;
+    for (int i0 = id; i0 < nv; i0 += B * nth) {
+      u32x4 r[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (i0 + u * nth < nv) r[u] = s4[i0 + u * nth];
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (i0 + u * nth < nv) d4[i0 + u * nth] = r[u];
+    }
+    done = nv * PER;
+  }
+  for (int i0 = done + id; i0 < count; i0 += B * nth) {
+    E r[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (i0 + u * nth < count) r[u] = src[i0 + u * nth];
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (i0 + u * nth < count) dst[i0 + u * nth] = r[u];
+  }
+}
+
+__global__ __launch_bounds__(1024) void qb_tau_kernel(const unsigned long long *__restrict__ pooled, int n, int nbins,
+                                                      int k, double *__restrict__ tau) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  unsigned long long *hp = (unsigned long long *)smem_raw;
+  qb_stage_lds<8>(hp, pooled, nbins, (int)threadIdx.x, (int)blockDim.x);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    long long v[QB_LANE_BINS];
+    const double t = qb_read_wave<false>(hp, v, nbins, (long long)k, (long long)n);
+    if (threadIdx.x == 0) *tau = t;
+  }
+}
+
+// wpb waves per work-group, wave w (expert blockIdx.x * wpb + w) in LDS region w
+// of nbins counters; tau from qb_tau_kernel.
+__global__ __launch_bounds__(256) void qb_solve_wide_kernel(const int32_t *__restrict__ hist,
+                                                            const double *__restrict__ tau, int n, int nbins, int k,
+                                                            int wpb, float *__restrict__ bias) {
+#pragma clang fp contract(off)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * wpb + w;
+  if (w >= wpb || e >= n) return;  // wave-uniform; no work-group barrier below
+  int32_t *mine = (int32_t *)smem_raw + (int64_t)w * nbins;
+  const int32_t *he = hist + (int64_t)e * nbins;
+  qb_stage_lds<16>(mine, he, nbins, lane, 64);
+  // the wave reads bins other lanes wrote: its LDS writes complete first
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  long long v[QB_LANE_BINS];
+  const double q = qb_read_wave<false>(mine, v, nbins, (long long)k, (long long)n);
+  const double t = *tau;
+  if (t != t || q != q) return;
+  if (lane == 0) bias[e] = (float)(t - q);
 }
 
 // Inverse of ord_f32 (for keys that came from a float): the float whose

@@ -37,7 +37,10 @@ def same_bits(a, b):
 
 
 @pytest.mark.parametrize("T,n,k,nbins", [(64, 16, 4, 1000), (4096, 128, 8, 1000), (777, 100, 3, 37),
-                                         (300, 896, 16, 10000), (5, 3, 1, 1)])
+                                         (300, 896, 16, 10000), (5, 3, 1, 1),
+                                         # wide histograms: tau read once, bins staged in LDS; n not a
+                                         # multiple of 4 (per-expert loads), the widest histogram
+                                         (513, 6, 2, 4099), (700, 40, 5, 16384), (2000, 12, 3, 8192)])
 def test_hist_and_bias_bit_exact(T, n, k, nbins):
     s = host_scores(T, n, seed=T + n, skew=1.0)
     s[0, 0] = 1.0
