@@ -498,9 +498,8 @@ LMOE_DEV float unord_f32(uint32_t u) {
 }
 
 // One wavefront per token: tk = the k-th and tk1 = the (k+1)-th largest of the
-// n keys s + b (tk1 = -inf when k == n).  Lane l holds experts l, l + 64, ...
-// as 64-bit keys (order-preserving bits of s + b, complemented index), so each
-// round's wave maximum is unique and its owner drops exactly that key.
+// n keys s + b (tk1 = -inf when k == n), selected as by the top-k kernel
+// (wave_topk), so the keys and their order are the same.
 template <int MAXJ>
 __global__ __launch_bounds__(256) void qb_thresholds_kernel(const float *__restrict__ s,
                                                             const float *__restrict__ bias, int T, int n, int k,
@@ -510,28 +509,14 @@ __global__ __launch_bounds__(256) void qb_thresholds_kernel(const float *__restr
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
   const int rounds = min(k + 1, n);
   for (int t = wave; t < T; t += nwaves) {
-    const float *row = s + (int64_t)t * n;
-    uint64_t key[MAXJ];
-#pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int e = lane + 64 * j;
-      const int ec = min(e, n - 1);
-      const float sel = row[ec] + bias[ec];
-      key[j] = e < n ? ((uint64_t)ord_f32(sel) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
-    }
+    uint32_t hi[MAXJ];
+    token_keys<MAXJ>(s + (int64_t)t * n, bias, n, hi);
     float tk = 0.0f, tk1 = -INFINITY;
-    for (int r = 0; r < rounds; ++r) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int j = 0; j < MAXJ; ++j) best = key[j] > best ? key[j] : best;
-      const uint64_t g = wave_max_key(best);
-#pragma unroll
-      for (int j = 0; j < MAXJ; ++j)
-        if (key[j] == g) key[j] = 0ull;
+    wave_topk<MAXJ>(hi, rounds, [&](int r, uint64_t g) {
       const float v = unord_f32((uint32_t)(g >> 32));
       if (r == k - 1) tk = v;
       if (r == k) tk1 = v;
-    }
+    });
     if (lane == 0) thr[t] = make_float2(tk, tk1);
   }
 }

@@ -65,6 +65,72 @@ LMOE_DEV uint64_t wave_max_key(uint64_t v) {
   return ((uint64_t)mh << 32) | ml;
 }
 
+// The k largest keys of one token, one wavefront: lane l holds experts
+// e = l + 64 j (j < MAXJ) as the score words hi[j] = ord_f32(s_e + b_e) (0 for
+// e >= n); the full key of e is (hi << 32) | ~e, so the larger biased score wins
+// and, among equal scores, the lower index.  The index half follows from the lane
+// and the slot, so a lane keeps only the score words and compares 32-bit words.
+// visit(r, g) receives the r-th largest key g, r = 0 .. rounds - 1.  Each lane
+// caches its two largest remaining keys; keys are unique and a lane's wins come
+// in decreasing order, so its remaining keys are exactly those below its last
+// win, and when the cache runs out (a lane's second, fourth, ... win) it rescans
+// for the two largest keys below that win (no key is ever cleared).
+template <int MAXJ, typename F>
+LMOE_DEV void wave_topk(const uint32_t (&hi)[MAXJ], int rounds, F &&visit) {
+  const int lane = threadIdx.x & 63;
+  uint32_t bh = 0, sh = 0;  // best and second remaining key of this lane: score word, slot
+  int bj = -1, sj = -1;     // (slot < 0: none)
+  auto top2_below = [&](uint32_t lh, int lj) {  // keys (h, j) below (lh, lj) in key order
+    bh = 0;
+    sh = 0;
+    bj = -1;
+    sj = -1;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const uint32_t h = hi[j];
+      const bool ok = h < lh || (h == lh && j > lj);
+      // slots ascend, so an equal score word never beats an earlier slot
+      const bool gb = ok && (bj < 0 || h > bh);
+      const bool gs = ok && !gb && (sj < 0 || h > sh);
+      sh = gb ? bh : (gs ? h : sh);
+      sj = gb ? bj : (gs ? j : sj);
+      bh = gb ? h : bh;
+      bj = gb ? j : bj;
+    }
+  };
+  top2_below(0xFFFFFFFFu, -1);  // every key (no score word reaches all ones)
+  for (int r = 0; r < rounds; ++r) {
+    const uint64_t mine = bj >= 0 ? ((uint64_t)bh << 32) | (0xFFFFFFFFu - (uint32_t)(lane + 64 * bj)) : 0ull;
+    const uint64_t g = wave_max_key(mine);
+    visit(r, g);
+    if (bj >= 0 && mine == g) {  // the owning lane drops the winner
+      if (sj >= 0) {
+        bh = sh;
+        bj = sj;
+        sj = -1;
+      } else {
+        top2_below(bh, bj);
+      }
+    }
+  }
+}
+
+// The score words of a token's keys (see wave_topk): s + b of expert
+// lane + 64 j, loads issued together (padding slots load nothing).
+template <int MAXJ>
+LMOE_DEV void token_keys(const float *row, const float *bias, int n, uint32_t (&hi)[MAXJ]) {
+  const int lane = threadIdx.x & 63;
+  float sv[MAXJ], bv[MAXJ];
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int e = lane + 64 * j;
+    sv[j] = e < n ? row[e] : 0.0f;
+    bv[j] = e < n ? bias[e] : 0.0f;
+  }
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) hi[j] = lane + 64 * j < n ? ord_f32(sv[j] + bv[j]) : 0u;
+}
+
 template <int MAXJ>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ s, const float *__restrict__ bias,
                                                    int T, int n, int k, int32_t *__restrict__ idx_out,
@@ -74,53 +140,12 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ s, 
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
   for (int t = wave; t < T; t += nwaves) {
     const float *row = s + (int64_t)t * n;
-    uint64_t key[MAXJ];
-    float sv_[MAXJ], bv_[MAXJ];
-    // all loads first (clamped, unconditional), so they are in flight together
-#pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int e = min(lane + 64 * j, n - 1);
-      sv_[j] = row[e];
-      bv_[j] = bias[e];
-    }
-#pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int e = lane + 64 * j;
-      // padding ranks below every real expert (NaN included)
-      key[j] = e < n ? ((uint64_t)ord_f32(sv_[j] + bv_[j]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0ull;
-    }
-    // Each lane keeps its two largest remaining keys (best, second).  Keys are
-    // unique and a lane's wins come in decreasing order, so its remaining keys
-    // are exactly those below its last win: when the winner's cached second is
-    // used up it rescans for the two largest keys below the win (no key is
-    // ever cleared), which happens on a lane's second, fourth, ... win only.
-    uint64_t best = 0, second = 0;
-    auto top2_below = [&](uint64_t lim) {
-      best = 0;
-      second = 0;
-#pragma unroll
-      for (int j = 0; j < MAXJ; ++j) {
-        const uint64_t v = key[j] < lim ? key[j] : 0ull;
-        const bool gt_best = v > best;
-        second = gt_best ? best : (v > second ? v : second);
-        best = gt_best ? v : best;
-      }
-    };
-    top2_below(~0ull);
+    uint32_t hi[MAXJ];
+    token_keys<MAXJ>(row, bias, n, hi);
     int my_e = 0;
-    for (int r = 0; r < k; ++r) {
-      const uint64_t g = wave_max_key(best);
-      const int e = (int)(0xFFFFFFFFu - (uint32_t)g);
-      if (lane == r) my_e = e;
-      if (best == g) {  // the owning lane drops the winner
-        if (second != 0) {
-          best = second;
-          second = 0;
-        } else {
-          top2_below(g);
-        }
-      }
-    }
+    wave_topk<MAXJ>(hi, k, [&](int r, uint64_t g) {
+      if (lane == r) my_e = (int)(0xFFFFFFFFu - (uint32_t)g);
+    });
     const float sv = lane < k ? row[my_e] : 0.0f;
     const float tot = wave_sum(sv);
     if (lane < k) {
