@@ -59,7 +59,8 @@ def label(name):
     if not m:
         return name[:60]
     lab = re.sub(r"^_ZN4lmoe\d+", "", m.group(1))  # drop the mangled namespace prefix
-    if lab == "qb_hist_kernel" and ("ILb1E" in name or "<true>" in name):
+    # the histogram's first template argument selects the margin form
+    if lab == "qb_hist_kernel" and ("qb_hist_kernelILb1E" in name or "qb_hist_kernel<true" in name):
         return "qb_hist_kernel (margin)"
     return lab
 
@@ -88,7 +89,9 @@ def stage(lab, name):
              ("qb_margin_solve", "QB margin form: bias solve"),
              ("signsgd", "fixed-step (SignSGD) bias update"),
              ("qb_hist", "QB histogram"),
+             ("qb_merge_pool", "QB histogram: the runs' counts merged, pooled sum"),
              ("qb_merge", "QB histogram: the runs' counts merged"),
+             ("qb_tau", "QB bias solve (wide histograms): tau, once"),
              ("qb_pool", "QB pooled histogram"),
              ("qb_solve", "QB bias solve"),
              ("synth", "input synthesis (outside the timed region)")]

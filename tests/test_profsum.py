@@ -78,6 +78,19 @@ def test_rows_are_split_by_grid(tmp_path):
     assert got == [(1024, 2, "100"), (8192, 1, "900")]
 
 
+def test_qb_kernel_labels():
+    # histogram instances <MARGIN, QUAD>, mangled and demangled
+    assert profsum.label("_ZN4lmoe14qb_hist_kernelILb1ELb1EEEvPKfl") == "qb_hist_kernel (margin)"
+    assert profsum.label("void lmoe::qb_hist_kernel<true, false>(float const*)") == "qb_hist_kernel (margin)"
+    for plain in ("_ZN4lmoe14qb_hist_kernelILb0ELb1EEEvPKfl", "void lmoe::qb_hist_kernel<false, true>(float const*)"):
+        assert profsum.label(plain) == "qb_hist_kernel"
+        assert profsum.stage(profsum.label(plain), plain) == "QB histogram"
+    mp = "lmoe::qb_merge_pool_kernel(int const*, int, int, int, int*, int, unsigned long long*)"
+    assert profsum.stage(profsum.label(mp), mp) == "QB histogram: the runs' counts merged, pooled sum"
+    tau = "_ZN4lmoe13qb_tau_kernelEPKyiiiPd"
+    assert profsum.stage(profsum.label(tau), tau) == "QB bias solve (wide histograms): tau, once"
+
+
 def test_missing_summary_and_stable_hash(tmp_path):
     assert profsum.read_counters(str(tmp_path / "none.md")) == (None, None)
     h = profsum.source_sha256()
