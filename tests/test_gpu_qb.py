@@ -40,7 +40,10 @@ def same_bits(a, b):
                                          (300, 896, 16, 10000), (5, 3, 1, 1),
                                          # wide histograms: tau read once, bins staged in LDS; n not a
                                          # multiple of 4 (per-expert loads), the widest histogram
-                                         (513, 6, 2, 4099), (700, 40, 5, 16384), (2000, 12, 3, 8192)])
+                                         (513, 6, 2, 4099), (700, 40, 5, 16384), (2000, 12, 3, 8192),
+                                         # group geometry edges: 4 experts in exactly 160 KB of LDS, one bin
+                                         # more (one expert per group), 32-expert groups with n % 4 != 0
+                                         (3000, 12, 3, 10240), (3000, 12, 3, 10241), (5000, 70, 7, 1000)])
 def test_hist_and_bias_bit_exact(T, n, k, nbins):
     s = host_scores(T, n, seed=T + n, skew=1.0)
     s[0, 0] = 1.0
