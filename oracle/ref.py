@@ -576,9 +576,11 @@ def backward(x, P, k, n_shared, dtype, dy, beta1=4.0, beta2=25.0, eps=1e-6, forc
     stores them).  The backward stores, in the work dtype, the tensors that feed
     a matrix product: the latent gradient du (and g du, the routed rows'
     output gradient), the gated hidden's gradient da, the gate inputs'
-    gradients dp1, dp2, the router logits' gradient dl and the latent's
-    gradient dz; every product is then taken in fp64 of those rounded values.
-    dv, the norm's backward and the routing weights' gradient stay unrounded.
+    gradients dp1, dp2, the router logits' gradient dl, the latent's gradient
+    dz and the rows it is summed from (one per routed slot, shared expert and
+    the router); every product is then taken in fp64 of those rounded values.
+    dv, the norm's backward, the routing weights' gradient and the sum of the dz
+    rows stay unrounded.
     Steps (chain rule, the forward's notation):
       dv = dy W_up;  dW_up = dy^T v
       norm "rms": u_hat = u / r, r = sqrt(mean(u^2) + eps); dgamma = sum_i dv (.) u_hat;
@@ -590,11 +592,11 @@ def backward(x, P, k, n_shared, dtype, dy, beta1=4.0, beta2=25.0, eps=1e-6, forc
       shared expert s: da = rnd(rnd(du_i) W3s_s);  dW3s_s += rnd(du_i)^T a
       gate: dp1 = rnd(da) C(p2) SiTU'(p1);  dp2 = rnd(da) SiTU(p1) C'(p2)
             with p1 = z W1^T, p2 = z W2^T recomputed from the stored z
-      dz_i += rnd(dp1) W1_e + rnd(dp2) W2_e;  dW1_e += rnd(dp1)^T z;  dW2_e += rnd(dp2)^T z
+      dz_i += rnd(rnd(dp1) W1_e + rnd(dp2) W2_e);  dW1_e += rnd(dp1)^T z;  dW2_e += rnd(dp2)^T z
       router, chosen experts only (selection is not differentiable; the bias b
       gets no gradient): g_j = s_j / S, S = sum_j s_j:
             ds_j = (dg_j - sum_j' dg_j' g_j') / S;  dl_j = ds_j s_j (1 - s_j)
-            dz += rnd(dl) W_r;  dW_r = rnd(dl)^T z
+            dz += rnd(rnd(dl) W_r);  dW_r = rnd(dl)^T z
       dx = rnd(dz) W_down;  dW_down = rnd(dz)^T x
     Returns a dict with the weight gradients (dw_down [L, d], dw_router [n, L],
     dw1, dw2 [n, D, L], dw3 [n, L, D], dws1, dws2 [n_s, D, L], dws3 [n_s, L, D],
@@ -641,7 +643,7 @@ def backward(x, P, k, n_shared, dtype, dy, beta1=4.0, beta2=25.0, eps=1e-6, forc
         dout = round_to(gr[:, None] * du_rows, dtype)
         dp1 = round_to(da * cap(p2, beta2, gate) * situ_grad(p1, beta1, gate), dtype)
         dp2 = round_to(da * situ(p1, beta1, gate) * softcap_grad(p2, beta2, gate), dtype)
-        return a, dp1 @ w1 + dp2 @ w2, dp1.T @ zr, dp2.T @ zr, dout.T @ a
+        return a, round_to(dp1 @ w1 + dp2 @ w2, dtype), dp1.T @ zr, dp2.T @ zr, dout.T @ a
 
     for e in range(n):
         lo, hi = offs[e], offs[e + 1]
@@ -667,7 +669,7 @@ def backward(x, P, k, n_shared, dtype, dy, beta1=4.0, beta2=25.0, eps=1e-6, forc
     np.put_along_axis(dl_pre, idx, dsk * sk * (1.0 - sk), axis=1)
     dl = round_to(dl_pre, dtype)
     w_r = P.w_router()
-    dz += dl @ w_r
+    dz += round_to(dl @ w_r, dtype)
     dw_router = dl.T @ z
     dz_r = round_to(dz, dtype)
     dx = dz_r @ P.w_down()

@@ -623,7 +623,7 @@ WsLayout bwd_layout(const lmoe_dims &d, int dtype) {
   sz[B_DL] = T * b.np * es;
   sz[B_DA] = b.R * D * es;
   sz[B_DP] = b.R * 2 * D * es;
-  sz[B_DZROWS] = T * (k + ns + 1) * L * 4;
+  sz[B_DZROWS] = T * (k + ns + 1) * L * es;
   sz[B_DZ] = T * L * es;
   sz[B_DYT] = d.d * b.Tp * es;
   sz[B_VT] = L * b.Tp * es;
@@ -705,7 +705,7 @@ hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, c
   T *dl = (T *)(ws + B.off[B_DL]);
   T *da = (T *)(ws + B.off[B_DA]);
   T *dp = (T *)(ws + B.off[B_DP]);
-  float *dzrows = (float *)(ws + B.off[B_DZROWS]);
+  T *dzrows = (T *)(ws + B.off[B_DZROWS]);
   T *dz = (T *)(ws + B.off[B_DZ]);
   T *dyT = (T *)(ws + B.off[B_DYT]);
   T *vT = (T *)(ws + B.off[B_VT]);
@@ -806,34 +806,35 @@ hipError_t run_backward(const lmoe_dims &d, const lmoe_weights &w, const T *x, c
       else LMOE_TRY((launch_gemm<CfgW12, T, T, EPI_GLU_BWD, true, true>(a, st)));
     }
   }
-  // dz rows = dp1 W1_e + dp2 W2_e, fp32: W1_e and W2_e [D, L] read as stored, one
-  // K = 2D contraction whose rows k >= D come from W2_e
+  // dz rows = dp1 W1_e + dp2 W2_e in the work dtype (summed per token in fp32
+  // below): W1_e and W2_e [D, L] read as stored, one K = 2D contraction whose
+  // rows k >= D come from W2_e
   {
     GemmArgs a = gargs();
     a.A = dp; a.lda = 2 * D; a.B = w.w1; a.B2 = w.w2; a.Bsh = w.ws1; a.B2sh = w.ws2; a.n_routed = n; a.ldb = L;
     a.b_group_stride = (int64_t)D * L; a.kb_len = D;
     a.C = dzrows; a.ldc = L; a.N = L; a.K = 2 * D; a.tiles = tiles1; a.ntiles = ntiles;
     a.tiles_m = (int)max_tiles(d, w12_bm(d)); a.sched = sched2 + 2 * SCHED_COUNTERS;
-    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, float, EPI_STORE, false, true, true>(a, st)));
-    else LMOE_TRY((launch_gemm<CfgExpertKN, T, float, EPI_STORE, false, true, true>(a, st)));
+    if (small_experts(d)) LMOE_TRY((launch_gemm<CfgW12Small, T, T, EPI_STORE, false, true, true>(a, st)));
+    else LMOE_TRY((launch_gemm<CfgExpertKN, T, T, EPI_STORE, false, true, true>(a, st)));
   }
   // the router's part, dl W_r, as one more row block of dz rows
   {
     GemmArgs a = gargs();
     a.A = dl; a.lda = np_; a.B = wrT; a.ldb = np_; a.C = dzrows + (int64_t)T_ * (k + ns) * L; a.ldc = L;
     a.M = T_; a.N = L; a.K = np_;
-    LMOE_TRY((launch_dense<CfgDense, T, float, EPI_STORE>(a, part, st)));
+    LMOE_TRY((launch_dense<CfgDense, T, T, EPI_STORE>(a, part, st)));
   }
   // dz = sum of the token's dz rows (routed slots, shared experts, router)
   {
     const int nch8 = L / 8;
     const T *gain = (const T *)w.rms_gain;
     const dim3 wg((unsigned)cdiv(d.T, 4));
-    if (nch8 <= 64) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 1>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
-    else if (nch8 <= 128) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 2>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
-    else if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 4>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
-    else if (nch8 <= 448) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 7>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
-    else hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, float, 8>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    if (nch8 <= 64) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, T, 1>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    else if (nch8 <= 128) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, T, 2>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    else if (nch8 <= 256) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, T, 4>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    else if (nch8 <= 448) hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, T, 7>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
+    else hipLaunchKernelGGL((combine_rmsnorm_wave_kernel<T, T, 8>), wg, dim3(256), 0, st, dzrows, slot_row, gain, dz, T_, L, k, ns + 1, 0.0f, 1);
     LMOE_TRY(hipGetLastError());
   }
   // dx = dz W_down

@@ -23,6 +23,12 @@ LMOE_DEV void load8_f32_stream(const f16 *p, float *o) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = (float)b[i];
 }
+LMOE_DEV void load8_f32_stream(const bf16 *p, float *o) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+  const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (float)b[i];
+}
 LMOE_DEV void load8_f32_stream(const float *p, float *o) {
   const f32x4 a = __builtin_nontemporal_load((const f32x4 *)p), b = __builtin_nontemporal_load((const f32x4 *)(p + 4));
 #pragma unroll
