@@ -311,8 +311,8 @@ size_t lmoe_backward_workspace_size(const lmoe_dims *dims, int dtype);
  *     dg_j = du_i . o_j;  ds_j = (dg_j - sum_j' dg_j' g_j') / S;
  *     dl_j = ds_j s_j (1 - s_j);  dz += dl w_router;  dw_router = dl^T z
  *   dx = dz w_down;  dw_down = dz^T x
- * du, g du, da, dp1, dp2, dl and dz are stored in the work dtype between steps;
- * sums run in fp32.  Restrictions: LMOE_NORM_BOTH is not supported
+ * du, g du, da, dp1, dp2, dl, dz and the per-slot rows dz is summed from are
+ * stored in the work dtype between steps; sums run in fp32.  Restrictions: LMOE_NORM_BOTH is not supported
  * (LMOE_ERR_VALUE); L <= 4096 (LMOE_ERR_SHAPE).  T == 0 writes zero weight
  * gradients.  workspace: lmoe_backward_workspace_size() bytes.
  * Ownership and errors: every buffer is the caller's (device pointers, 16-byte
