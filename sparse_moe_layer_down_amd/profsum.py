@@ -81,6 +81,9 @@ def stage(lab, name):
              ("store out=bf16 gather=0 grouped=0", "W_down / W_up"),
              ("split-K", "split-K partial sums"),
              ("splitk_finalize", "split-K finalize"),
+             # the backward sums the dz rows with the combine kernel over bf16 rows (the
+             # forward's staged rows are fp16)
+             ("combine_rmsnorm_wave_kernelIDF16bDF16b", "backward: dz sum (the token's dz rows)"),
              ("combine", "combine + RMSNorm"),
              ("topk", "top-k + routing weights"),
              ("perm_", "permutation"),
