@@ -2,8 +2,8 @@
 // in the MFMA GEMM of gemm.hpp; these kernels prepare its operands and do the
 // element-wise and per-token steps).
 //
-//   transpose_kernel   out[c][kk] = scale(row) * in[row(kk)][c], a 64 x 64 tile
-//                      through LDS with 16-byte global accesses: plain
+//   transpose_kernel   out[c][kk] = scale(row) * in[row(kk)][c], 64-row tiles of
+//                      up to 256 columns through LDS with 16-byte global accesses: plain
 //                      transposes (row(kk) = kk, zero past R) and, for the
 //                      experts' weight gradients, gathered ones whose 64-wide
 //                      column blocks each belong to one expert's segment of rows
@@ -29,15 +29,18 @@ namespace lmoe {
 
 constexpr int TP_TILE = 64;
 
-// Tile (blockIdx.x: 64 columns c of the input, blockIdx.y: 64 output columns kk,
-// blockIdx.z: batch).  Without a block table, output column kk takes input row
-// kk (zero for kk >= R).  With one (int4 per 64-column block: {first input row,
-// valid rows, -, -}), column kk = 64 b + q takes input row rows[first + q] (or
-// first + q without a row map) for q < valid and zero beyond; blocks at or past
-// *nblocks are skipped; rscale[first + q] scales the row.  C, ld_in and ld_out
-// are multiples of the 16-byte element count; out columns are written in whole
-// 64-wide blocks (ld_out >= the padded column count).
-template <typename T>
+// Tiles of 64 rows (blockIdx.y: 64 output columns kk) by CT x 64 columns c of
+// the input (blockIdx.x), blockIdx.z: batch.  Without a block table, output
+// column kk takes input row kk (zero for kk >= R).  With one (int4 per 64-column
+// block: {first input row, valid rows, -, -}), column kk = 64 b + q takes input
+// row rows[first + q] (or first + q without a row map) for q < valid and zero
+// beyond; blocks at or past *nblocks are skipped; rscale[first + q] scales the
+// row.  C, ld_in and ld_out are multiples of the 16-byte element count; out
+// columns are written in whole 64-wide blocks (ld_out >= the padded column
+// count).  A thread issues all its loads of the CT tiles (the same rows, CT
+// column pieces each) before its LDS stores, so a block waits for memory once;
+// 256 threads.
+template <typename T, int CT>
 __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ in, int64_t ld_in, int64_t in_bs,
                                                         T *__restrict__ out, int64_t ld_out, int64_t out_bs, int R,
                                                         int C, const int4 *__restrict__ blocks,
@@ -46,8 +49,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ in
                                                         const float *__restrict__ rscale) {
   constexpr int EPT = 16 / (int)sizeof(T);       // elements per 16 bytes
   constexpr int CPR = TP_TILE / EPT;              // 16-byte chunks per tile row
-  __shared__ __attribute__((aligned(16))) T tile[TP_TILE][TP_TILE + EPT];
-  const int c0 = blockIdx.x * TP_TILE;
+  constexpr int PER = TP_TILE * CPR / 256;        // a thread's chunks of one tile
+  __shared__ __attribute__((aligned(16))) T tile[CT][TP_TILE][TP_TILE + EPT];
+  const int c0 = blockIdx.x * TP_TILE * CT;
   const int kb = blockIdx.y;
   if (blocks && kb >= *nblocks) return;  // uniform over the work-group
   const int64_t b = blockIdx.z;
@@ -59,34 +63,54 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *__restrict__ in
     first = e.x;
     valid = e.y;
   }
-  // load: 64 rows x CPR chunks
-  for (int i = threadIdx.x; i < TP_TILE * CPR; i += blockDim.x) {
-    const int q = i / CPR, ch = i % CPR;
-    const int c = c0 + ch * EPT;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (q < valid && c < C) {
-      const int r = blocks && rows ? rows[first + q] : first + q;
-      v = *(const u32x4 *)(in + (int64_t)r * ld_in + c);
-      if (rscale) {
-        const float sc = rscale[first + q];
-        T *e = (T *)&v;
+  // the thread's rows (the same in every column tile): chunk i = tid + 256 p is
+  // row q = i / CPR, 16-byte chunk i % CPR of the tile's 64 columns
+  int src[PER];
+  float sc[PER];
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) e[j] = from_f32<T>(to_f32(e[j]) * sc);
-      }
+  for (int p = 0; p < PER; ++p) {
+    const int q = ((int)threadIdx.x + 256 * p) / CPR;
+    src[p] = q < valid ? (blocks && rows ? rows[first + q] : first + q) : -1;
+    sc[p] = rscale && q < valid ? rscale[first + q] : 1.0f;
+  }
+  u32x4 v[CT][PER];
+#pragma unroll
+  for (int t = 0; t < CT; ++t)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int c = c0 + t * TP_TILE + (((int)threadIdx.x + 256 * p) % CPR) * EPT;
+      v[t][p] = u32x4{0u, 0u, 0u, 0u};
+      if (src[p] >= 0 && c < C) v[t][p] = *(const u32x4 *)(in + (int64_t)src[p] * ld_in + c);
     }
-    *(u32x4 *)&tile[q][ch * EPT] = v;
-  }
-  __syncthreads();
-  // store: output row c (64 of them) x CPR chunks of consecutive kk
-  for (int i = threadIdx.x; i < TP_TILE * CPR; i += blockDim.x) {
-    const int cc = i / CPR, ch = i % CPR;
-    if (c0 + cc >= C) continue;
-    u32x4 v;
-    T *e = (T *)&v;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) e[j] = tile[ch * EPT + j][cc];
-    *(u32x4 *)(out + (int64_t)(c0 + cc) * ld_out + (int64_t)kb * TP_TILE + ch * EPT) = v;
-  }
+  for (int t = 0; t < CT; ++t)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int i = (int)threadIdx.x + 256 * p;
+      u32x4 w = v[t][p];
+      if (rscale) {
+        T *e = (T *)&w;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) e[j] = from_f32<T>(to_f32(e[j]) * sc[p]);
+      }
+      *(u32x4 *)&tile[t][i / CPR][(i % CPR) * EPT] = w;
+    }
+  __syncthreads();
+  // store: output row c (64 per tile) x CPR chunks of consecutive kk
+#pragma unroll
+  for (int t = 0; t < CT; ++t)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int i = (int)threadIdx.x + 256 * p;
+      const int cc = i / CPR, ch = i % CPR;
+      const int c = c0 + t * TP_TILE + cc;
+      if (c >= C) continue;
+      u32x4 w;
+      T *e = (T *)&w;
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) e[j] = tile[t][ch * EPT + j][cc];
+      *(u32x4 *)(out + (int64_t)c * ld_out + (int64_t)kb * TP_TILE + ch * EPT) = w;
+    }
 }
 
 // Segments of the experts' padded row axis (one work-group of 1024 threads).

@@ -663,8 +663,9 @@ hipError_t launch_transpose(const T *in, int64_t ld_in, int64_t in_bs, T *out, i
                             const float *rscale = nullptr) {
   const unsigned gy = blocks ? (unsigned)nblk : (unsigned)cdiv(R, 64);
   if (gy == 0 || C == 0 || batches == 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_kernel<T>, dim3((unsigned)cdiv(C, 64), gy, (unsigned)batches), dim3(256), 0, st, in,
-                     ld_in, in_bs, out, ld_out, out_bs, R, C, blocks, nb, rows, rscale);
+  constexpr int CT = sizeof(T) == 2 ? 4 : 2;  // column tiles per block (36 KB / 34 KB of LDS)
+  hipLaunchKernelGGL((transpose_kernel<T, CT>), dim3((unsigned)cdiv(C, 64 * CT), gy, (unsigned)batches), dim3(256), 0,
+                     st, in, ld_in, in_bs, out, ld_out, out_bs, R, C, blocks, nb, rows, rscale);
   return hipGetLastError();
 }
 
