@@ -194,17 +194,25 @@ __global__ __launch_bounds__(256) void norm_bwd_wave_kernel(const TS *__restrict
   for (int q = 0; q < CPT; ++q)
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[q][i] = 0.0f;
-  // u: the token's staged rows summed in fp32, in the forward's order
-  for (int r = 0; r < nrows; ++r) {
-    const int64_t row = row_of(r);
+  // u: the token's staged rows summed in fp32, in the forward's order, two
+  // rows' loads in flight together
+  for (int r0 = 0; r0 < nrows; r0 += 2) {
+    const int64_t row0 = row_of(r0), row1 = row_of(min(r0 + 1, nrows - 1));
+    float y[2][CPT][8];
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int ch = min(lane + q * 64, nch - 1);
-      float y[8];
-      load8_f32(ystage + row * L + ch * 8, y);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) u[q][i] += y[i];
+      load8_f32(ystage + row0 * L + ch * 8, y[0][q]);
+      load8_f32(ystage + row1 * L + ch * 8, y[1][q]);
     }
+    const bool two = r0 + 1 < nrows;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        u[q][i] += y[0][q][i];
+        if (two) u[q][i] += y[1][q][i];
+      }
   }
   // dv -> h
 #pragma unroll
@@ -253,21 +261,34 @@ __global__ __launch_bounds__(256) void norm_bwd_wave_kernel(const TS *__restrict
     store8(du32 + t * L + ch * 8, h[q]);
     store8(du + t * L + ch * 8, h[q]);
   }
-  // dg_j = du . o_j where the staged row holds g_j o_j
-  for (int r = 0; r < k; ++r) {
-    const int64_t row = row_of(r);
-    float acc = 0.0f;
+  // dg_j = du . o_j where the staged row holds g_j o_j; two rows' loads in
+  // flight together, each row's dot product in the same order as alone
+  for (int r0 = 0; r0 < k; r0 += 2) {
+    const int r1 = min(r0 + 1, k - 1);
+    const int64_t row0 = row_of(r0), row1 = row_of(r1);
+    float y[2][CPT][8];
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
-      const int ch = lane + q * 64;
-      if (ch >= nch) continue;
-      float y[8];
-      load8_f32(ystage + row * L + ch * 8, y);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc += h[q][i] * y[i];
+      const int ch = min(lane + q * 64, nch - 1);
+      load8_f32(ystage + row0 * L + ch * 8, y[0][q]);
+      load8_f32(ystage + row1 * L + ch * 8, y[1][q]);
     }
-    acc = wave_sum(acc);
-    if (lane == 0) dg[t * k + r] = acc / gw[t * k + r];
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      if (lane + q * 64 >= nch) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        acc0 += h[q][i] * y[0][q][i];
+        acc1 += h[q][i] * y[1][q][i];
+      }
+    }
+    acc0 = wave_sum(acc0);
+    acc1 = wave_sum(acc1);
+    if (lane == 0) {
+      dg[t * k + r0] = acc0 / gw[t * k + r0];
+      if (r0 + 1 < k) dg[t * k + r1] = acc1 / gw[t * k + r1];
+    }
   }
 }
 
