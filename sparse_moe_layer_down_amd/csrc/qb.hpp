@@ -76,7 +76,7 @@ LMOE_DEV float qb_margin_u(float s, float b, float tk, float tk1) {
 // path gets its own register allocation and occupancy.)
 // Output: with runs == 1 the group's bins go to hist (stored, or added when
 // accumulate != 0: every bin of the group belongs to this work-group alone);
-// with runs > 1 to part[r][e][bin], summed by qb_merge_kernel.
+// with runs > 1 to part[r][e][bin], summed by qb_merge_kernel (or qb_merge_pool_kernel).
 // MARGIN: bin qb_margin_u of the score (bias [n], thr [T] = {tk, tk1}) instead
 // of the score itself.  pooled (may be null): nbins counters that work-group 0
 // zeroes for a later qb_merge_pool_kernel.
