@@ -357,26 +357,37 @@ LMOE_DEV double qb_read_wave(const CT *h, const long long (&v)[QB_LANE_BINS], in
         }
       }
     }
-  } else {  // the same walk from the top, a chunk of loads at a time
-    bool found = false;
-    for (int j0 = lo + (hi - lo - 1) / QB_LANE_BINS * QB_LANE_BINS; !found && j0 >= lo; j0 -= QB_LANE_BINS) {
-      long long w[QB_LANE_BINS];
+  } else {
+    // Only the range that holds j* needs the walk: it is the highest non-empty
+    // lane range whose bottom bin has G(lo) = incl >= c (G does not increase
+    // with j, and G(0) = N >= c).  That range is split over the wave (a few
+    // bins per lane), tail sums are taken across the lanes again, and each lane
+    // walks its piece from the top as above.
+    const unsigned long long holds = __ballot(lo < hi && (double)incl >= c);
+    const int ol = 63 - __clzll((long long)holds);
+    const int olo = __shfl(lo, ol, 64), ohi = __shfl(hi, ol, 64);
+    const long long otop = __shfl(G, ol, 64);  // G(ohi)
+    const int pp = (ohi - olo + 63) / 64;
+    const int plo = min(olo + lane * pp, ohi), phi = min(plo + pp, ohi);
+    long long part = 0;
+    for (int j = plo; j < phi; ++j) part += (long long)h[j];
+    long long pin = part;  // inclusive suffix scan of the pieces (lanes >= me)
 #pragma unroll
-      for (int i = 0; i < QB_LANE_BINS; ++i) w[i] = j0 + i < hi ? (long long)h[j0 + i] : 0;
-#pragma unroll
-      for (int i = QB_LANE_BINS - 1; i >= 0; --i) {
-        if (!found && j0 + i < hi) {
-          const long long gj = G + w[i];
-          if ((double)gj >= c) {
-            jcand = j0 + i;
-            Gnext = G;
-            hj = w[i];
-            found = true;
-          } else {
-            G = gj;
-          }
-        }
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long other = __shfl_down(pin, o, 64);
+      if (lane + o < 64) pin += other;
+    }
+    long long Gp = otop + (pin - part);  // G(phi)
+    for (int j = phi - 1; j >= plo; --j) {
+      const long long hv = (long long)h[j];
+      const long long gj = Gp + hv;
+      if ((double)gj >= c) {
+        jcand = j;
+        Gnext = Gp;
+        hj = hv;
+        break;
       }
+      Gp = gj;
     }
   }
   // j* = max over lanes of jcand
