@@ -542,16 +542,28 @@ hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_
   auto kern = quad ? qb_hist_kernel<MARGIN, true> : qb_hist_kernel<MARGIN, false>;
   const size_t lds = (size_t)g.eg * kb * 4;
   if (lds > 65536 && set_lds_limit((const void *)kern, QB_LDS_MAX) != hipSuccess) return hipErrorInvalidValue;
+  // 16-bit slabs when a run's counts fit and each group's counts start 16-byte aligned
+  const bool slab16 = runs > 1 && tpb < 65536 && g.eg % 8 == 0 && (n * kb) % 8 == 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)(8 * cdiv(items, 8))), dim3(QB_HIST_THREADS), lds, st, scores,
                      T, ni, kb, g.eg, (int)g.groups, (int)runs, tpb, hist, part, accumulate, bias, thr,
-                     fuse_pool ? pooled : nullptr);
+                     fuse_pool ? pooled : nullptr, slab16 ? 1 : 0);
+  const uint16_t *part16 = (const uint16_t *)part;
   if (fuse_pool) {
-    hipLaunchKernelGGL(qb_merge_pool_kernel, dim3((unsigned)cdiv(kb, 64), (unsigned)cdiv(n, QB_MP_SLICE)), dim3(256),
-                       0, st, part, (int)runs, ni, kb, hist, accumulate, pooled);
+    const dim3 grid((unsigned)cdiv(kb, 64), (unsigned)cdiv(n, QB_MP_SLICE));
+    if (slab16)
+      hipLaunchKernelGGL(qb_merge_pool_kernel<uint16_t>, grid, dim3(256), 0, st, part16, (int)runs, ni, kb, hist,
+                         accumulate, pooled);
+    else
+      hipLaunchKernelGGL(qb_merge_pool_kernel<int32_t>, grid, dim3(256), 0, st, part, (int)runs, ni, kb, hist,
+                         accumulate, pooled);
   } else if (runs > 1) {
     const int64_t cnt = n * kb;
-    hipLaunchKernelGGL(qb_merge_kernel, dim3((unsigned)cdiv(cnt, 256)), dim3(256), 0, st, part, (int)runs, cnt, hist,
-                       accumulate);
+    if (slab16)
+      hipLaunchKernelGGL(qb_merge_kernel<uint16_t>, dim3((unsigned)cdiv(cnt, 256)), dim3(256), 0, st, part16,
+                         (int)runs, cnt, hist, accumulate);
+    else
+      hipLaunchKernelGGL(qb_merge_kernel<int32_t>, dim3((unsigned)cdiv(cnt, 256)), dim3(256), 0, st, part,
+                         (int)runs, cnt, hist, accumulate);
   }
   return hipGetLastError();
 }

@@ -79,7 +79,9 @@ LMOE_DEV float qb_margin_u(float s, float b, float tk, float tk1) {
 // with runs > 1 to part[r][e][bin], summed by qb_merge_kernel (or qb_merge_pool_kernel).
 // MARGIN: bin qb_margin_u of the score (bias [n], thr [T] = {tk, tk1}) instead
 // of the score itself.  pooled (may be null): nbins counters that work-group 0
-// zeroes for a later qb_merge_pool_kernel.
+// zeroes for a later qb_merge_pool_kernel.  slab16: the runs' slabs hold 16-bit
+// counts (a run has fewer than 65536 tokens; n * nbins and the group width are
+// multiples of 8, so each group's counts start 16-byte aligned).
 constexpr int QB_HIST_THREADS = 512;
 constexpr int QB_MAX_RUNS = 16;  // token runs of one histogram launch (slabs in the workspace)
 
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(QB_HIST_THREADS) void qb_hist_kernel(const float *_
                                                       int32_t *__restrict__ part, int accumulate,
                                                       const float *__restrict__ bias,
                                                       const float2 *__restrict__ thr,
-                                                      unsigned long long *__restrict__ pooled) {
+                                                      unsigned long long *__restrict__ pooled, int slab16) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   int32_t *h = (int32_t *)smem_raw;
   const int items = groups * runs;
@@ -189,7 +191,16 @@ __global__ __launch_bounds__(QB_HIST_THREADS) void qb_hist_kernel(const float *_
   // the group's bins are contiguous ([e0, e0 + ne) x nbins) in hist and in the slab
   const int64_t off = (int64_t)e0 * nbins;
   const int cnt = ne * nbins;
-  if (runs > 1) {
+  if (runs > 1 && slab16) {  // eight counts per 16-byte store
+    uint16_t *dst = (uint16_t *)part + (int64_t)run * n * nbins + off;
+    const int c8 = cnt / 8;
+    for (int i = threadIdx.x; i < c8; i += blockDim.x) {
+      const int4 a = *(const int4 *)(h + 8 * i), b = *(const int4 *)(h + 8 * i + 4);
+      *(u32x4 *)(dst + 8 * i) = u32x4{(uint32_t)a.x | ((uint32_t)a.y << 16), (uint32_t)a.z | ((uint32_t)a.w << 16),
+                                      (uint32_t)b.x | ((uint32_t)b.y << 16), (uint32_t)b.z | ((uint32_t)b.w << 16)};
+    }
+    for (int i = 8 * c8 + threadIdx.x; i < cnt; i += blockDim.x) dst[i] = (uint16_t)h[i];
+  } else if (runs > 1) {
     int32_t *dst = part + (int64_t)run * n * nbins + off;
     for (int i = threadIdx.x; i < cnt; i += blockDim.x) dst[i] = h[i];
   } else if (accumulate) {
@@ -200,14 +211,16 @@ __global__ __launch_bounds__(QB_HIST_THREADS) void qb_hist_kernel(const float *_
 }
 
 // hist[i] = (accumulate ? hist[i] : 0) + sum over r < runs of part[r][i], r in
-// order; one element per thread, the runs' loads issued together.
-__global__ __launch_bounds__(256) void qb_merge_kernel(const int32_t *__restrict__ part, int runs, int64_t cnt,
+// order; one element per thread, the runs' loads issued together.  SL: the slab
+// element type (int32_t, or uint16_t for 16-bit slabs).
+template <typename SL>
+__global__ __launch_bounds__(256) void qb_merge_kernel(const SL *__restrict__ part, int runs, int64_t cnt,
                                                        int32_t *__restrict__ hist, int accumulate) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= cnt) return;
   int32_t v[QB_MAX_RUNS];
 #pragma unroll
-  for (int r = 0; r < QB_MAX_RUNS; ++r) v[r] = r < runs ? part[r * cnt + i] : 0;
+  for (int r = 0; r < QB_MAX_RUNS; ++r) v[r] = r < runs ? (int32_t)part[r * cnt + i] : 0;
   int32_t s = accumulate ? hist[i] : 0;
 #pragma unroll
   for (int r = 0; r < QB_MAX_RUNS; ++r) s += v[r];
@@ -221,7 +234,8 @@ __global__ __launch_bounds__(256) void qb_merge_kernel(const int32_t *__restrict
 // QB_MP_SLICE); a block of 256 threads = 64 bins x 4 expert stripes sums its
 // slice and adds it to pooled with one 64-bit atomic per bin.
 constexpr int QB_MP_SLICE = 32;
-__global__ __launch_bounds__(256) void qb_merge_pool_kernel(const int32_t *__restrict__ part, int runs, int n,
+template <typename SL>
+__global__ __launch_bounds__(256) void qb_merge_pool_kernel(const SL *__restrict__ part, int runs, int n,
                                                             int nbins, int32_t *__restrict__ hist, int accumulate,
                                                             unsigned long long *__restrict__ pooled) {
   __shared__ long long red[4][64];
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(256) void qb_merge_pool_kernel(const int32_t *__res
         const int64_t idx = (int64_t)e * nbins + j;
         int32_t v[QB_MAX_RUNS];
 #pragma unroll
-        for (int r = 0; r < QB_MAX_RUNS; ++r) v[r] = r < runs ? part[r * cnt + idx] : 0;
+        for (int r = 0; r < QB_MAX_RUNS; ++r) v[r] = r < runs ? (int32_t)part[r * cnt + idx] : 0;
         int32_t hv = accumulate ? hist[idx] : 0;
 #pragma unroll
         for (int r = 0; r < QB_MAX_RUNS; ++r) hv += v[r];
