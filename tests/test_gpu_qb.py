@@ -54,6 +54,21 @@ def test_hist_and_bias_bit_exact(T, n, k, nbins):
     assert same_bits(b, B)
 
 
+@pytest.mark.parametrize("T", [16 * 65535, 1_100_000])
+def test_run_counts_at_the_16_bit_limit(T):
+    """Every score equal, so each token run's counts all land in one bin: with 16
+    runs of 65535 tokens that bin holds 65535 in every run (the most a 16-bit slab
+    takes); with 68750 tokens per run the runs' slabs are 32-bit."""
+    n, k, nbins = 8, 2, 1000
+    s = np.full((T, n), 0.5, dtype=np.float32)
+    s[::3, 1] = 0.25
+    h, b = gpu_qb(s, k, nbins)
+    H, B = ref.qb_update(s, nbins, k)
+    assert np.array_equal(h, H)
+    assert same_bits(b, B)
+    assert h[0, 500] == T
+
+
 def test_special_scores_bins():
     s = np.array([[0.0, 0.0005, 0.001, 0.9995, 0.999, 1.0, 1.5, -0.1, np.nan] * 2], dtype=np.float32).reshape(2, 9)
     h, _ = gpu_qb(s, 1, 1000, solve=False)
