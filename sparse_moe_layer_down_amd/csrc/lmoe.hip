@@ -377,7 +377,7 @@ hipError_t run_forward(const lmoe_dims &d, const lmoe_weights &w, const T *x, T 
                        tiles1, w3_bm(d), tiles2, ntiles);
     LMOE_TRY(hipGetLastError());
     hipLaunchKernelGGL(perm_scatter_kernel, dim3(nch, (unsigned)cdiv(k, 4)), dim3(PERM_CHUNK), 0, st, idx, gw, T_, n, k,
-                       ns, masks, cbase,
+                       ns, masks, cbase, offs,
                        row_token, row_w, slot_row);
     LMOE_TRY(hipGetLastError());
   }

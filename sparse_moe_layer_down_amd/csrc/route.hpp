@@ -13,10 +13,10 @@
 // Permutation (dispatch of tokens to experts, rows ordered by expert then
 // token): tokens are cut into chunks of 256.  For each chunk and expert a
 // 256-bit mask of the tokens that chose the expert is built in LDS; a single
-// scan work-group turns mask popcounts into per-(chunk, expert) bases and the
+// scan work-group turns mask popcounts into per-(chunk, expert) prefixes and the
 // global expert offsets, and writes the grouped-GEMM tile table; the scatter
-// kernel then places (token, slot) at base + popcount(mask bits below the
-// token).  Every step is integer and deterministic.
+// kernel then places (token, slot) at expert offset + prefix + popcount(mask
+// bits below the token).  Every step is integer and deterministic.
 #pragma once
 #include "common.hpp"
 
@@ -180,8 +180,10 @@ __global__ __launch_bounds__(256) void perm_mask_kernel(const int32_t *__restric
                                  __popcll(m[e * 4 + 3]);
 }
 
-// Single work-group: per-(chunk, expert) bases, expert counts/offsets, and two
-// grouped-GEMM tile tables (M-tile heights bm1 and bm2): entry j of a table is
+// Single work-group: each (chunk, expert) count replaced by the expert's rows in
+// the chunks before it (the chunk's rows of expert e start at offs[e] plus
+// that), the expert counts and offsets, and two grouped-GEMM tile tables
+// (M-tile heights bm1 and bm2): entry j of a table is
 // {expert, first row, end row} of one M tile.  The n_shared shared experts are
 // appended as experts n .. n + n_shared - 1 whose rows are all T tokens (rows
 // T*k + s*T .. + T, see perm_scatter_kernel); their tiles are interleaved
@@ -192,7 +194,7 @@ LMOE_DEV int interleave_pos(int i, bool shared, int nr, int ns, int q) {
   if (!shared) return i + min(i / q, ns);
   return (i + 1) * q <= nr ? (i + 1) * q + i : nr + i;
 }
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ cbase /* in: counts, out: bases */,
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ cbase /* in: counts, out: prefixes */,
                                                          int nchunks, int n, int T, int k, int n_shared,
                                                          int32_t *__restrict__ counts, int32_t *__restrict__ offs,
                                                          int bm1, int4 *__restrict__ tiles1, int bm2,
@@ -246,14 +248,6 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ c
       ntiles[0] = nr1 + ns1;
       ntiles[1] = nr2 + ns2;
     }
-    for (int c0 = 0; c0 < nchunks; c0 += CB) {
-      int v[CB];
-#pragma unroll
-      for (int j = 0; j < CB; ++j) v[j] = c0 + j < nchunks ? cbase[(int64_t)(c0 + j) * n + e] : 0;
-#pragma unroll
-      for (int j = 0; j < CB; ++j)
-        if (c0 + j < nchunks) cbase[(int64_t)(c0 + j) * n + e] = v[j] + off;
-    }
     const int s1 = s_t1[e] - t1, s2 = s_t2[e] - t2;
     for (int j = 0; j < t1; ++j) {
       const int r0 = off + j * bm1;
@@ -282,6 +276,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
                                                            const float *__restrict__ w, int T, int n, int k,
                                                            int n_shared, const uint64_t *__restrict__ masks,
                                                            const int32_t *__restrict__ cbase,
+                                                           const int32_t *__restrict__ offs,
                                                            int32_t *__restrict__ row_token,
                                                            float *__restrict__ row_w,
                                                            int32_t *__restrict__ slot_row) {
@@ -316,7 +311,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t *__rest
       const uint64_t *m = masks + ((int64_t)c * n + e[u]) * 4;
 #pragma unroll
       for (int q = 0; q < 4; ++q) mw[u][q] = m[q];
-      base[u] = cbase[(int64_t)c * n + e[u]];
+      base[u] = offs[e[u]] + cbase[(int64_t)c * n + e[u]];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
