@@ -536,7 +536,8 @@ hipError_t launch_qb_hist(const float *scores, int64_t T, int ni, int kb, int32_
   const int64_t tpb = cdiv(T, runs);
   runs = cdiv(T, tpb);
   const int64_t items = g.groups * runs;
-  const bool fuse_pool = pooled != nullptr && runs > 1;
+  // (the fused merge's grid has one row per QB_MP_SLICE experts, at most 65535)
+  const bool fuse_pool = pooled != nullptr && runs > 1 && cdiv(n, QB_MP_SLICE) <= 65535;
   if (pooled_done) *pooled_done = fuse_pool;
   const bool quad = (n % 4) == 0 && (g.eg % 4) == 0;  // every group's width and first expert too
   auto kern = quad ? qb_hist_kernel<MARGIN, true> : qb_hist_kernel<MARGIN, false>;

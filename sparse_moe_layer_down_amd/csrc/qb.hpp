@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void qb_merge_kernel(const SL *__restrict__ pa
 // (pooled zeroed beforehand).  Grid (bin chunks of 64, expert slices of
 // QB_MP_SLICE); a block of 256 threads = 64 bins x 4 expert stripes sums its
 // slice and adds it to pooled with one 64-bit atomic per bin.
-constexpr int QB_MP_SLICE = 32;
+constexpr int QB_MP_SLICE = 16;
 template <typename SL>
 __global__ __launch_bounds__(256) void qb_merge_pool_kernel(const SL *__restrict__ part, int runs, int n,
                                                             int nbins, int32_t *__restrict__ hist, int accumulate,
