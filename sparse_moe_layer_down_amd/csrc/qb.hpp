@@ -524,7 +524,7 @@ LMOE_DEV float unord_f32(uint32_t u) {
 
 // One wavefront per token: tk = the k-th and tk1 = the (k+1)-th largest of the
 // n keys s + b (tk1 = -inf when k == n), selected as by the top-k kernel
-// (wave_topk), so the keys and their order are the same.
+// (wave_topk, which keys order the same way) but in its values-only form.
 template <int MAXJ>
 __global__ __launch_bounds__(256) void qb_thresholds_kernel(const float *__restrict__ s,
                                                             const float *__restrict__ bias, int T, int n, int k,
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(256) void qb_thresholds_kernel(const float *__restr
     uint32_t hi[MAXJ];
     token_keys<MAXJ>(s + (int64_t)t * n, bias, n, hi);
     float tk = 0.0f, tk1 = -INFINITY;
-    wave_topk<MAXJ>(hi, rounds, [&](int r, uint64_t g) {
+    wave_topk<MAXJ, true>(hi, rounds, [&](int r, uint64_t g) {
       const float v = unord_f32((uint32_t)(g >> 32));
       if (r == k - 1) tk = v;
       if (r == k) tk1 = v;

@@ -75,7 +75,11 @@ LMOE_DEV uint64_t wave_max_key(uint64_t v) {
 // in decreasing order, so its remaining keys are exactly those below its last
 // win, and when the cache runs out (a lane's second, fourth, ... win) it rescans
 // for the two largest keys below that win (no key is ever cleared).
-template <int MAXJ, typename F>
+// VALUES: only the score words of the r-th largest keys are wanted (the k-th
+// largest value, counted with multiplicity, does not depend on which of several
+// equal keys is taken), so a round takes the 32-bit maximum alone and the lowest
+// lane holding it drops one key; visit then receives the word in the high half.
+template <int MAXJ, bool VALUES = false, typename F>
 LMOE_DEV void wave_topk(const uint32_t (&hi)[MAXJ], int rounds, F &&visit) {
   const int lane = threadIdx.x & 63;
   uint32_t bh = 0, sh = 0;  // best and second remaining key of this lane: score word, slot
@@ -100,10 +104,19 @@ LMOE_DEV void wave_topk(const uint32_t (&hi)[MAXJ], int rounds, F &&visit) {
   };
   top2_below(0xFFFFFFFFu, -1);  // every key (no score word reaches all ones)
   for (int r = 0; r < rounds; ++r) {
-    const uint64_t mine = bj >= 0 ? ((uint64_t)bh << 32) | (0xFFFFFFFFu - (uint32_t)(lane + 64 * bj)) : 0ull;
-    const uint64_t g = wave_max_key(mine);
-    visit(r, g);
-    if (bj >= 0 && mine == g) {  // the owning lane drops the winner
+    bool drop;
+    if constexpr (VALUES) {
+      const uint32_t mh = wave_max_u32(bj >= 0 ? bh : 0u);
+      const uint64_t holders = __ballot(bj >= 0 && bh == mh);
+      visit(r, (uint64_t)mh << 32);
+      drop = lane == __ffsll((long long)holders) - 1;
+    } else {
+      const uint64_t mine = bj >= 0 ? ((uint64_t)bh << 32) | (0xFFFFFFFFu - (uint32_t)(lane + 64 * bj)) : 0ull;
+      const uint64_t g = wave_max_key(mine);
+      visit(r, g);
+      drop = bj >= 0 && mine == g;
+    }
+    if (drop) {  // the owning lane drops the winner
       if (sj >= 0) {
         bh = sh;
         bj = sj;
