@@ -1063,8 +1063,8 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
       if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
     }
     if (nbins <= 64 * QB_LANE_BINS) {
-      hipLaunchKernelGGL(qb_solve_kernel, dim3((unsigned)cdiv(n, 4)), dim3(256), 0, st, hist, pooled, ni, kb, (int)k,
-                         bias);
+      hipLaunchKernelGGL(qb_solve_kernel, dim3((unsigned)cdiv(n, QB_SOLVE_EXPERTS)), dim3(64 * (QB_SOLVE_EXPERTS + 1)), 0,
+                         st, hist, pooled, ni, kb, (int)k, bias);
     } else {
       double *tau = (double *)(pooled + nbins);
       const int tau_lds = nbins * 8;

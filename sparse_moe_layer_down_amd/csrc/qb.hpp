@@ -418,26 +418,34 @@ LMOE_DEV double qb_read_wave(const CT *h, const long long (&v)[QB_LANE_BINS], in
   return ((double)(js + 1) - frac) / (double)nbins;
 }
 
-__global__ __launch_bounds__(256) void qb_solve_kernel(const int32_t *__restrict__ hist,
-                                                       const unsigned long long *__restrict__ pooled, int n, int nbins,
-                                                       int k, float *__restrict__ bias) {
+// Histograms of up to 64 * QB_LANE_BINS bins.  A work-group of five waves:
+// waves 0-3 read q of experts 4 * blockIdx.x + w, wave 4 reads tau from the
+// pooled histogram at the same time (the two reads overlap instead of running
+// one after the other in each wave), then waves 0-3 write fp32(tau - q).
+constexpr int QB_SOLVE_EXPERTS = 4;  // experts per work-group (plus one wave for tau)
+__global__ __launch_bounds__(64 * (QB_SOLVE_EXPERTS + 1)) void qb_solve_kernel(
+    const int32_t *__restrict__ hist, const unsigned long long *__restrict__ pooled, int n, int nbins, int k,
+    float *__restrict__ bias) {
 #pragma clang fp contract(off)
-  const int e = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  if (e >= n) return;  // wave-uniform
-  const int32_t *he = hist + (int64_t)e * nbins;
-  double tau, q;
-  long long vp[QB_LANE_BINS], vh[QB_LANE_BINS];
-  if (nbins <= 64 * QB_LANE_BINS) {  // both histograms' loads in flight together
-    qb_lane_load(pooled, nbins, vp);
-    qb_lane_load(he, nbins, vh);
-    tau = qb_read_wave<true>(pooled, vp, nbins, (long long)k, (long long)n);
-    q = qb_read_wave<true>(he, vh, nbins, (long long)k, (long long)n);
-  } else {
-    tau = qb_read_wave<false>(pooled, vp, nbins, (long long)k, (long long)n);
-    q = qb_read_wave<false>(he, vh, nbins, (long long)k, (long long)n);
+  __shared__ double s_tau;
+  const int w = threadIdx.x >> 6;
+  const int e = blockIdx.x * QB_SOLVE_EXPERTS + w;
+  long long v[QB_LANE_BINS];
+  double r = 0.0;
+  if (w == QB_SOLVE_EXPERTS) {
+    qb_lane_load(pooled, nbins, v);
+    r = qb_read_wave<true>(pooled, v, nbins, (long long)k, (long long)n);
+    if ((threadIdx.x & 63) == 0) s_tau = r;
+  } else if (e < n) {
+    const int32_t *he = hist + (int64_t)e * nbins;
+    qb_lane_load(he, nbins, v);
+    r = qb_read_wave<true>(he, v, nbins, (long long)k, (long long)n);
   }
-  if (tau != tau || q != q) return;
-  if ((threadIdx.x & 63) == 0) bias[e] = (float)(tau - q);
+  __syncthreads();
+  if (w == QB_SOLVE_EXPERTS || e >= n) return;
+  const double tau = s_tau;
+  if (tau != tau || r != r) return;
+  if ((threadIdx.x & 63) == 0) bias[e] = (float)(tau - r);
 }
 
 // Histograms wider than a lane's register copy (nbins > 64 * QB_LANE_BINS).
