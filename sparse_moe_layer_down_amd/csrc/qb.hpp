@@ -17,7 +17,8 @@
 //   qb_solve_kernel  one wavefront per expert: tail sums G(j) by a wave scan,
 //                    j* = max{j : G(j) >= c}, q by linear interpolation inside
 //                    bin j*, bias = fp32(tau - q) with tau read the same way
-//                    from the pooled histogram.  All counts are integers and
+//                    from the pooled histogram (by one more wave of the
+//                    work-group, beside the experts' reads).  All counts are integers and
 //                    the interpolation is the same sequence of IEEE fp64
 //                    operations as the definition, so the result is exact.
 //
