@@ -267,8 +267,9 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
                    size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace lmoe_qb_update needs for n experts and nbins bins
- * (the pooled histogram, int64 [nbins], and one double, then up to 16 int32
- * [n, nbins] slabs of per-run counts); 0 for an invalid n or nbins. */
+ * (the pooled histogram, int64 [nbins], tau and a completion counter, n
+ * doubles of per-expert reads, then up to 16 int32 [n, nbins] slabs of per-run
+ * counts); 0 for an invalid n or nbins. */
 size_t lmoe_qb_workspace_size(int64_t n, int32_t nbins);
 
 /* Gradients of the layer (device pointers, work dtype, overwritten).  Shapes as

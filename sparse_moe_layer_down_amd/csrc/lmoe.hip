@@ -1018,13 +1018,14 @@ int lmoe_forward_static(const lmoe_dims *dims, const lmoe_weights *w, int dtype,
   return forward_impl(dims, w, dtype, x, y, topk_idx, topk_w, scores, ws, LMOE_STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
-// QB update workspace: the pooled histogram (nbins int64) and tau (one double),
-// then the runs' slabs.
-int64_t qb_pooled_bytes(int nbins) { return align256((int64_t)nbins * 8 + 8); }
+// QB update workspace: the pooled histogram (nbins int64), tau (one double), the
+// wide solve's completion counter (in an 8-byte slot) and its q of every expert
+// (n doubles), then the runs' slabs.
+int64_t qb_pooled_bytes(int64_t n, int nbins) { return align256(((int64_t)nbins + QB_POOLED_EXTRA + n) * 8); }
 
 size_t lmoe_qb_workspace_size(int64_t n, int32_t nbins) {
   if (nbins < 1 || nbins > 16384 || n < 1 || n > ((int64_t)1 << 20)) return 0;
-  return (size_t)(qb_pooled_bytes(nbins) + qb_part_bytes(n, nbins));
+  return (size_t)(qb_pooled_bytes(n, nbins) + qb_part_bytes(n, nbins));
 }
 
 int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t nbins, int32_t *hist,
@@ -1044,7 +1045,7 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
   unsigned long long *pooled = solve ? (unsigned long long *)workspace : nullptr;
   bool pooled_done = false;
   if (T > 0) {
-    int32_t *part = (int32_t *)((unsigned char *)workspace + qb_pooled_bytes(nbins));
+    int32_t *part = (int32_t *)((unsigned char *)workspace + qb_pooled_bytes(n, nbins));
     if (launch_qb_hist<false>(scores, T, ni, kb, hist, part, accumulate, nullptr, nullptr, st, pooled,
                               &pooled_done) != hipSuccess)
       return LMOE_ERR_HIP;
@@ -1056,7 +1057,8 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
   }
   if (solve) {
     if (!pooled_done) {
-      hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)cdiv(nbins, 256)), dim3(256), 0, st, pooled, (int64_t)nbins);
+      hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)cdiv(nbins + QB_POOLED_EXTRA, 256)), dim3(256), 0, st, pooled,
+                         (int64_t)nbins + QB_POOLED_EXTRA);
       if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
       hipLaunchKernelGGL(qb_pool_kernel, dim3((unsigned)cdiv(nbins, 64), (unsigned)cdiv(n, QB_POOL_SLICE)), dim3(256),
                          0, st, hist, ni, kb, pooled);
@@ -1067,16 +1069,17 @@ int lmoe_qb_update(const float *scores, int64_t T, int64_t n, int64_t k, int32_t
                          st, hist, pooled, ni, kb, (int)k, bias);
     } else {
       double *tau = (double *)(pooled + nbins);
-      const int tau_lds = nbins * 8;
-      if (tau_lds > 65536 && set_lds_limit((const void *)qb_tau_kernel, QB_LDS_MAX) != hipSuccess) return LMOE_ERR_HIP;
-      hipLaunchKernelGGL(qb_tau_kernel, dim3(1), dim3(1024), (size_t)tau_lds, st, pooled, ni, kb, (int)k, tau);
-      if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
-      const int wpb = (int)std::max<int64_t>(1, std::min<int64_t>(4, QB_LDS_MAX / ((int64_t)nbins * 4)));
-      const int solve_lds = wpb * nbins * 4;
+      unsigned int *done = (unsigned int *)(pooled + nbins + 1);
+      double *qv = (double *)(pooled + nbins + QB_POOLED_EXTRA);
+      // wpb expert regions of nbins int32, or the pooled histogram (nbins int64),
+      // then the work-group's completion flag
+      const int wpb = (int)std::max<int64_t>(1, std::min<int64_t>(4, (QB_LDS_MAX - 1024) / ((int64_t)nbins * 4)));
+      const int flag_off = std::max(wpb * nbins * 4, nbins * 8);
+      const int solve_lds = flag_off + 16;
       if (solve_lds > 65536 && set_lds_limit((const void *)qb_solve_wide_kernel, QB_LDS_MAX) != hipSuccess)
         return LMOE_ERR_HIP;
-      hipLaunchKernelGGL(qb_solve_wide_kernel, dim3((unsigned)cdiv(n, wpb)), dim3(64 * wpb), (size_t)solve_lds, st,
-                         hist, tau, ni, kb, (int)k, wpb, bias);
+      hipLaunchKernelGGL(qb_solve_wide_kernel, dim3((unsigned)(cdiv(n, wpb) + 1)), dim3(64 * wpb), (size_t)solve_lds, st,
+                         hist, pooled, tau, done, qv, ni, kb, (int)k, wpb, flag_off, bias);
     }
     if (hipGetLastError() != hipSuccess) return LMOE_ERR_HIP;
   }

@@ -12,8 +12,9 @@
 //   qb_merge_pool_kernel  the same merge, also summing the pooled histogram (used
 //                    when the update solves).
 //   qb_pool_kernel   pooled histogram sum_e H[e] (int64), per expert slice, atomically summed.
-//   qb_tau_kernel, qb_solve_wide_kernel  the same solve for histograms of more
-//                    than 1024 bins, tau read once and each expert's bins staged in LDS
+//   qb_solve_wide_kernel  the same solve for histograms of more than 1024
+//                    bins, each expert's bins staged in LDS, tau read once by an
+//                    extra work-group, the bias written by the last one to finish
 //   qb_solve_kernel  one wavefront per expert: tail sums G(j) by a wave scan,
 //                    j* = max{j : G(j) >= c}, q by linear interpolation inside
 //                    bin j*, bias = fp32(tau - q) with tau read the same way
@@ -84,6 +85,9 @@ LMOE_DEV float qb_margin_u(float s, float b, float tk, float tk1) {
 // counts (a run has fewer than 65536 tokens; n * nbins and the group width are
 // multiples of 8, so each group's counts start 16-byte aligned).
 constexpr int QB_HIST_THREADS = 512;
+// The pooled histogram's nbins counters are followed by tau (a double) and the
+// wide solve's completion counter, zeroed with the counters.
+constexpr int QB_POOLED_EXTRA = 2;
 constexpr int QB_MAX_RUNS = 16;  // token runs of one histogram launch (slabs in the workspace)
 
 template <bool MARGIN, bool QUAD>
@@ -101,7 +105,7 @@ __global__ __launch_bounds__(QB_HIST_THREADS) void qb_hist_kernel(const float *_
   const int w = (int)(blockIdx.x % 8) * chunk + (int)(blockIdx.x / 8);
   if (w >= items) return;  // uniform over the work-group, before any barrier
   if (pooled && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < nbins; i += blockDim.x) pooled[i] = 0ull;
+    for (int i = threadIdx.x; i < nbins + QB_POOLED_EXTRA; i += blockDim.x) pooled[i] = 0ull;
   const int run = w / groups, g = w - run * groups;
   const int e0 = g * eg;
   const int ne = min(eg, n - e0);
@@ -449,12 +453,12 @@ __global__ __launch_bounds__(64 * (QB_SOLVE_EXPERTS + 1)) void qb_solve_kernel(
   if ((threadIdx.x & 63) == 0) bias[e] = (float)(tau - r);
 }
 
-// Histograms wider than a lane's register copy (nbins > 64 * QB_LANE_BINS).
-// qb_tau_kernel reads tau from the pooled histogram once (one work-group stages
-// it in LDS, wave 0 reads it) and qb_solve_wide_kernel gives each expert one
-// wave that stages the expert's histogram in its own LDS region (coalesced
-// loads) before reading q; the reads are those of qb_read_wave, so the bias is
-// the same bits as qb_solve_kernel's.
+// Histograms wider than a lane's register copy (nbins > 64 * QB_LANE_BINS):
+// qb_solve_wide_kernel (below) gives each expert one wave that stages the
+// expert's histogram in its own LDS region (coalesced loads) before reading q,
+// and one more work-group that stages the pooled histogram and reads tau; the
+// reads are those of qb_read_wave, so the bias is the same bits as
+// qb_solve_kernel's.
 // Copies `count` 4- or 8-byte counters from global memory to LDS with `nth`
 // threads (this one is `id`): 16-byte loads when both sides are 16-byte
 // aligned, each thread's loads of a batch (up to B of them) issued before any
@@ -489,40 +493,58 @@ LMOE_DEV void qb_stage_lds(E *dst, const E *__restrict__ src, int count, int id,
   }
 }
 
-__global__ __launch_bounds__(1024) void qb_tau_kernel(const unsigned long long *__restrict__ pooled, int n, int nbins,
-                                                      int k, double *__restrict__ tau) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  unsigned long long *hp = (unsigned long long *)smem_raw;
-  qb_stage_lds<8>(hp, pooled, nbins, (int)threadIdx.x, (int)blockDim.x);
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    long long v[QB_LANE_BINS];
-    const double t = qb_read_wave<false>(hp, v, nbins, (long long)k, (long long)n);
-    if (threadIdx.x == 0) *tau = t;
-  }
-}
-
-// wpb waves per work-group, wave w (expert blockIdx.x * wpb + w) in LDS region w
-// of nbins counters; tau from qb_tau_kernel.
+// Work-groups 0 .. gridDim.x - 2: wpb waves, wave w reads q of expert
+// blockIdx.x * wpb + w from its own LDS region of nbins counters and stores it
+// to qv[e]; the last work-group stages the pooled histogram in LDS (nbins
+// 64-bit counters) and its wave 0 reads tau into *tau.  Each work-group then
+// counts itself done (*done, zero at launch); the last one to finish writes
+// bias[e] = fp32(tau - q_e) for every expert, so tau is read beside the q reads
+// instead of by a launch before them.  No work-group waits for another.
+// Dynamic LDS: flag_off = max(wpb * nbins * 4, nbins * 8) bytes of staging,
+// then one word.
 __global__ __launch_bounds__(256) void qb_solve_wide_kernel(const int32_t *__restrict__ hist,
-                                                            const double *__restrict__ tau, int n, int nbins, int k,
-                                                            int wpb, float *__restrict__ bias) {
+                                                            const unsigned long long *__restrict__ pooled,
+                                                            double *__restrict__ tau, unsigned int *__restrict__ done,
+                                                            double *__restrict__ qv, int n, int nbins, int k, int wpb,
+                                                            int flag_off, float *__restrict__ bias) {
 #pragma clang fp contract(off)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  int &s_last = *(int *)(smem_raw + flag_off);  // one LDS word past the staging regions
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * wpb + w;
-  if (w >= wpb || e >= n) return;  // wave-uniform; no work-group barrier below
-  int32_t *mine = (int32_t *)smem_raw + (int64_t)w * nbins;
-  const int32_t *he = hist + (int64_t)e * nbins;
-  qb_stage_lds<16>(mine, he, nbins, lane, 64);
-  // the wave reads bins other lanes wrote: its LDS writes complete first
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
   long long v[QB_LANE_BINS];
-  const double q = qb_read_wave<false>(mine, v, nbins, (long long)k, (long long)n);
-  const double t = *tau;
-  if (t != t || q != q) return;
-  if (lane == 0) bias[e] = (float)(t - q);
+  if (blockIdx.x == gridDim.x - 1) {
+    unsigned long long *hp = (unsigned long long *)smem_raw;
+    qb_stage_lds<8>(hp, pooled, nbins, (int)threadIdx.x, (int)blockDim.x);
+    __syncthreads();
+    if (w == 0) {
+      const double t = qb_read_wave<false>(hp, v, nbins, (long long)k, (long long)n);
+      if (lane == 0) *tau = t;
+    }
+  } else {
+    const int e = blockIdx.x * wpb + w;
+    if (e < n) {  // wave-uniform
+      int32_t *mine = (int32_t *)smem_raw + (int64_t)w * nbins;
+      qb_stage_lds<16>(mine, hist + (int64_t)e * nbins, nbins, lane, 64);
+      // the wave reads bins other lanes wrote: its LDS writes complete first
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const double q = qb_read_wave<false>(mine, v, nbins, (long long)k, (long long)n);
+      if (lane == 0) qv[e] = q;
+    }
+  }
+  __syncthreads();  // this work-group's stores precede its count
+  if (threadIdx.x == 0) {
+    __threadfence();
+    s_last = atomicAdd(done, 1u) == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;  // uniform over the work-group
+  __threadfence();      // every other work-group's stores are visible from here
+  const double t = *(volatile const double *)tau;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) {
+    const double q = *(volatile const double *)(qv + e);
+    if (t == t && q == q) bias[e] = (float)(t - q);
+  }
 }
 
 // Inverse of ord_f32 (for keys that came from a float): the float whose

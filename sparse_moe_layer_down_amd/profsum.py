@@ -94,7 +94,6 @@ def stage(lab, name):
              ("qb_hist", "QB histogram"),
              ("qb_merge_pool", "QB histogram: the runs' counts merged, pooled sum"),
              ("qb_merge", "QB histogram: the runs' counts merged"),
-             ("qb_tau", "QB bias solve (wide histograms): tau, once"),
              ("qb_pool", "QB pooled histogram"),
              ("qb_solve", "QB bias solve"),
              ("synth", "input synthesis (outside the timed region)")]

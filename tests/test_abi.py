@@ -148,11 +148,11 @@ def test_qb_validation():
     # the pooled histogram (int64 per bin), then one int32 [n, nbins] count slab per token run:
     # 16-expert groups of 64 KB of LDS, two resident per CU: runs = min(16, 512 // groups)
     # (56 groups at n = 896: 9 runs)
-    assert lmoe.qb_workspace_size(896, 1000) == 8192 + 9 * 896 * 1000 * 4
+    assert lmoe.qb_workspace_size(896, 1000) == 15360 + 9 * 896 * 1000 * 4  # (1000 + 2 + 896) x 8 B, rounded to 256
     assert lmoe.qb_workspace_size(8, 1000) == 8192 + 16 * 8 * 1000 * 4
     # one expert per group at 10000 bins (40 KB, four per CU): 896 groups fill 1024 slots in one run
-    assert lmoe.qb_workspace_size(896, 10000) == 80128
-    assert lmoe.qb_workspace_size(200, 10000) == 80128 + 5 * 200 * 10000 * 4
+    assert lmoe.qb_workspace_size(896, 10000) == 87296  # (10000 + 2 + 896) x 8 B, rounded to 256
+    assert lmoe.qb_workspace_size(200, 10000) == 81664 + 5 * 200 * 10000 * 4
     assert lmoe.qb_workspace_size(896, 0) == 0 and lmoe.qb_workspace_size(0, 1000) == 0
 
 

@@ -91,8 +91,6 @@ def test_qb_kernel_labels():
     assert profsum.stage(profsum.label(dzsum), dzsum) == "backward: dz sum (the token's dz rows)"
     fwd = "_ZN4lmoe27combine_rmsnorm_wave_kernelIDF16bDF16_Li7EEEvPKT0_PKiPKT_PS6_iiiifi"
     assert profsum.stage(profsum.label(fwd), fwd) == "combine + RMSNorm"
-    tau = "_ZN4lmoe13qb_tau_kernelEPKyiiiPd"
-    assert profsum.stage(profsum.label(tau), tau) == "QB bias solve (wide histograms): tau, once"
 
 
 def test_missing_summary_and_stable_hash(tmp_path):
